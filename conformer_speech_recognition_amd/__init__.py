@@ -1,0 +1,279 @@
+"""Python binding of libgigaam.so, the gfx950 Conformer CTC encoder (C ABI in
+include/gigaam.h). Argument marshalling only: every step of the forward pass runs in
+the library's HIP kernels; PyTorch only supplies device memory and the stream.
+
+    import conformer_speech_recognition_amd as gg
+    model = gg.Model(cfg, weights)                      # cfg: dict, weights: name -> array
+    out = model.encode(pcm_cuda_f32[B, L], lengths)     # dict of torch tensors
+
+The library is loaded after torch so that it binds to the HIP runtime torch already
+loaded (one runtime per process: torch's streams and pointers are valid in it).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgigaam.so")
+
+OK, E_INVAL, E_WORKSPACE, E_UNSUPPORTED, E_HIP = 0, -1, -2, -3, -4
+DTYPES = {"f32": 0, "f16": 1, "bf16": 2, "w8f16": 3}
+STAGE_MEL, STAGE_SUB, STAGE_LAYER = 0, 1, 2
+MAX_BATCH = 256
+
+
+def stage_sublayer(layer: int, part: int) -> int:
+    """Tap inside block ``layer``: part 0 after FFN1, 1 after attention, 2 after the
+    conv module, 3 after FFN2 (before the block's final norm)."""
+    return 1000 + 10 * layer + part
+
+
+class GigaamError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"gigaam error {code}: {msg}")
+        self.code = code
+
+
+class Config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("n_layers", "d_model", "n_heads", "d_ff", "conv_kernel", "n_classes", "n_mels",
+                 "n_fft", "win_length", "hop_length", "sub_kernel", "sub_stride", "dtype")] + \
+               [(n, ctypes.c_float) for n in ("rope_base", "ln_eps", "bn_eps")]
+
+
+def make_config(cfg: dict) -> Config:
+    c = Config()
+    for name, _ in Config._fields_:
+        v = cfg[name]
+        if name == "dtype":
+            v = DTYPES[v] if isinstance(v, str) else int(v)
+        setattr(c, name, v)
+    return c
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_SZ = ctypes.c_size_t
+_IP = ctypes.POINTER(ctypes.c_int32)
+
+_SIGNATURES = {
+    "gigaam_version": (_I, []),
+    "gigaam_last_error": (ctypes.c_char_p, []),
+    "gigaam_frames": (ctypes.c_int, [_I, _IP, _IP, _IP]),
+    "gigaam_check_config": (ctypes.c_int, [ctypes.POINTER(Config)]),
+    "gigaam_canonical_count": (ctypes.c_int, [ctypes.POINTER(Config), _IP, ctypes.POINTER(_SZ)]),
+    "gigaam_canonical_entry": (ctypes.c_int, [ctypes.POINTER(Config), _I, ctypes.c_char_p, _I, _IP,
+                                              _IP, ctypes.POINTER(_SZ)]),
+    "gigaam_packed_bytes": (ctypes.c_int, [ctypes.POINTER(Config), ctypes.POINTER(_SZ)]),
+    "gigaam_pack_weights": (ctypes.c_int, [ctypes.POINTER(Config), _P, _SZ, _P, _SZ]),
+    "gigaam_default_frontend": (ctypes.c_int, [_P, _P, _P]),
+    "gigaam_create": (ctypes.c_int, [ctypes.POINTER(Config), _P, _P, _P, ctypes.POINTER(_P)]),
+    "gigaam_destroy": (None, [_P]),
+    "gigaam_workspace_bytes": (ctypes.c_int, [_P, _I, _I, ctypes.POINTER(_SZ)]),
+    "gigaam_encode": (ctypes.c_int, [_P, _P, _IP, _I, _I, _P, _SZ, _P, _P, _P, _P, _P, _IP, _P]),
+    "gigaam_encode_stage": (ctypes.c_int, [_P, _P, _IP, _I, _I, _P, _SZ, _I, _P, _SZ, _P]),
+    "gigaam_debug_gemm": (ctypes.c_int, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
+}
+
+
+def lib(require_torch: bool = True):
+    """Load libgigaam.so (after torch, so the HIP runtime is shared). Raises if the
+    library has not been built: there is no fallback path."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if require_torch:
+        import torch  # noqa: F401  (loads the HIP runtime the library must bind to)
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m conformer_speech_recognition_amd.build`")
+    L = ctypes.CDLL(LIB_PATH, mode=ctypes.RTLD_GLOBAL)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(rc: int):
+    if rc != OK:
+        raise GigaamError(rc, lib(False).gigaam_last_error().decode())
+
+
+def frames(n_samples: int) -> tuple[int, int, int]:
+    t, s, u = _I(), _I(), _I()
+    _check(lib(False).gigaam_frames(n_samples, ctypes.byref(t), ctypes.byref(s), ctypes.byref(u)))
+    return t.value, s.value, u.value
+
+
+def canonical_entries(cfg: dict) -> list[tuple[str, tuple[int, ...], int]]:
+    L = lib(False)
+    c = make_config(cfg)
+    n, nf = _I(), _SZ()
+    _check(L.gigaam_canonical_count(ctypes.byref(c), ctypes.byref(n), ctypes.byref(nf)))
+    out = []
+    buf = ctypes.create_string_buffer(256)
+    rank = _I()
+    shape = (_I * 3)()
+    off = _SZ()
+    for i in range(n.value):
+        _check(L.gigaam_canonical_entry(ctypes.byref(c), i, buf, 256, ctypes.byref(rank), shape,
+                                        ctypes.byref(off)))
+        out.append((buf.value.decode(), tuple(shape[j] for j in range(rank.value)), off.value))
+    return out
+
+
+def canonical_buffer(cfg: dict, weights: dict) -> np.ndarray:
+    """Concatenate the checkpoint tensors into the library's canonical float32 buffer."""
+    ents = canonical_entries(cfg)
+    total = ents[-1][2] + int(np.prod(ents[-1][1]))
+    buf = np.empty(total, dtype=np.float32)
+    for name, shape, off in ents:
+        a = np.asarray(weights[name])
+        if a.shape != shape:
+            raise ValueError(f"{name}: shape {a.shape}, expected {shape}")
+        buf[off: off + a.size] = a.astype(np.float32).ravel()
+    return buf
+
+
+def pack_weights(cfg: dict, weights: dict) -> np.ndarray:
+    L = lib(False)
+    c = make_config(cfg)
+    canon = canonical_buffer(cfg, weights)
+    nb = _SZ()
+    _check(L.gigaam_packed_bytes(ctypes.byref(c), ctypes.byref(nb)))
+    out = np.empty(nb.value, dtype=np.uint8)
+    _check(L.gigaam_pack_weights(ctypes.byref(c), canon.ctypes.data, canon.size, out.ctypes.data,
+                                 out.size))
+    return out
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+class Model:
+    """A packed model on one GPU. ``window`` [320] and ``melfb`` [161, 64] default to
+    the library's periodic Hann window and HTK filterbank (built on the device)."""
+
+    def __init__(self, cfg: dict, weights: dict, device="cuda", window=None, melfb=None):
+        import torch
+        L = lib()
+        self.cfg = dict(cfg)
+        self.device = torch.device(device)
+        self._c = make_config(cfg)
+        packed = pack_weights(cfg, weights)
+        self.packed = torch.from_numpy(packed).to(self.device)
+        stream = torch.cuda.current_stream(self.device).cuda_stream
+        if window is None or melfb is None:
+            self.window = torch.empty(320, dtype=torch.float32, device=self.device)
+            self.melfb = torch.empty(161 * 64, dtype=torch.float32, device=self.device)
+            _check(L.gigaam_default_frontend(self.window.data_ptr(), self.melfb.data_ptr(), stream))
+        if window is not None:
+            self.window = torch.as_tensor(window, dtype=torch.float32).reshape(320).to(self.device).contiguous()
+        if melfb is not None:
+            self.melfb = torch.as_tensor(melfb, dtype=torch.float32).reshape(161 * 64).to(self.device).contiguous()
+        h = _P()
+        _check(L.gigaam_create(ctypes.byref(self._c), self.packed.data_ptr(), self.window.data_ptr(),
+                               self.melfb.data_ptr(), ctypes.byref(h)))
+        self._h = h
+        self._ws = None
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().gigaam_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def workspace_bytes(self, batch: int, max_samples: int) -> int:
+        nb = _SZ()
+        _check(lib().gigaam_workspace_bytes(self._h, batch, max_samples, ctypes.byref(nb)))
+        return nb.value
+
+    def workspace(self, batch: int, max_samples: int):
+        import torch
+        need = self.workspace_bytes(batch, max_samples)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def _args(self, pcm, lengths):
+        import torch
+        if not (pcm.is_cuda and pcm.dtype == torch.float32 and pcm.dim() == 2 and pcm.is_contiguous()):
+            raise ValueError("pcm must be a contiguous float32 CUDA tensor [B, L]")
+        lens = np.ascontiguousarray(np.asarray(lengths, dtype=np.int32))
+        if lens.shape != (pcm.shape[0],):
+            raise ValueError("lengths must have one entry per clip")
+        return lens, lens.ctypes.data_as(_IP)
+
+    def encode(self, pcm, lengths, want_enc: bool = False, want_frame_ids: bool = True,
+               stream=None) -> dict:
+        import torch
+        lens, lp = self._args(pcm, lengths)
+        B, stride = pcm.shape
+        U = [frames(int(n))[2] for n in lens]
+        U_max = max(U)
+        C, d = self.cfg["n_classes"], self.cfg["d_model"]
+        dev = self.device
+        ws = self.workspace(B, int(lens.max()))
+        out = dict(
+            log_probs=torch.empty(B, U_max, C, dtype=torch.float32, device=dev),
+            token_ids=torch.empty(B, U_max, dtype=torch.int32, device=dev),
+            n_tokens=torch.empty(B, dtype=torch.int32, device=dev),
+        )
+        if want_frame_ids:
+            out["frame_ids"] = torch.empty(B, U_max, dtype=torch.int32, device=dev)
+        if want_enc:
+            out["enc_out"] = torch.empty(B, U_max, d, dtype=torch.float32, device=dev)
+        nfr = np.zeros(B, dtype=np.int32)
+        s = (stream or torch.cuda.current_stream(dev)).cuda_stream
+        _check(lib().gigaam_encode(self._h, pcm.data_ptr(), lp, B, stride, ws.data_ptr(), ws.numel(),
+                                   out["log_probs"].data_ptr(), out["token_ids"].data_ptr(),
+                                   out["n_tokens"].data_ptr(), _ptr(out.get("frame_ids")),
+                                   _ptr(out.get("enc_out")), nfr.ctypes.data_as(_IP), s))
+        out["n_frames"] = nfr
+        return out
+
+    def encode_stage(self, pcm, lengths, stage: int, stream=None):
+        import torch
+        lens, lp = self._args(pcm, lengths)
+        B, stride = pcm.shape
+        fr = [frames(int(n)) for n in lens]
+        rows = sum(f[0] for f in fr) if stage == STAGE_MEL else sum(f[2] for f in fr)
+        width = 64 if stage == STAGE_MEL else self.cfg["d_model"]
+        out = torch.empty(rows, width, dtype=torch.float32, device=self.device)
+        ws = self.workspace(B, int(lens.max()))
+        s = (stream or torch.cuda.current_stream(self.device)).cuda_stream
+        _check(lib().gigaam_encode_stage(self._h, pcm.data_ptr(), lp, B, stride, ws.data_ptr(),
+                                         ws.numel(), stage, out.data_ptr(), out.numel(), s))
+        return out
+
+
+def tokens_list(out: dict) -> list[list[int]]:
+    """Host copy of the collapsed token sequences."""
+    ids = out["token_ids"].cpu().numpy()
+    n = out["n_tokens"].cpu().numpy()
+    return [ids[b, : n[b]].tolist() for b in range(len(n))]
+
+
+def debug_gemm(dtype: str, A, W, bias=None, scale=None, stream=None):
+    """C = A @ W.T + bias with the encoder's GEMM kernel (A, W device tensors in the
+    storage type of ``dtype``; int8 W with fp16 ``scale`` for 'w8f16')."""
+    import torch
+    M, K = A.shape
+    N = W.shape[0]
+    C = torch.empty(M, N, dtype=torch.float32, device=A.device)
+    s = (stream or torch.cuda.current_stream(A.device)).cuda_stream
+    _check(lib().gigaam_debug_gemm(DTYPES[dtype], M, N, K, A.data_ptr(), W.data_ptr(), _ptr(scale),
+                                   _ptr(bias), C.data_ptr(), s))
+    return C

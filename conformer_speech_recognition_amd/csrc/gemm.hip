@@ -1,0 +1,331 @@
+// MFMA GEMM for gfx950: C = epilogue(A * W^T + bias), A [M][K] and W [N][K] both
+// K-contiguous (PyTorch Linear layout), fp32 accumulation.
+//
+// These are the dense contractions of the encoder (subsampling convs as implicit GEMMs,
+// FFN, q/k/v/out projections, pointwise convs, CTC head): "GigaAM MLX port for Mac",
+// section "Why parts of the model cannot simply be removed", notes that most of the time
+// goes to multiplying large matrices.
+//
+// Structure: 256 threads = 4 waves on a WGM x WGN grid; block tile BM x BN; k-tile of
+// 128 bytes per row (64 fp16/bf16 or 32 fp32 elements); LDS double buffer with register
+// staging, one barrier per k-tile. Each wave owns (BM/WGM) x (BN/WGN) built from 32x32
+// MFMA blocks: v_mfma_f32_32x32x16_{f16,bf16} (8 elements per lane) or four
+// v_mfma_f32_32x32x2_f32 for fp32. A 16-byte LDS fragment per lane feeds either.
+// Because the A and B fragments of a lane always carry the same k indices, the sum over
+// k is exact whatever order the hardware assigns to the k slots.
+#include "kernels.h"
+
+namespace gg {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T> struct Mma;
+template <> struct Mma<f16> {
+  static __device__ __forceinline__ void run(f32x16& acc, u32x4 a, u32x4 b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                 __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
+  }
+};
+template <> struct Mma<bf16> {
+  static __device__ __forceinline__ void run(f32x16& acc, u32x4 a, u32x4 b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+  }
+};
+template <> struct Mma<float> {
+  static __device__ __forceinline__ void run(f32x16& acc, u32x4 a, u32x4 b) {
+    const f32x4 fa = __builtin_bit_cast(f32x4, a), fb = __builtin_bit_cast(f32x4, b);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[0], fb[0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[1], fb[1], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[2], fb[2], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[3], fb[3], acc, 0, 0, 0);
+  }
+};
+
+// 8 floats -> 8 elements of T packed in 16 bytes (round to nearest even).
+template <typename T> __device__ __forceinline__ u32x4 pack8(f32x4 lo, f32x4 hi);
+template <> __device__ __forceinline__ u32x4 pack8<f16>(f32x4 lo, f32x4 hi) {
+  f16x8 h;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { h[i] = (f16)lo[i]; h[4 + i] = (f16)hi[i]; }
+  return __builtin_bit_cast(u32x4, h);
+}
+template <> __device__ __forceinline__ u32x4 pack8<bf16>(f32x4 lo, f32x4 hi) {
+  bf16x8 h;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { h[i] = (bf16)lo[i]; h[4 + i] = (bf16)hi[i]; }
+  return __builtin_bit_cast(u32x4, h);
+}
+
+// 16 int8 weights times one fp16 scale -> 16 fp16 (two 16-byte chunks).
+__device__ __forceinline__ void dequant16(u32x4 q, float s, u32x4& lo, u32x4& hi) {
+  f16x8 a, b;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int v = (int)(int8_t)((q[w] >> (8 * i)) & 0xff);
+      f16 h = (f16)((float)v * s);
+      if (w < 2) a[w * 4 + i] = h; else b[(w - 2) * 4 + i] = h;
+    }
+  }
+  lo = __builtin_bit_cast(u32x4, a);
+  hi = __builtin_bit_cast(u32x4, b);
+}
+
+template <typename T, int BM, int BN, int WGM, int WGN, int AM, bool Q8, int EP>
+__global__ void __launch_bounds__(256) k_gemm(GemmParams p) {
+  constexpr int ES = sizeof(T);
+  constexpr int EPC = 16 / ES;                  // elements per 16-byte chunk
+  constexpr int BKE = 128 / ES;                 // elements per k-tile
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int MI = WTM / 32, NI = WTN / 32;
+  constexpr int LDR = 9;                        // 16-byte slots per LDS row (8 + pad)
+  constexpr int A_CH = BM * 8 / 256;
+  constexpr int B_CH = Q8 ? BN * 4 / 256 : BN * 8 / 256;
+  constexpr bool AF = (AM == A_F32 || AM == A_CONV_F32) && ES == 2;   // float source
+  constexpr bool CONV = (AM == A_CONV || AM == A_CONV_F32);
+  static_assert(WGM * WGN == 4 && MI >= 1 && NI >= 1, "tile");
+  static_assert(A_CH >= 1 && B_CH >= 1, "tile");
+  static_assert(EP != E_GLU || NI % 2 == 0, "GLU needs value/gate block pairs");
+
+  __shared__ u32x4 sA[2][BM][LDR];
+  __shared__ u32x4 sB[2][BN][LDR];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
+  const int KT = p.K / BKE;
+
+  const char* Abase = (const char*)((AM == A_DUAL && n0 >= p.nsplit) ? p.A2 : p.A);
+
+  // ---- per-thread A rows
+  int a_row[A_CH], a_col[A_CH];
+  long a_off[A_CH];
+  int a_lo[A_CH], a_hi[A_CH];
+#pragma unroll
+  for (int i = 0; i < A_CH; ++i) {
+    const int c = tid + 256 * i;
+    a_row[i] = c >> 3;
+    a_col[i] = c & 7;
+    int gm = m0 + a_row[i];
+    gm = gm < p.M ? gm : p.M - 1;
+    if constexpr (CONV) {
+      const int b = p.rowclip[gm];
+      const int s = gm - p.cu_out[b];
+      a_lo[i] = p.cu_in[b];
+      a_hi[i] = p.cu_in[b + 1];
+      a_off[i] = (long)a_lo[i] + 2 * s - 2;     // source row of tap 0
+    } else {
+      a_lo[i] = a_hi[i] = 0;
+      a_off[i] = (long)gm * p.lda;
+    }
+  }
+  // ---- per-thread W rows
+  int b_row[B_CH], b_col[B_CH];
+  long b_off[B_CH];
+#pragma unroll
+  for (int i = 0; i < B_CH; ++i) {
+    const int c = tid + 256 * i;
+    b_row[i] = Q8 ? (c >> 2) : (c >> 3);
+    b_col[i] = Q8 ? (c & 3) : (c & 7);
+    int gn = n0 + b_row[i];
+    gn = gn < p.N ? gn : p.N - 1;
+    b_off[i] = (long)gn * p.ldw;
+  }
+
+  u32x4 ra[A_CH][AF ? 2 : 1];
+  u32x4 rb[B_CH];
+  float rs[B_CH];
+
+  auto load_tile = [&](int kt) {
+    const int kk = kt * BKE;
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+      long src;
+      bool ok = true;
+      if constexpr (CONV) {
+        const int j = kk / p.cin, c0 = kk - j * p.cin;
+        const long r = a_off[i] + j;
+        ok = (r >= a_lo[i]) && (r < a_hi[i]);
+        src = (ok ? r : a_lo[i]) * p.cin + c0 + a_col[i] * EPC;
+      } else {
+        src = a_off[i] + kk + a_col[i] * EPC;
+      }
+      if constexpr (AF) {
+        const f32x4* q = (const f32x4*)((const float*)Abase + src);
+        f32x4 lo = q[0], hi = q[1];
+        if (!ok) { lo = f32x4{0, 0, 0, 0}; hi = lo; }
+        ra[i][0] = __builtin_bit_cast(u32x4, lo);
+        ra[i][1] = __builtin_bit_cast(u32x4, hi);
+      } else {
+        u32x4 v = *(const u32x4*)(Abase + src * ES);
+        if (!ok) v = u32x4{0, 0, 0, 0};
+        ra[i][0] = v;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) {
+      if constexpr (Q8) {
+        rb[i] = *(const u32x4*)((const int8_t*)p.W + b_off[i] + kk + b_col[i] * 16);
+        int gn = n0 + b_row[i];
+        gn = gn < p.N ? gn : p.N - 1;
+        rs[i] = (float)p.Wscale[(long)gn * (p.K / 64) + kt];
+      } else {
+        rb[i] = *(const u32x4*)((const char*)p.W + (b_off[i] + kk + b_col[i] * EPC) * ES);
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+      if constexpr (AF)
+        sA[buf][a_row[i]][a_col[i]] = pack8<T>(__builtin_bit_cast(f32x4, ra[i][0]),
+                                               __builtin_bit_cast(f32x4, ra[i][1]));
+      else
+        sA[buf][a_row[i]][a_col[i]] = ra[i][0];
+    }
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) {
+      if constexpr (Q8) {
+        u32x4 lo, hi;
+        dequant16(rb[i], rs[i], lo, hi);
+        sB[buf][b_row[i]][b_col[i] * 2] = lo;
+        sB[buf][b_row[i]][b_col[i] * 2 + 1] = hi;
+      } else {
+        sB[buf][b_row[i]][b_col[i]] = rb[i];
+      }
+    }
+  };
+
+  f32x16 acc[MI][NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  const int fr = lane & 31, fk = lane >> 5;
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < KT) load_tile(kt + 1);
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      u32x4 af[MI], bfr[NI];
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) af[mi] = sA[cur][wm * WTM + mi * 32 + fr][kc * 2 + fk];
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) bfr[ni] = sB[cur][wn * WTN + ni * 32 + fr][kc * 2 + fk];
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) Mma<T>::run(acc[mi][ni], af[mi], bfr[ni]);
+    }
+    if (kt + 1 < KT) store_tile(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue. 32x32 accumulator: lane holds column (lane & 31) and rows
+  // 8 * (r / 4) + 4 * (lane / 32) + (r % 4) for r = 0..15.
+  const int rbase = m0 + wm * WTM + 4 * (lane >> 5);
+  const int cbase = n0 + wn * WTN + (lane & 31);
+  if constexpr (EP == E_GLU) {
+#pragma unroll
+    for (int q = 0; q < NI / 2; ++q) {
+      const int cv = cbase + 2 * q * 32, cg = cv + 32;
+      const int co = (n0 + wn * WTN) / 2 + q * 32 + (lane & 31);
+      const float bv = p.bias ? p.bias[cv] : 0.f, bg = p.bias ? p.bias[cg] : 0.f;
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = rbase + mi * 32 + 8 * (r >> 2) + (r & 3);
+          if (row < p.M && cv < p.N) {
+            const float v = acc[mi][2 * q][r] + bv, g = acc[mi][2 * q + 1][r] + bg;
+            ((T*)p.C)[(long)row * p.ldc + co] = from_f32<T>(v * sigmoidf_(g));
+          }
+        }
+    }
+  } else {
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      const int col = cbase + ni * 32;
+      const bool cok = col < p.N;
+      const float bb = (p.bias && cok) ? p.bias[col] : 0.f;
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = rbase + mi * 32 + 8 * (r >> 2) + (r & 3);
+          if (row < p.M && cok) {
+            const float v = acc[mi][ni][r] + bb;
+            const long o = (long)row * p.ldc + col;
+            if constexpr (EP == E_STORE) ((T*)p.C)[o] = from_f32<T>(v);
+            else if constexpr (EP == E_SILU) ((T*)p.C)[o] = from_f32<T>(siluf_(v));
+            else if constexpr (EP == E_RELU) ((T*)p.C)[o] = from_f32<T>(fmaxf(v, 0.f));
+            else if constexpr (EP == E_RELU_F32) ((float*)p.C)[o] = fmaxf(v, 0.f);
+            else if constexpr (EP == E_RESID) ((float*)p.C)[o] += p.alpha * v;
+            else ((float*)p.C)[o] = v;
+          }
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// dispatch
+
+template <typename T, int BM, int BN, int WGM, int WGN, bool Q8>
+static hipError_t run_epi(AMode am, Epi ep, const GemmParams& p, hipStream_t s) {
+  dim3 grid((p.M + BM - 1) / BM, (p.N + BN - 1) / BN);
+#define GG_L(AMv, EPv)                                                                   \
+  if (am == AMv && ep == EPv) {                                                          \
+    hipLaunchKernelGGL((k_gemm<T, BM, BN, WGM, WGN, AMv, Q8, EPv>), grid, dim3(256), 0, s, p); \
+    return hipGetLastError();                                                            \
+  }
+  if constexpr (Q8) {
+    GG_L(A_PLAIN, E_SILU) GG_L(A_PLAIN, E_RESID) GG_L(A_DUAL, E_STORE) GG_L(A_PLAIN, E_GLU)
+    GG_L(A_PLAIN, E_F32)
+  } else {
+    GG_L(A_PLAIN, E_STORE) GG_L(A_PLAIN, E_SILU) GG_L(A_PLAIN, E_RESID) GG_L(A_DUAL, E_STORE)
+    GG_L(A_PLAIN, E_GLU) GG_L(A_PLAIN, E_F32) GG_L(A_CONV, E_RELU_F32)
+    if constexpr (sizeof(T) == 2) {
+      GG_L(A_F32, E_F32) GG_L(A_CONV_F32, E_RELU)
+    } else {
+      GG_L(A_CONV, E_RELU)
+    }
+  }
+#undef GG_L
+  return hipErrorInvalidValue;
+}
+
+template <typename T, bool Q8>
+static hipError_t run_tiles(AMode am, Epi ep, const GemmParams& p, hipStream_t s) {
+  if (p.N <= 512 && ep != E_GLU) return run_epi<T, 128, 64, 4, 1, Q8>(am, ep, p, s);
+  return run_epi<T, 128, 128, 2, 2, Q8>(am, ep, p, s);
+}
+
+hipError_t launch_gemm(DType dt, bool w_int8, AMode am, Epi ep, const GemmParams& p,
+                       hipStream_t s) {
+  if (p.M <= 0) return hipSuccess;
+  // fp32 A sources are native for the fp32 GEMM
+  if (dt == DT_F32) {
+    if (am == A_F32) am = A_PLAIN;
+    if (am == A_CONV_F32) am = A_CONV;
+  }
+  switch (dt) {
+    case DT_F32: return run_tiles<float, false>(am, ep, p, s);
+    case DT_F16: return run_tiles<f16, false>(am, ep, p, s);
+    case DT_BF16: return run_tiles<bf16, false>(am, ep, p, s);
+    case DT_W8F16:
+      return w_int8 ? run_tiles<f16, true>(am, ep, p, s) : run_tiles<f16, false>(am, ep, p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gg

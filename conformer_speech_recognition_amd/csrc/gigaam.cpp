@@ -1,0 +1,714 @@
+// Host side of the C ABI declared in include/gigaam.h: argument validation, frame
+// arithmetic, weight repacking, workspace planning and the launch sequence of one
+// encoder forward pass on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "gigaam.h"
+#include "kernels.h"
+
+using namespace gg;
+
+// --------------------------------------------------------------------------- errors
+static thread_local std::string g_err;
+
+static int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define HIP_TRY(expr)                                                                   \
+  do {                                                                                  \
+    hipError_t e_ = (expr);                                                             \
+    if (e_ != hipSuccess)                                                               \
+      return fail(GIGAAM_E_HIP, "%s failed: %s", #expr, hipGetErrorString(e_));       \
+  } while (0)
+
+extern "C" int32_t gigaam_version(void) { return 100; }
+extern "C" const char* gigaam_last_error(void) { return g_err.c_str(); }
+
+// --------------------------------------------------------------------------- frames
+static void frame_counts(int n, int& T, int& S, int& U) {
+  T = (n - 320) / 160 + 1;        // un-centred STFT, window 320, hop 160
+  S = (T + 2 * 2 - 5) / 2 + 1;    // Conv1d k5 s2 p2
+  U = (S + 2 * 2 - 5) / 2 + 1;
+}
+
+extern "C" int gigaam_frames(int32_t n_samples, int32_t* mel, int32_t* sub, int32_t* enc) {
+  if (n_samples < 320) return fail(GIGAAM_E_INVAL, "n_samples %d < 320 (one window)", n_samples);
+  int T, S, U;
+  frame_counts(n_samples, T, S, U);
+  if (mel) *mel = T;
+  if (sub) *sub = S;
+  if (enc) *enc = U;
+  return GIGAAM_OK;
+}
+
+// --------------------------------------------------------------------------- config
+extern "C" int gigaam_check_config(const gigaam_config* c) {
+  if (!c) return fail(GIGAAM_E_INVAL, "config is NULL");
+  if (c->n_mels != 64 || c->n_fft != 320 || c->win_length != 320 || c->hop_length != 160)
+    return fail(GIGAAM_E_UNSUPPORTED, "frontend must be 64 mels, FFT/window 320, hop 160");
+  if (c->sub_kernel != 5 || c->sub_stride != 2)
+    return fail(GIGAAM_E_UNSUPPORTED, "subsampling must be Conv1d kernel 5 stride 2");
+  if (c->n_layers < 1 || c->n_layers > 128) return fail(GIGAAM_E_INVAL, "n_layers %d", c->n_layers);
+  if (c->d_model != 768 && c->d_model != 1024)
+    return fail(GIGAAM_E_UNSUPPORTED, "d_model %d (kernels built for 768 and 1024)", c->d_model);
+  if (c->n_heads != 16) return fail(GIGAAM_E_UNSUPPORTED, "n_heads %d (16 supported)", c->n_heads);
+  if (c->d_ff < 128 || c->d_ff % 128) return fail(GIGAAM_E_UNSUPPORTED, "d_ff %d not a multiple of 128", c->d_ff);
+  if (c->conv_kernel != 31 && c->conv_kernel != 15 && c->conv_kernel != 5)
+    return fail(GIGAAM_E_UNSUPPORTED, "conv_kernel %d (5, 15, 31 built)", c->conv_kernel);
+  if (c->n_classes < 2 || c->n_classes > 8192) return fail(GIGAAM_E_INVAL, "n_classes %d", c->n_classes);
+  if (c->dtype < GIGAAM_F32 || c->dtype > GIGAAM_W8F16) return fail(GIGAAM_E_INVAL, "dtype %d", c->dtype);
+  if (!(c->rope_base > 0.f) || !(c->ln_eps > 0.f) || !(c->bn_eps > 0.f))
+    return fail(GIGAAM_E_INVAL, "rope_base / eps must be positive");
+  return GIGAAM_OK;
+}
+
+// --------------------------------------------------------------------------- canonical list
+namespace {
+
+struct Entry {
+  std::string name;
+  int rank;
+  int shape[3];
+  size_t offset;   // floats
+  size_t count;
+};
+
+const char* kQuantized[] = {"ff1.linear1", "ff1.linear2", "att.linear_q", "att.linear_k",
+                            "att.linear_v", "att.linear_out", "conv.pointwise1",
+                            "conv.pointwise2", "ff2.linear1", "ff2.linear2"};
+
+std::vector<Entry> canonical(const gigaam_config& c) {
+  std::vector<Entry> e;
+  size_t off = 0;
+  auto add = [&](const std::string& n, int r, int a, int b = 0, int d = 0) {
+    Entry x{n, r, {a, b, d}, off, (size_t)a * (r > 1 ? b : 1) * (r > 2 ? d : 1)};
+    off += x.count;
+    e.push_back(x);
+  };
+  const bool q8 = c.dtype == GIGAAM_W8F16;
+  auto lin = [&](const std::string& pre, const char* local, int N, int K) {
+    bool q = false;
+    for (const char* s : kQuantized) q |= (std::strcmp(s, local) == 0);
+    if (q && q8) {
+      add(pre + local + ".weight_q", 2, N, K);
+      add(pre + local + ".weight_scale", 2, N, K / 64);
+    } else {
+      add(pre + local + ".weight", 2, N, K);
+    }
+    add(pre + local + ".bias", 1, N);
+  };
+  const int d = c.d_model, f = c.d_ff, k = c.conv_kernel;
+  add("pre.conv1.weight", 3, d, c.n_mels, c.sub_kernel);
+  add("pre.conv1.bias", 1, d);
+  add("pre.conv2.weight", 3, d, d, c.sub_kernel);
+  add("pre.conv2.bias", 1, d);
+  for (int i = 0; i < c.n_layers; ++i) {
+    const std::string p = "layers." + std::to_string(i) + ".";
+    add(p + "ff1.norm.weight", 1, d);
+    add(p + "ff1.norm.bias", 1, d);
+    lin(p, "ff1.linear1", f, d);
+    lin(p, "ff1.linear2", d, f);
+    add(p + "att.norm.weight", 1, d);
+    add(p + "att.norm.bias", 1, d);
+    lin(p, "att.linear_q", d, d);
+    lin(p, "att.linear_k", d, d);
+    lin(p, "att.linear_v", d, d);
+    lin(p, "att.linear_out", d, d);
+    add(p + "conv.norm.weight", 1, d);
+    add(p + "conv.norm.bias", 1, d);
+    lin(p, "conv.pointwise1", 2 * d, d);
+    add(p + "conv.depthwise.weight", 2, d, k);
+    add(p + "conv.depthwise.bias", 1, d);
+    add(p + "conv.bn.weight", 1, d);
+    add(p + "conv.bn.bias", 1, d);
+    add(p + "conv.bn.running_mean", 1, d);
+    add(p + "conv.bn.running_var", 1, d);
+    lin(p, "conv.pointwise2", d, d);
+    add(p + "ff2.norm.weight", 1, d);
+    add(p + "ff2.norm.bias", 1, d);
+    lin(p, "ff2.linear1", f, d);
+    lin(p, "ff2.linear2", d, f);
+    add(p + "norm_out.weight", 1, d);
+    add(p + "norm_out.bias", 1, d);
+  }
+  add("head.weight", 2, c.n_classes, d);
+  add("head.bias", 1, c.n_classes);
+  return e;
+}
+
+// --------------------------------------------------------------------------- packed layout
+struct Lin { size_t w = 0, s = 0, b = 0; bool q8 = false; };
+struct LayerOff {
+  size_t ff1_g, ff1_b; Lin ff1_1, ff1_2;
+  size_t att_g, att_b; Lin qkv, out;
+  size_t cv_g, cv_b; Lin pw1; size_t dw_w, dw_b, bn_g, bn_b, bn_m, bn_v; Lin pw2;
+  size_t ff2_g, ff2_b; Lin ff2_1, ff2_2;
+  size_t no_g, no_b;
+};
+struct Layout {
+  size_t conv1_w, conv1_b, conv2_w, conv2_b, head_w, head_b;
+  std::vector<LayerOff> layers;
+  size_t total;
+  int wsize;   // bytes per element of non-quantised GEMM weights
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+Layout layout(const gigaam_config& c) {
+  Layout L;
+  const int es = c.dtype == GIGAAM_F32 ? 4 : 2;
+  L.wsize = es;
+  const bool q8 = c.dtype == GIGAAM_W8F16;
+  const size_t d = c.d_model, f = c.d_ff;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+  auto lin = [&](size_t N, size_t K, bool quant) {
+    Lin l;
+    l.q8 = quant && q8;
+    if (l.q8) { l.w = take(N * K); l.s = take(N * (K / 64) * 2); }
+    else l.w = take(N * K * es);
+    l.b = take(N * 4);
+    return l;
+  };
+  L.conv1_w = take(d * 5 * c.n_mels * es);
+  L.conv1_b = take(d * 4);
+  L.conv2_w = take(d * 5 * d * es);
+  L.conv2_b = take(d * 4);
+  for (int i = 0; i < c.n_layers; ++i) {
+    LayerOff o;
+    o.ff1_g = take(d * 4); o.ff1_b = take(d * 4);
+    o.ff1_1 = lin(f, d, true); o.ff1_2 = lin(d, f, true);
+    o.att_g = take(d * 4); o.att_b = take(d * 4);
+    o.qkv = lin(3 * d, d, true); o.out = lin(d, d, true);
+    o.cv_g = take(d * 4); o.cv_b = take(d * 4);
+    o.pw1 = lin(2 * d, d, true);
+    o.dw_w = take(d * c.conv_kernel * 4); o.dw_b = take(d * 4);
+    o.bn_g = take(d * 4); o.bn_b = take(d * 4); o.bn_m = take(d * 4); o.bn_v = take(d * 4);
+    o.pw2 = lin(d, d, true);
+    o.ff2_g = take(d * 4); o.ff2_b = take(d * 4);
+    o.ff2_1 = lin(f, d, true); o.ff2_2 = lin(d, f, true);
+    o.no_g = take(d * 4); o.no_b = take(d * 4);
+    L.layers.push_back(o);
+  }
+  L.head_w = take((size_t)c.n_classes * d * es);
+  L.head_b = take((size_t)c.n_classes * 4);
+  L.total = off;
+  return L;
+}
+
+// ---- host conversions (round to nearest even)
+uint16_t f32_to_f16_bits(float v) {
+  uint32_t x;
+  std::memcpy(&x, &v, 4);
+  const uint32_t sign = (x >> 16) & 0x8000u;
+  const uint32_t ax = x & 0x7fffffffu;
+  if (ax >= 0x7f800000u) return (uint16_t)(sign | 0x7c00u | (ax > 0x7f800000u ? 0x200u : 0u));
+  if (ax >= 0x477ff000u) return (uint16_t)(sign | 0x7c00u);          // rounds to >= 65520
+  if (ax < 0x38800000u) {                                             // fp16 subnormal or 0
+    if (ax < 0x33000000u) return (uint16_t)sign;                      // < 2^-25: rounds to 0
+    const uint32_t mant = (ax & 0x7fffffu) | 0x800000u;
+    const int e = (int)(ax >> 23);                                    // 102..112
+    const int shift = 126 - e;                                        // 14..24
+    uint32_t r = mant >> shift;
+    const uint32_t rem = mant & ((1u << shift) - 1u), halfway = 1u << (shift - 1);
+    if (rem > halfway || (rem == halfway && (r & 1u))) ++r;
+    return (uint16_t)(sign | r);
+  }
+  uint32_t r = ((ax >> 13) - (112u << 10));
+  const uint32_t rem = ax & 0x1fffu;
+  if (rem > 0x1000u || (rem == 0x1000u && (r & 1u))) ++r;
+  return (uint16_t)(sign | r);
+}
+
+uint16_t f32_to_bf16_bits(float v) {
+  uint32_t x;
+  std::memcpy(&x, &v, 4);
+  if ((x & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((x >> 16) | 0x40u);
+  x += 0x7fffu + ((x >> 16) & 1u);
+  return (uint16_t)(x >> 16);
+}
+
+struct Packer {
+  const gigaam_config& c;
+  const float* src;
+  char* dst;
+  std::vector<Entry> ents;
+  int es;
+  int err = 0;
+  const Entry* find(const std::string& n) {
+    for (const Entry& e : ents) if (e.name == n) return &e;
+    return nullptr;
+  }
+  const float* get(const std::string& n) {
+    const Entry* e = find(n);
+    return e ? src + e->offset : nullptr;
+  }
+  void put_w(size_t off, size_t idx, float v) {   // GEMM weight element in storage type
+    if (es == 4) std::memcpy(dst + off + idx * 4, &v, 4);
+    else {
+      const uint16_t h = c.dtype == GIGAAM_BF16 ? f32_to_bf16_bits(v) : f32_to_f16_bits(v);
+      std::memcpy(dst + off + idx * 2, &h, 2);
+    }
+  }
+  void put_f(size_t off, size_t idx, float v) { std::memcpy(dst + off + idx * 4, &v, 4); }
+  void copy_f(size_t off, const std::string& n, size_t count) {
+    const float* s = get(n);
+    for (size_t i = 0; i < count; ++i) put_f(off, i, s[i]);
+  }
+  // Linear weight rows [N][K] from several canonical tensors (row_map gives, for each
+  // packed row, the source tensor index and its row).
+  void linear(const Lin& l, const std::vector<std::string>& names, size_t K,
+              const std::vector<std::pair<int, int>>& row_map) {
+    for (size_t r = 0; r < row_map.size(); ++r) {
+      const std::string& base = names[row_map[r].first];
+      const size_t sr = row_map[r].second;
+      if (l.q8) {
+        const float* q = get(base + ".weight_q");
+        const float* s = get(base + ".weight_scale");
+        for (size_t k = 0; k < K; ++k) {
+          const float v = q[sr * K + k];
+          if (!(v >= -127.f && v <= 127.f) || v != std::nearbyint(v)) err = 1;
+          dst[l.w + r * K + k] = (char)(int8_t)v;
+        }
+        for (size_t g = 0; g < K / 64; ++g) {
+          const uint16_t h = f32_to_f16_bits(s[sr * (K / 64) + g]);
+          std::memcpy(dst + l.s + (r * (K / 64) + g) * 2, &h, 2);
+        }
+      } else {
+        const float* w = get(base + ".weight");
+        for (size_t k = 0; k < K; ++k) put_w(l.w, r * K + k, w[sr * K + k]);
+      }
+      put_f(l.b, r, get(base + ".bias")[sr]);
+    }
+  }
+};
+
+}  // namespace
+
+extern "C" int gigaam_canonical_count(const gigaam_config* cfg, int32_t* n_entries, size_t* n_floats) {
+  int rc = gigaam_check_config(cfg);
+  if (rc) return rc;
+  std::vector<Entry> e = canonical(*cfg);
+  if (n_entries) *n_entries = (int32_t)e.size();
+  if (n_floats) *n_floats = e.back().offset + e.back().count;
+  return GIGAAM_OK;
+}
+
+extern "C" int gigaam_canonical_entry(const gigaam_config* cfg, int32_t i, char* name_buf,
+                                      int32_t name_cap, int32_t* rank, int32_t* shape,
+                                      size_t* offset_floats) {
+  int rc = gigaam_check_config(cfg);
+  if (rc) return rc;
+  std::vector<Entry> e = canonical(*cfg);
+  if (i < 0 || i >= (int)e.size()) return fail(GIGAAM_E_INVAL, "entry %d out of range", i);
+  const Entry& x = e[i];
+  if (name_buf) {
+    if (name_cap <= (int)x.name.size()) return fail(GIGAAM_E_INVAL, "name buffer too small");
+    std::memcpy(name_buf, x.name.c_str(), x.name.size() + 1);
+  }
+  if (rank) *rank = x.rank;
+  if (shape) for (int j = 0; j < 3; ++j) shape[j] = j < x.rank ? x.shape[j] : 0;
+  if (offset_floats) *offset_floats = x.offset;
+  return GIGAAM_OK;
+}
+
+extern "C" int gigaam_packed_bytes(const gigaam_config* cfg, size_t* bytes) {
+  int rc = gigaam_check_config(cfg);
+  if (rc) return rc;
+  if (!bytes) return fail(GIGAAM_E_INVAL, "bytes is NULL");
+  *bytes = layout(*cfg).total;
+  return GIGAAM_OK;
+}
+
+extern "C" int gigaam_pack_weights(const gigaam_config* cfg, const float* canonical_host,
+                                   size_t n_floats, void* packed_host, size_t packed_bytes) {
+  int rc = gigaam_check_config(cfg);
+  if (rc) return rc;
+  if (!canonical_host || !packed_host) return fail(GIGAAM_E_INVAL, "NULL buffer");
+  const gigaam_config& c = *cfg;
+  Packer P{c, canonical_host, (char*)packed_host, canonical(c), c.dtype == GIGAAM_F32 ? 4 : 2};
+  const size_t need = P.ents.back().offset + P.ents.back().count;
+  if (n_floats != need) return fail(GIGAAM_E_INVAL, "canonical buffer has %zu floats, expected %zu", n_floats, need);
+  const Layout L = layout(c);
+  if (packed_bytes < L.total) return fail(GIGAAM_E_INVAL, "packed buffer %zu < %zu bytes", packed_bytes, L.total);
+  std::memset(packed_host, 0, L.total);
+  const size_t d = c.d_model, f = c.d_ff, m = c.n_mels;
+  // subsampling convs: [out][in][5] -> [out][5][in]
+  {
+    const float* w1 = P.get("pre.conv1.weight");
+    for (size_t o = 0; o < d; ++o)
+      for (size_t j = 0; j < 5; ++j)
+        for (size_t ci = 0; ci < m; ++ci) P.put_w(L.conv1_w, (o * 5 + j) * m + ci, w1[(o * m + ci) * 5 + j]);
+    P.copy_f(L.conv1_b, "pre.conv1.bias", d);
+    const float* w2 = P.get("pre.conv2.weight");
+    for (size_t o = 0; o < d; ++o)
+      for (size_t j = 0; j < 5; ++j)
+        for (size_t ci = 0; ci < d; ++ci) P.put_w(L.conv2_w, (o * 5 + j) * d + ci, w2[(o * d + ci) * 5 + j]);
+    P.copy_f(L.conv2_b, "pre.conv2.bias", d);
+  }
+  auto ident = [](int n) {
+    std::vector<std::pair<int, int>> v;
+    for (int i = 0; i < n; ++i) v.push_back({0, i});
+    return v;
+  };
+  for (int i = 0; i < c.n_layers; ++i) {
+    const std::string p = "layers." + std::to_string(i) + ".";
+    const LayerOff& o = L.layers[i];
+    P.copy_f(o.ff1_g, p + "ff1.norm.weight", d); P.copy_f(o.ff1_b, p + "ff1.norm.bias", d);
+    P.linear(o.ff1_1, {p + "ff1.linear1"}, d, ident(f));
+    P.linear(o.ff1_2, {p + "ff1.linear2"}, f, ident(d));
+    P.copy_f(o.att_g, p + "att.norm.weight", d); P.copy_f(o.att_b, p + "att.norm.bias", d);
+    {
+      std::vector<std::pair<int, int>> rm;
+      for (int s = 0; s < 3; ++s) for (size_t r = 0; r < d; ++r) rm.push_back({s, (int)r});
+      P.linear(o.qkv, {p + "att.linear_q", p + "att.linear_k", p + "att.linear_v"}, d, rm);
+    }
+    P.linear(o.out, {p + "att.linear_out"}, d, ident(d));
+    P.copy_f(o.cv_g, p + "conv.norm.weight", d); P.copy_f(o.cv_b, p + "conv.norm.bias", d);
+    {
+      // pointwise-1 rows: each 64-row group = 32 value rows then their 32 gate rows
+      std::vector<std::pair<int, int>> rm;
+      for (size_t q = 0; q < d / 32; ++q) {
+        for (int r = 0; r < 32; ++r) rm.push_back({0, (int)(32 * q + r)});
+        for (int r = 0; r < 32; ++r) rm.push_back({0, (int)(d + 32 * q + r)});
+      }
+      P.linear(o.pw1, {p + "conv.pointwise1"}, d, rm);
+    }
+    P.copy_f(o.dw_w, p + "conv.depthwise.weight", d * c.conv_kernel);
+    P.copy_f(o.dw_b, p + "conv.depthwise.bias", d);
+    P.copy_f(o.bn_g, p + "conv.bn.weight", d); P.copy_f(o.bn_b, p + "conv.bn.bias", d);
+    P.copy_f(o.bn_m, p + "conv.bn.running_mean", d); P.copy_f(o.bn_v, p + "conv.bn.running_var", d);
+    P.linear(o.pw2, {p + "conv.pointwise2"}, d, ident(d));
+    P.copy_f(o.ff2_g, p + "ff2.norm.weight", d); P.copy_f(o.ff2_b, p + "ff2.norm.bias", d);
+    P.linear(o.ff2_1, {p + "ff2.linear1"}, d, ident(f));
+    P.linear(o.ff2_2, {p + "ff2.linear2"}, f, ident(d));
+    P.copy_f(o.no_g, p + "norm_out.weight", d); P.copy_f(o.no_b, p + "norm_out.bias", d);
+  }
+  {
+    const float* w = P.get("head.weight");
+    for (size_t i = 0; i < (size_t)c.n_classes * d; ++i) P.put_w(L.head_w, i, w[i]);
+    P.copy_f(L.head_b, "head.bias", c.n_classes);
+  }
+  if (P.err) return fail(GIGAAM_E_INVAL, "an int8 weight is not an integer in [-127, 127]");
+  return GIGAAM_OK;
+}
+
+extern "C" int gigaam_default_frontend(float* window_dev, float* melfb_dev, void* hip_stream) {
+  if (!window_dev || !melfb_dev) return fail(GIGAAM_E_INVAL, "NULL table pointer");
+  HIP_TRY(launch_default_frontend(window_dev, melfb_dev, (hipStream_t)hip_stream));
+  return GIGAAM_OK;
+}
+
+// --------------------------------------------------------------------------- model
+struct gigaam_model {
+  gigaam_config cfg;
+  const char* w;
+  const float* window;
+  const float* fb;
+  Layout L;
+};
+
+extern "C" int gigaam_create(const gigaam_config* cfg, const void* packed_weights_dev,
+                             const float* window_dev, const float* melfb_dev, gigaam_model** out) {
+  int rc = gigaam_check_config(cfg);
+  if (rc) return rc;
+  if (!packed_weights_dev || !window_dev || !melfb_dev || !out)
+    return fail(GIGAAM_E_INVAL, "NULL pointer argument");
+  if ((uintptr_t)packed_weights_dev & 255) return fail(GIGAAM_E_INVAL, "packed weights not 256-B aligned");
+  gigaam_model* m = new gigaam_model;
+  m->cfg = *cfg;
+  m->w = (const char*)packed_weights_dev;
+  m->window = window_dev;
+  m->fb = melfb_dev;
+  m->L = layout(*cfg);
+  *out = m;
+  return GIGAAM_OK;
+}
+
+extern "C" void gigaam_destroy(gigaam_model* m) { delete m; }
+
+// --------------------------------------------------------------------------- workspace
+namespace {
+
+struct Ws {
+  size_t cuT, cuS, cuU, cuQ, rowT, rowS, rowU, tileQ;
+  size_t mel, h1, x, y, r, qkv, ao, hid, cos_t, sin_t, logits, fids;
+  size_t total;
+};
+
+Ws plan(const gigaam_config& c, int B, int T_tot, int S_tot, int U_tot, int nQ, int U_max) {
+  Ws w;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+  const size_t es = c.dtype == GIGAAM_F32 ? 4 : 2, d = c.d_model;
+  const size_t hidw = (size_t)c.d_ff > 2 * d ? (size_t)c.d_ff : 2 * d;
+  w.cuT = take((B + 1) * 4); w.cuS = take((B + 1) * 4); w.cuU = take((B + 1) * 4); w.cuQ = take((B + 1) * 4);
+  w.rowT = take((size_t)T_tot * 4); w.rowS = take((size_t)S_tot * 4); w.rowU = take((size_t)U_tot * 4);
+  w.tileQ = take((size_t)nQ * 4);
+  w.mel = take((size_t)T_tot * 64 * 4);
+  w.h1 = take((size_t)S_tot * d * es);
+  w.x = take((size_t)U_tot * d * 4);
+  w.y = take((size_t)U_tot * d * es);
+  w.r = take((size_t)U_tot * d * es);
+  w.qkv = take((size_t)U_tot * 3 * d * es);
+  w.ao = take((size_t)U_tot * d * es);
+  w.hid = take((size_t)U_tot * hidw * es);
+  w.cos_t = take((size_t)U_max * (d / c.n_heads / 2) * 4);
+  w.sin_t = take((size_t)U_max * (d / c.n_heads / 2) * 4);
+  w.logits = take((size_t)U_tot * c.n_classes * 4);
+  w.fids = take((size_t)B * U_max * 4);
+  w.total = off;
+  return w;
+}
+
+Ws plan_bound(const gigaam_config& c, int B, int max_samples) {
+  int T, S, U;
+  frame_counts(max_samples, T, S, U);
+  const int nQ = B * ((U + kQTile - 1) / kQTile);
+  return plan(c, B, B * T, B * S, B * U, nQ, U);
+}
+
+}  // namespace
+
+extern "C" int gigaam_workspace_bytes(const gigaam_model* m, int32_t batch, int32_t max_samples,
+                                      size_t* bytes) {
+  if (!m || !bytes) return fail(GIGAAM_E_INVAL, "NULL argument");
+  if (batch < 1 || batch > GIGAAM_MAX_BATCH) return fail(GIGAAM_E_INVAL, "batch %d out of [1, %d]", batch, GIGAAM_MAX_BATCH);
+  if (max_samples < 320) return fail(GIGAAM_E_INVAL, "max_samples %d < 320", max_samples);
+  *bytes = plan_bound(m->cfg, batch, max_samples).total;
+  return GIGAAM_OK;
+}
+
+// --------------------------------------------------------------------------- forward
+namespace {
+
+enum { STAGE_NONE = -1 };
+
+GemmParams gemm(int M, int N, int K, const void* A, int lda, const void* W, const void* scale,
+                const float* bias, void* C, int ldc, float alpha = 1.f) {
+  GemmParams p;
+  std::memset(&p, 0, sizeof p);
+  p.M = M; p.N = N; p.K = K; p.A = A; p.lda = lda; p.W = W; p.ldw = K;
+  p.Wscale = (const f16*)scale; p.bias = bias; p.C = C; p.ldc = ldc; p.alpha = alpha;
+  return p;
+}
+
+int run(gigaam_model* m, const float* pcm, const int32_t* lengths, int32_t B, int32_t stride,
+        void* ws, size_t ws_bytes, int stage, float* stage_out, size_t stage_floats,
+        float* log_probs, int32_t* token_ids, int32_t* n_tokens, int32_t* frame_ids,
+        float* enc_out, int32_t* n_frames, void* stream_v) {
+  if (!m) return fail(GIGAAM_E_INVAL, "model is NULL");
+  if (!pcm || !lengths || !ws) return fail(GIGAAM_E_INVAL, "NULL pcm / lengths / workspace");
+  if (B < 1 || B > GIGAAM_MAX_BATCH) return fail(GIGAAM_E_INVAL, "batch %d out of [1, %d]", B, GIGAAM_MAX_BATCH);
+  if (stride < 320) return fail(GIGAAM_E_INVAL, "pcm_stride %d < 320", stride);
+  if ((uintptr_t)ws & 255) return fail(GIGAAM_E_INVAL, "workspace not 256-B aligned");
+  if (stage == STAGE_NONE && (!log_probs || !token_ids || !n_tokens))
+    return fail(GIGAAM_E_INVAL, "NULL output pointer");
+  const gigaam_config& c = m->cfg;
+  const int d = c.d_model, f = c.d_ff, H = c.n_heads, dk = d / H, C = c.n_classes;
+  const DType dt = (DType)c.dtype;
+  const bool q8 = dt == DT_W8F16;
+  const size_t es = dt == DT_F32 ? 4 : 2;
+  hipStream_t s = (hipStream_t)stream_v;
+
+  // ---- geometry (host)
+  MetaArgs meta;
+  std::memset(&meta, 0, sizeof meta);
+  meta.B = B;
+  int U_max = 0, nQ = 0, maxlen = 0;
+  std::vector<int> Ub(B);
+  for (int b = 0; b < B; ++b) {
+    const int L = lengths[b];
+    if (L < 320 || L > stride)
+      return fail(GIGAAM_E_INVAL, "lengths[%d] = %d outside [320, pcm_stride = %d]", b, L, stride);
+    int T, S, U;
+    frame_counts(L, T, S, U);
+    meta.cuT[b + 1] = meta.cuT[b] + T;
+    meta.cuS[b + 1] = meta.cuS[b] + S;
+    meta.cuU[b + 1] = meta.cuU[b] + U;
+    Ub[b] = U;
+    U_max = U > U_max ? U : U_max;
+    nQ += (U + kQTile - 1) / kQTile;
+    maxlen = L > maxlen ? L : maxlen;
+  }
+  const int T_tot = meta.cuT[B], S_tot = meta.cuS[B], U_tot = meta.cuU[B];
+  const Ws need = plan_bound(c, B, maxlen);
+  if (ws_bytes < need.total)
+    return fail(GIGAAM_E_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need.total);
+  const Ws w = plan(c, B, T_tot, S_tot, U_tot, nQ, U_max);
+  if (stage != STAGE_NONE) {
+    size_t n = 0;
+    if (stage == GIGAAM_STAGE_MEL) n = (size_t)T_tot * 64;
+    else if (stage == GIGAAM_STAGE_SUB || (stage >= GIGAAM_STAGE_LAYER && stage < GIGAAM_STAGE_LAYER + c.n_layers) ||
+             (stage >= 1000 && stage < 1000 + 10 * c.n_layers && stage % 10 < 4))
+      n = (size_t)U_tot * d;
+    else return fail(GIGAAM_E_INVAL, "stage %d out of range", stage);
+    if (!stage_out || stage_floats < n) return fail(GIGAAM_E_INVAL, "stage output too small (%zu < %zu)", stage_floats, n);
+  }
+  if (n_frames) for (int b = 0; b < B; ++b) n_frames[b] = Ub[b];
+
+  char* W = (char*)ws;
+  MetaDev md{(int*)(W + w.cuT), (int*)(W + w.cuS), (int*)(W + w.cuU), (int*)(W + w.cuQ),
+             (int*)(W + w.rowT), (int*)(W + w.rowS), (int*)(W + w.rowU), (int*)(W + w.tileQ)};
+  float* mel = (float*)(W + w.mel);
+  char* h1 = W + w.h1;
+  float* x = (float*)(W + w.x);
+  char* y = W + w.y;
+  char* r = W + w.r;
+  char* qkv = W + w.qkv;
+  char* ao = W + w.ao;
+  char* hid = W + w.hid;
+  char* hid2 = hid + (size_t)U_tot * d * es;
+  float* cos_t = (float*)(W + w.cos_t);
+  float* sin_t = (float*)(W + w.sin_t);
+  float* logits = (float*)(W + w.logits);
+  int* fids = frame_ids ? frame_ids : (int*)(W + w.fids);
+  const char* P = m->w;
+  const Layout& L = m->L;
+  auto copy_out = [&](const float* src, size_t n) -> int {
+    HIP_TRY(hipMemcpyAsync(stage_out, src, n * 4, hipMemcpyDeviceToDevice, s));
+    return GIGAAM_OK;
+  };
+  auto G = [&](AMode am, Epi ep, bool wq, const GemmParams& gp) -> int {
+    HIP_TRY(launch_gemm(dt, wq, am, ep, gp, s));
+    return GIGAAM_OK;
+  };
+  auto lin = [&](const Lin& l, int M, int N, int K, const void* A, int lda, void* Cp, int ldc,
+                 float alpha = 1.f) {
+    return gemm(M, N, K, A, lda, P + l.w, l.q8 ? P + l.s : nullptr, (const float*)(P + l.b), Cp, ldc, alpha);
+  };
+  int rc;
+
+  // ---- geometry to the device
+  HIP_TRY(launch_meta(meta, md, T_tot, S_tot, U_tot, s));
+  // ---- a1 frontend
+  HIP_TRY(launch_frontend(pcm, stride, m->window, m->fb, md, T_tot, mel, s));
+  if (stage == GIGAAM_STAGE_MEL) return copy_out(mel, (size_t)T_tot * 64);
+  // ---- a2, a3 subsampling (implicit-GEMM Conv1d k5 s2 p2 + ReLU)
+  {
+    GemmParams g1 = gemm(S_tot, d, 5 * 64, mel, 0, P + L.conv1_w, nullptr, (const float*)(P + L.conv1_b), h1, d);
+    g1.rowclip = md.rowS; g1.cu_in = md.cuT; g1.cu_out = md.cuS; g1.cin = 64;
+    if ((rc = G(A_CONV_F32, E_RELU, false, g1))) return rc;
+    GemmParams g2 = gemm(U_tot, d, 5 * d, h1, 0, P + L.conv2_w, nullptr, (const float*)(P + L.conv2_b), x, d);
+    g2.rowclip = md.rowU; g2.cu_in = md.cuS; g2.cu_out = md.cuU; g2.cin = d;
+    if ((rc = G(A_CONV, E_RELU_F32, false, g2))) return rc;
+  }
+  if (stage == GIGAAM_STAGE_SUB) return copy_out(x, (size_t)U_tot * d);
+  // ---- a4 rotary tables for positions 0..U_max-1
+  HIP_TRY(launch_rope_table(cos_t, sin_t, U_max, dk, c.rope_base, s));
+
+  LnParams ln;
+  std::memset(&ln, 0, sizeof ln);
+  ln.rows = U_tot; ln.d = d; ln.x = x; ln.eps = c.ln_eps;
+  ln.cos_t = cos_t; ln.sin_t = sin_t; ln.rowclip = md.rowU; ln.cu = md.cuU;
+  auto LN = [&](LnMode mode, size_t g1, size_t b1, const float* g2, const float* b2, void* yo,
+                void* ro) -> int {
+    LnParams q = ln;
+    q.g1 = (const float*)(P + g1); q.b1 = (const float*)(P + b1);
+    q.g2 = g2; q.b2 = b2; q.y = yo; q.r = ro;
+    HIP_TRY(launch_layernorm(dt, mode, q, s));
+    return GIGAAM_OK;
+  };
+  AttnParams ap{qkv, ao, d, H, nQ, md.cuU, md.cuQ, md.tileQ, (float)(1.4426950408889634 / std::sqrt((double)dk))};
+  DwParams dp;
+  dp.in = hid; dp.out = hid2; dp.d = d; dp.n_tiles = nQ; dp.cuU = md.cuU; dp.cuQ = md.cuQ;
+  dp.tileQ = md.tileQ; dp.eps = c.bn_eps;
+
+  if ((rc = LN(LN_PLAIN, L.layers[0].ff1_g, L.layers[0].ff1_b, nullptr, nullptr, y, nullptr))) return rc;
+  for (int li = 0; li < c.n_layers; ++li) {
+    const LayerOff& o = L.layers[li];
+    const int tap = 1000 + 10 * li;
+    // a5 FFN1 (half step)
+    if ((rc = G(A_PLAIN, E_SILU, o.ff1_1.q8, lin(o.ff1_1, U_tot, f, d, y, d, hid, f)))) return rc;
+    if ((rc = G(A_PLAIN, E_RESID, o.ff1_2.q8, lin(o.ff1_2, U_tot, d, f, hid, f, x, d, 0.5f)))) return rc;
+    if (stage == tap + 0) return copy_out(x, (size_t)U_tot * d);
+    // a6-a9 attention: LN + rope(y) -> [Q|K] from r, V from y -> flash attention -> out proj
+    if ((rc = LN(LN_ROPE, o.att_g, o.att_b, nullptr, nullptr, y, r))) return rc;
+    {
+      GemmParams gq = lin(o.qkv, U_tot, 3 * d, d, r, d, qkv, 3 * d);
+      gq.A2 = y; gq.nsplit = 2 * d;
+      if ((rc = G(A_DUAL, E_STORE, o.qkv.q8, gq))) return rc;
+    }
+    HIP_TRY(launch_attention(dt, dk, ap, s));
+    if ((rc = G(A_PLAIN, E_RESID, o.out.q8, lin(o.out, U_tot, d, d, ao, d, x, d)))) return rc;
+    if (stage == tap + 1) return copy_out(x, (size_t)U_tot * d);
+    // a10-a12 conv module
+    if ((rc = LN(LN_PLAIN, o.cv_g, o.cv_b, nullptr, nullptr, y, nullptr))) return rc;
+    if ((rc = G(A_PLAIN, E_GLU, o.pw1.q8, lin(o.pw1, U_tot, 2 * d, d, y, d, hid, d)))) return rc;
+    dp.w = (const float*)(P + o.dw_w); dp.b = (const float*)(P + o.dw_b);
+    dp.bn_g = (const float*)(P + o.bn_g); dp.bn_b = (const float*)(P + o.bn_b);
+    dp.bn_m = (const float*)(P + o.bn_m); dp.bn_v = (const float*)(P + o.bn_v);
+    HIP_TRY(launch_dwconv(dt, c.conv_kernel, dp, s));
+    if ((rc = G(A_PLAIN, E_RESID, o.pw2.q8, lin(o.pw2, U_tot, d, d, hid2, d, x, d)))) return rc;
+    if (stage == tap + 2) return copy_out(x, (size_t)U_tot * d);
+    // a13 FFN2 (half step) + final norm fused with the next block's first pre-norm
+    if ((rc = LN(LN_PLAIN, o.ff2_g, o.ff2_b, nullptr, nullptr, y, nullptr))) return rc;
+    if ((rc = G(A_PLAIN, E_SILU, o.ff2_1.q8, lin(o.ff2_1, U_tot, f, d, y, d, hid, f)))) return rc;
+    if ((rc = G(A_PLAIN, E_RESID, o.ff2_2.q8, lin(o.ff2_2, U_tot, d, f, hid, f, x, d, 0.5f)))) return rc;
+    if (stage == tap + 3) return copy_out(x, (size_t)U_tot * d);
+    if (li + 1 < c.n_layers) {
+      const LayerOff& nx = L.layers[li + 1];
+      if ((rc = LN(LN_TWO, o.no_g, o.no_b, (const float*)(P + nx.ff1_g), (const float*)(P + nx.ff1_b), y, nullptr))) return rc;
+    } else {
+      if ((rc = LN(LN_TWO, o.no_g, o.no_b, nullptr, nullptr, nullptr, nullptr))) return rc;
+    }
+    if (stage == GIGAAM_STAGE_LAYER + li) return copy_out(x, (size_t)U_tot * d);
+  }
+  // ---- a14 CTC head + log-softmax + argmax, a15 greedy collapse
+  {
+    GemmParams gh = gemm(U_tot, C, d, x, d, P + L.head_w, nullptr, (const float*)(P + L.head_b), logits, C);
+    if ((rc = G(A_F32, E_F32, false, gh))) return rc;
+  }
+  HIP_TRY(launch_logsoftmax_argmax(logits, C, B, U_max, md.cuU, log_probs, fids, s));
+  HIP_TRY(launch_collapse(fids, B, U_max, md.cuU, C - 1, token_ids, n_tokens, s));
+  if (enc_out) HIP_TRY(launch_scatter_rows(x, d, B, U_max, md.cuU, enc_out, s));
+  return GIGAAM_OK;
+}
+
+}  // namespace
+
+extern "C" int gigaam_encode(gigaam_model* model, const float* pcm_dev, const int32_t* lengths_host,
+                             int32_t batch, int32_t pcm_stride, void* workspace, size_t workspace_bytes,
+                             float* log_probs_dev, int32_t* token_ids_dev, int32_t* n_tokens_dev,
+                             int32_t* frame_ids_dev, float* enc_out_dev, int32_t* n_frames_host,
+                             void* hip_stream) {
+  return run(model, pcm_dev, lengths_host, batch, pcm_stride, workspace, workspace_bytes, STAGE_NONE,
+             nullptr, 0, log_probs_dev, token_ids_dev, n_tokens_dev, frame_ids_dev, enc_out_dev,
+             n_frames_host, hip_stream);
+}
+
+extern "C" int gigaam_encode_stage(gigaam_model* model, const float* pcm_dev, const int32_t* lengths_host,
+                                   int32_t batch, int32_t pcm_stride, void* workspace,
+                                   size_t workspace_bytes, int32_t stage, float* out_dev,
+                                   size_t out_floats, void* hip_stream) {
+  if (stage < 0) return fail(GIGAAM_E_INVAL, "stage %d out of range", stage);
+  return run(model, pcm_dev, lengths_host, batch, pcm_stride, workspace, workspace_bytes, stage,
+             out_dev, out_floats, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, hip_stream);
+}
+
+extern "C" int gigaam_debug_gemm(int32_t dtype, int32_t M, int32_t N, int32_t K, const void* A_dev,
+                                 const void* W_dev, const void* scale_dev, const float* bias_dev,
+                                 float* C_dev, void* hip_stream) {
+  if (dtype < GIGAAM_F32 || dtype > GIGAAM_W8F16) return fail(GIGAAM_E_INVAL, "dtype %d", dtype);
+  if (M < 1 || N < 1 || K < 1) return fail(GIGAAM_E_INVAL, "bad shape %d x %d x %d", M, N, K);
+  if (K % (dtype == GIGAAM_F32 ? 32 : 64)) return fail(GIGAAM_E_INVAL, "K %d not a multiple of the k-tile", K);
+  if (!A_dev || !W_dev || !C_dev || (dtype == GIGAAM_W8F16 && !scale_dev))
+    return fail(GIGAAM_E_INVAL, "NULL pointer");
+  GemmParams p = gemm(M, N, K, A_dev, K, W_dev, scale_dev, bias_dev, C_dev, N);
+  HIP_TRY(launch_gemm((DType)dtype, dtype == GIGAAM_W8F16, A_PLAIN, E_F32, p, (hipStream_t)hip_stream));
+  return GIGAAM_OK;
+}

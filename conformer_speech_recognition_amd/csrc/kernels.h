@@ -1,0 +1,99 @@
+// Internal launcher interface between the host orchestration and the kernels.
+#pragma once
+#include "common.h"
+
+namespace gg {
+
+// ---- GEMM: C[m, n] = epilogue( sum_k A[m, k] * W[n, k] + bias[n] ) -------------------
+enum AMode {
+  A_PLAIN = 0,     // A: T [M][lda]
+  A_F32 = 1,       // A: float [M][lda], rounded to T while staging
+  A_DUAL = 2,      // A for output columns < nsplit, A2 for the rest (both T)
+  A_CONV = 3,      // implicit Conv1d k5 s2 p2 over packed clips, source T [rows][cin]
+  A_CONV_F32 = 4   // same, source float
+};
+enum Epi {
+  E_STORE = 0,     // C (T)      = acc + b
+  E_SILU = 1,      // C (T)      = silu(acc + b)
+  E_RELU = 2,      // C (T)      = relu(acc + b)
+  E_RELU_F32 = 3,  // C (float)  = relu(acc + b)
+  E_GLU = 4,       // C (T) [M][N/2]: value/gate pairs of 32-column blocks
+  E_RESID = 5,     // C (float) += alpha * (acc + b)
+  E_F32 = 6        // C (float)  = acc + b
+};
+
+struct GemmParams {
+  int M, N, K;
+  const void* A; int lda;
+  const void* A2; int nsplit;
+  const void* W; int ldw;          // [N][ldw], T or int8
+  const f16* Wscale;               // int8 weights: [N][K/64] fp16 scales
+  const float* bias;               // [N] or nullptr
+  void* C; int ldc;
+  float alpha;
+  const int* rowclip;              // conv modes: clip of each output row
+  const int* cu_in;                // conv modes: input row offsets per clip
+  const int* cu_out;               // conv modes: output row offsets per clip
+  int cin;                         // conv modes: input channels (row length of source)
+};
+
+hipError_t launch_gemm(DType dt, bool w_int8, AMode am, Epi ep, const GemmParams& p,
+                       hipStream_t s);
+
+// ---- meta -------------------------------------------------------------------------
+hipError_t launch_meta(const MetaArgs& a, const MetaDev& m, int T_tot, int S_tot, int U_tot,
+                       hipStream_t s);
+
+// ---- frontend -----------------------------------------------------------------------
+hipError_t launch_frontend(const float* pcm, int stride, const float* window, const float* fb,
+                           const MetaDev& m, int T_tot, float* mel, hipStream_t s);
+hipError_t launch_default_frontend(float* window, float* fb, hipStream_t s);
+
+// ---- norms / rotary -----------------------------------------------------------------
+enum LnMode { LN_PLAIN = 0, LN_ROPE = 1, LN_TWO = 2 };
+struct LnParams {
+  int rows, d;
+  float* x;                        // [rows][d] fp32 (LN_TWO writes x back in place)
+  const float* g1; const float* b1;
+  const float* g2; const float* b2;  // LN_TWO: second norm applied to the first's output
+  void* y;                         // T out
+  void* r;                         // LN_ROPE: rotated copy (T)
+  const float* cos_t; const float* sin_t;  // [U_max][d_k/2]
+  const int* rowclip; const int* cu;       // encoder-space clip map (for positions)
+  float eps;
+};
+hipError_t launch_layernorm(DType dt, LnMode mode, const LnParams& p, hipStream_t s);
+hipError_t launch_rope_table(float* cos_t, float* sin_t, int n_pos, int dk, float base,
+                             hipStream_t s);
+
+// ---- attention ----------------------------------------------------------------------
+struct AttnParams {
+  const void* qkv;                 // T [rows][3d]: q | k | v
+  void* out;                       // T [rows][d]
+  int d, n_heads, n_tiles;
+  const int* cuU; const int* cuQ; const int* tileQ;
+  float scale_log2;                // log2(e) / sqrt(d_k)
+};
+hipError_t launch_attention(DType dt, int dk, const AttnParams& p, hipStream_t s);
+
+// ---- conv module: depthwise + BatchNorm + SiLU --------------------------------------
+struct DwParams {
+  const void* in; void* out;       // T [rows][d]
+  const float* w; const float* b;  // [d][K], [d]
+  const float* bn_g; const float* bn_b; const float* bn_m; const float* bn_v;
+  int d, n_tiles;
+  const int* cuU; const int* cuQ; const int* tileQ;
+  float eps;
+};
+hipError_t launch_dwconv(DType dt, int kernel, const DwParams& p, hipStream_t s);
+
+// ---- CTC head -----------------------------------------------------------------------
+hipError_t launch_logsoftmax_argmax(const float* logits, int C, int B, int U_max,
+                                    const int* cuU, float* logp, int* frame_ids,
+                                    hipStream_t s);
+hipError_t launch_collapse(const int* frame_ids, int B, int U_max, const int* cuU, int blank,
+                           int* tokens, int* n_tokens, hipStream_t s);
+hipError_t launch_scatter_rows(const float* x, int d, int B, int U_max, const int* cuU,
+                               float* out, hipStream_t s);
+
+}  // namespace gg

@@ -1,0 +1,53 @@
+// Batch geometry on the device: clip offsets and row -> clip maps of the packed
+// mel (T), first-conv (S) and encoder (U) row spaces, plus the 64-frame q-tiles.
+// Variable-length clips are packed back to back so every per-frame kernel touches valid
+// frames only (batched chunks with masks: "GigaAM MLX port for Mac", section "What is
+// inside the model").
+#include "kernels.h"
+
+namespace gg {
+
+__device__ __forceinline__ int find_clip(const int* cu, int B, int r) {
+  int lo = 0, hi = B - 1;                 // largest b with cu[b] <= r
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= r) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__global__ void __launch_bounds__(256) k_meta(MetaArgs a, MetaDev m, int T_tot, int S_tot,
+                                              int U_tot) {
+  __shared__ int cuQ[kMaxBatch + 1];
+  if (threadIdx.x == 0) {
+    int q = 0;
+    for (int b = 0; b < a.B; ++b) {
+      cuQ[b] = q;
+      q += (a.cuU[b + 1] - a.cuU[b] + kQTile - 1) / kQTile;
+    }
+    cuQ[a.B] = q;
+  }
+  __syncthreads();
+  const int nQ = cuQ[a.B];
+  const int gid = blockIdx.x * blockDim.x + threadIdx.x;
+  if (blockIdx.x == 0) {
+    for (int b = threadIdx.x; b <= a.B; b += blockDim.x) {
+      m.cuT[b] = a.cuT[b]; m.cuS[b] = a.cuS[b]; m.cuU[b] = a.cuU[b]; m.cuQ[b] = cuQ[b];
+    }
+  }
+  const int stride = gridDim.x * blockDim.x;
+  for (int r = gid; r < T_tot; r += stride) m.rowT[r] = find_clip(a.cuT, a.B, r);
+  for (int r = gid; r < S_tot; r += stride) m.rowS[r] = find_clip(a.cuS, a.B, r);
+  for (int r = gid; r < U_tot; r += stride) m.rowU[r] = find_clip(a.cuU, a.B, r);
+  for (int r = gid; r < nQ; r += stride) m.tileQ[r] = find_clip(cuQ, a.B, r);
+}
+
+hipError_t launch_meta(const MetaArgs& a, const MetaDev& m, int T_tot, int S_tot, int U_tot,
+                       hipStream_t s) {
+  int blocks = (T_tot + 255) / 256;
+  blocks = blocks < 1 ? 1 : (blocks > 512 ? 512 : blocks);
+  hipLaunchKernelGGL(k_meta, dim3(blocks), dim3(256), 0, s, a, m, T_tot, S_tot, U_tot);
+  return hipGetLastError();
+}
+
+}  // namespace gg

@@ -1,0 +1,209 @@
+/*
+ * gigaam.h - C ABI of the MI355X (gfx950) Conformer CTC encoder forward pass.
+ *
+ * The path (pages cited by title and section):
+ *   PCM 16 kHz -> log-mel frontend (window 320, hop 160, FFT 320, 64 HTK mel bins,
+ *       no centring, log(clip(x, 1e-9, 1e9)))          ["GigaAM v3 MLX" card, Frontend
+ *                                                      configuration; "GigaAM v3 RNNT - MLX"
+ *                                                      card, Notes for other runtimes]
+ *   -> two Conv1d, kernel 5, stride 2 (4x fewer frames) ["GigaAM on MLX: the transcripts
+ *                                                      matched, but the model was broken",
+ *                                                      What we're porting]
+ *   -> N Conformer blocks: FFN, rotary self-attention with the rotation (base 5000)
+ *      applied to the per-head LayerNorm output BEFORE linear_q/linear_k and value not
+ *      rotated, convolution module, FFN               [same page, Trap 1 and Trap 2;
+ *                                                      "GigaAM MLX port for Mac", What is
+ *                                                      inside the model]
+ *   -> CTC linear + log-softmax, greedy collapse with blank = n_classes - 1
+ *                                                     ["GigaAM v3 RNNT - MLX" card, Notes]
+ *
+ * Conventions for every entry point
+ *   - Returns GIGAAM_OK (0) or a negative error code; no exception crosses the ABI.
+ *     gigaam_last_error() then holds a message (thread-local, valid until the next
+ *     call on the same thread).
+ *   - All argument checks happen before the first GPU launch, so a failed call leaves
+ *     every output untouched.
+ *   - "dev" pointers are device memory on the current HIP device; "host" pointers are
+ *     host memory. The caller allocates and owns every buffer; the library never calls
+ *     hipMalloc. A model handle borrows its device pointers: they must outlive it.
+ *   - Device work is enqueued on the caller's hip_stream (NULL = default stream) and
+ *     is complete when that stream is; host-side outputs are written before return.
+ *   - A model handle is immutable after creation: concurrent encodes are allowed when
+ *     each uses its own workspace and stream.
+ */
+#ifndef GIGAAM_H
+#define GIGAAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  GIGAAM_OK = 0,
+  GIGAAM_E_INVAL = -1,       /* bad argument (null pointer, size out of range ...) */
+  GIGAAM_E_WORKSPACE = -2,   /* workspace smaller than gigaam_workspace_bytes()     */
+  GIGAAM_E_UNSUPPORTED = -3, /* shape/dtype this build has no kernel for            */
+  GIGAAM_E_HIP = -4          /* a HIP runtime call or launch failed                  */
+};
+
+/* Arithmetic of the encoder GEMMs and attention. Residual stream, norms, soft-max,
+ * frontend and head soft-max are always fp32.                                        */
+enum {
+  GIGAAM_F32 = 0,    /* fp32 weights and operands (fp32 MFMA)                         */
+  GIGAAM_F16 = 1,    /* fp16 weights and GEMM/attention operands, fp32 accumulate     */
+  GIGAAM_BF16 = 2,   /* bf16 weights and operands, fp32 accumulate                    */
+  GIGAAM_W8F16 = 3   /* FFN, attention and pointwise-conv linears stored as int8 with
+                        one fp16 scale per group of 64 input weights, dequantised
+                        in-kernel to fp16; everything else as GIGAAM_F16             */
+};
+
+/* Largest batch one gigaam_encode call accepts. */
+#define GIGAAM_MAX_BATCH 256
+
+typedef struct gigaam_config {
+  int32_t n_layers;     /* Conformer blocks (16 for v3, 24 for the multilingual model) */
+  int32_t d_model;      /* 768 or 1024; multiple of 64                                 */
+  int32_t n_heads;      /* 16; d_model / n_heads must be 48 or 64                      */
+  int32_t d_ff;         /* FFN width (4 d_model); multiple of 64                       */
+  int32_t conv_kernel;  /* depthwise kernel, odd, <= 63 (31)                           */
+  int32_t n_classes;    /* CTC classes including blank; blank id = n_classes - 1      */
+  int32_t n_mels;       /* 64   (fixed)                                                */
+  int32_t n_fft;        /* 320  (fixed)                                                */
+  int32_t win_length;   /* 320  (fixed)                                                */
+  int32_t hop_length;   /* 160  (fixed)                                                */
+  int32_t sub_kernel;   /* 5    (fixed; padding 2)                                     */
+  int32_t sub_stride;   /* 2    (fixed)                                                */
+  int32_t dtype;        /* GIGAAM_F32 ... GIGAAM_W8F16                                 */
+  float rope_base;      /* 5000                                                        */
+  float ln_eps;         /* LayerNorm epsilon (1e-5)                                    */
+  float bn_eps;         /* BatchNorm epsilon (1e-5)                                    */
+} gigaam_config;
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int32_t gigaam_version(void);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* gigaam_last_error(void);
+
+/* Host arithmetic, no GPU: frame counts of one clip of n_samples samples.
+ * mel = floor((n - 320)/160) + 1 (un-centred STFT), sub = floor((mel - 1)/2) + 1,
+ * enc = floor((sub - 1)/2) + 1 (each Conv1d k5 s2 p2). Any output pointer may be NULL.
+ * Error: GIGAAM_E_INVAL if n_samples < 320.                                           */
+int gigaam_frames(int32_t n_samples, int32_t* mel_frames, int32_t* sub_frames,
+                  int32_t* enc_frames);
+
+/* Validate a configuration (same checks as gigaam_create). */
+int gigaam_check_config(const gigaam_config* cfg);
+
+/* ---------------------------------------------------------------------------------
+ * Weights.
+ * A checkpoint is handed over as one host float32 "canonical" buffer: the tensors
+ * listed by gigaam_canonical_entry, concatenated in that order, each in PyTorch layout
+ * (Linear [out, in]; Conv1d [out, in, K]; pointwise convs [out, in]; depthwise
+ * [channels, K]), holding the checkpoint values exactly (fp16/bf16 values for those
+ * dtypes; for GIGAAM_W8F16 the quantised linears appear as "<name>.weight_q" holding
+ * integers in [-127, 127] and "<name>.weight_scale" [out, in/64] holding fp16 values).
+ * gigaam_pack_weights turns it into the device layout (host -> host); the caller
+ * copies the packed bytes to the device and passes that pointer to gigaam_create.
+ * ------------------------------------------------------------------------------- */
+
+/* Number of canonical tensors and total float count of the canonical buffer. */
+int gigaam_canonical_count(const gigaam_config* cfg, int32_t* n_entries, size_t* n_floats);
+
+/* Entry i: name (NUL-terminated, written to name_buf of name_cap bytes), rank (1..3),
+ * shape (up to 3 dims) and float offset in the canonical buffer.                     */
+int gigaam_canonical_entry(const gigaam_config* cfg, int32_t i, char* name_buf,
+                           int32_t name_cap, int32_t* rank, int32_t* shape,
+                           size_t* offset_floats);
+
+/* Size in bytes of the packed device blob. */
+int gigaam_packed_bytes(const gigaam_config* cfg, size_t* bytes);
+
+/* Host-side repacking: casts (round-to-nearest-even) to the kernel storage type,
+ * transposes subsampling convs to [out, K, in], interleaves the pointwise-1 rows so
+ * each 64-row group holds 32 value rows followed by their 32 gate rows, concatenates
+ * q/k/v. canonical: host float[n_floats]; packed: host buffer of packed_bytes.
+ * Errors: GIGAAM_E_INVAL on size mismatch or an int8 value outside [-127, 127].      */
+int gigaam_pack_weights(const gigaam_config* cfg, const float* canonical_host,
+                        size_t n_floats, void* packed_host, size_t packed_bytes);
+
+/* ---------------------------------------------------------------------------------
+ * Frontend tables. The STFT window [win_length] and mel filterbank
+ * [n_fft/2 + 1][n_mels] are model data ("port the matrix": "GigaAM on MLX ...",
+ * Trap 3). This fills them on the device with the defaults: periodic Hann and an HTK
+ * triangular bank on [0, 8000] Hz without normalisation, computed in fp64 on the GPU.
+ * window_dev: float[320]; melfb_dev: float[161 * 64] row-major [bin][mel].           */
+int gigaam_default_frontend(float* window_dev, float* melfb_dev, void* hip_stream);
+
+/* ---------------------------------------------------------------------------------
+ * Model handle.
+ * packed_weights_dev: device copy of the gigaam_pack_weights output (256-B aligned).
+ * window_dev, melfb_dev: device frontend tables as above (any values allowed).
+ * ------------------------------------------------------------------------------- */
+typedef struct gigaam_model gigaam_model;
+
+int gigaam_create(const gigaam_config* cfg, const void* packed_weights_dev,
+                  const float* window_dev, const float* melfb_dev, gigaam_model** out);
+void gigaam_destroy(gigaam_model* model);
+
+/* Bytes of device workspace one call needs for `batch` clips of at most max_samples
+ * samples each (an upper bound over all length mixes).                               */
+int gigaam_workspace_bytes(const gigaam_model* model, int32_t batch, int32_t max_samples,
+                           size_t* bytes);
+
+/* ---------------------------------------------------------------------------------
+ * Encode a padded batch.
+ *   pcm_dev      float [batch][pcm_stride] 16 kHz samples; clip b uses its first
+ *                lengths_host[b] samples (the rest is never read).
+ *   lengths_host int32 [batch], each in [320, pcm_stride].
+ *   batch        1 .. GIGAAM_MAX_BATCH.
+ *   workspace    device scratch of at least gigaam_workspace_bytes(model, batch,
+ *                max(lengths)) bytes, 256-B aligned; contents need no initialisation.
+ * Outputs (U_b = encoder frames of clip b, U_max = max_b U_b):
+ *   log_probs_dev  float [batch][U_max][n_classes] CTC log-probabilities; rows t >= U_b
+ *                  are 0.
+ *   token_ids_dev  int32 [batch][U_max] greedy CTC tokens of clip b (argmax per frame,
+ *                  lowest index on ties, repeats merged, then blanks removed), -1 padded.
+ *   n_tokens_dev   int32 [batch] number of tokens of each clip.
+ *   frame_ids_dev  int32 [batch][U_max] per-frame argmax, -1 padded; may be NULL.
+ *   enc_out_dev    float [batch][U_max][d_model] encoder output; rows t >= U_b are 0;
+ *                  may be NULL.
+ *   n_frames_host  int32 [batch] receives U_b; may be NULL.
+ * Errors: GIGAAM_E_INVAL (null pointer, batch or a length out of range),
+ *         GIGAAM_E_WORKSPACE, GIGAAM_E_HIP.                                          */
+int gigaam_encode(gigaam_model* model, const float* pcm_dev, const int32_t* lengths_host,
+                  int32_t batch, int32_t pcm_stride, void* workspace, size_t workspace_bytes,
+                  float* log_probs_dev, int32_t* token_ids_dev, int32_t* n_tokens_dev,
+                  int32_t* frame_ids_dev, float* enc_out_dev, int32_t* n_frames_host,
+                  void* hip_stream);
+
+/* Stage taps for parity diagnostics: run the path up to `stage` and copy that
+ * tensor, packed over clips (rows of clip b follow those of clip b-1), as float32:
+ *   GIGAAM_STAGE_MEL     [sum_b T_b][n_mels]     log-mel
+ *   GIGAAM_STAGE_SUB     [sum_b U_b][d_model]    subsampling output
+ *   GIGAAM_STAGE_LAYER+i [sum_b U_b][d_model]    output of Conformer block i
+ * out_dev must hold out_floats floats (at least the tensor size).                    */
+enum { GIGAAM_STAGE_MEL = 0, GIGAAM_STAGE_SUB = 1, GIGAAM_STAGE_LAYER = 2 };
+int gigaam_encode_stage(gigaam_model* model, const float* pcm_dev, const int32_t* lengths_host,
+                        int32_t batch, int32_t pcm_stride, void* workspace,
+                        size_t workspace_bytes, int32_t stage, float* out_dev,
+                        size_t out_floats, void* hip_stream);
+
+/* ---------------------------------------------------------------------------------
+ * Diagnostics: the encoder's GEMM kernel on its own,
+ *   C[m][n] = sum_k A[m][k] * W[n][k] + bias[n]      (fp32 accumulate, fp32 out)
+ * A_dev [M][K] and W_dev [N][K] in the storage type of `dtype` (GIGAAM_F32: float,
+ * GIGAAM_F16: fp16, GIGAAM_BF16: bf16; GIGAAM_W8F16: A fp16, W int8 with scale_dev
+ * [N][K/64] fp16 scales); bias_dev float[N] or NULL; C_dev float [M][N].
+ * K must be a multiple of 64 (32 for GIGAAM_F32). Errors: GIGAAM_E_INVAL, GIGAAM_E_HIP. */
+int gigaam_debug_gemm(int32_t dtype, int32_t M, int32_t N, int32_t K, const void* A_dev,
+                      const void* W_dev, const void* scale_dev, const float* bias_dev,
+                      float* C_dev, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GIGAAM_H */

@@ -190,4 +190,5 @@ def quantize_int8_g64(w: np.ndarray, group: int = 64) -> tuple[np.ndarray, np.nd
     return q, s
 
 
-from .workloads import WORKLOADS, workload  # noqa: E402,F401
+from .workloads import (WORKLOADS, workload, workload_config,  # noqa: E402,F401
+                        workload_signals, workload_weights)

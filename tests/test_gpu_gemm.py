@@ -1,0 +1,58 @@
+"""GPU: the encoder's MFMA GEMM alone (through gigaam_debug_gemm) against a float64
+matmul of the same stored operands, for every operand type and ragged shapes."""
+import numpy as np
+import pytest
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [(1, 34, 64), (77, 200, 320), (300, 768, 768), (129, 1536, 256), (513, 257, 128),
+          (64, 64, 3840)]
+
+
+def _operands(dtype, M, N, K, seed):
+    import torch
+    rng = np.random.default_rng(seed)
+    a = rng.standard_normal((M, K)).astype(np.float32)
+    w = (0.05 * rng.standard_normal((N, K))).astype(np.float32)
+    b = rng.standard_normal(N).astype(np.float32)
+    scale = None
+    if dtype == "f32":
+        A, W = torch.from_numpy(a), torch.from_numpy(w)
+        w_eff = w.astype(np.float64)
+    elif dtype == "f16":
+        A, W = torch.from_numpy(a).half(), torch.from_numpy(w).half()
+        a, w_eff = A.float().numpy(), W.float().double().numpy()
+    elif dtype == "bf16":
+        a = synth.round_to_bf16(a)
+        w = synth.round_to_bf16(w)
+        A, W = torch.from_numpy(a).bfloat16(), torch.from_numpy(w).bfloat16()
+        w_eff = w.astype(np.float64)
+    else:  # int8 weights with one fp16 scale per 64 inputs, dequantised to fp16 in-kernel
+        A = torch.from_numpy(a).half()
+        a = A.float().numpy()
+        q, s = synth.quantize_int8_g64(synth.round_to_f16(w))
+        W = torch.from_numpy(q)
+        scale = torch.from_numpy(s)
+        deq = q.astype(np.float32) * np.repeat(s.astype(np.float32), 64, axis=1)
+        w_eff = deq.astype(np.float16).astype(np.float64)
+    return A.cuda(), W.cuda(), (scale.cuda() if scale is not None else None), \
+        torch.from_numpy(b).cuda(), a.astype(np.float64), w_eff, b.astype(np.float64)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "w8f16"])
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_gemm_matches_float64(dtype, M, N, K):
+    import conformer_speech_recognition_amd as gg
+    if dtype == "w8f16" and K % 64:
+        pytest.skip("int8 groups need K % 64 == 0")
+    print(f"[gemm] {dtype} M={M} N={N} K={K}", flush=True)
+    A, W, S, bias, a, w, b = _operands(dtype, M, N, K, seed=M * 7 + N + K)
+    C = gg.debug_gemm(dtype, A, W, bias=bias, scale=S).cpu().numpy().astype(np.float64)
+    ref = a @ w.T + b
+    # fp32 accumulation of K exact products: |err| <= K * 2^-24 * sum|a||w| (loose)
+    bound = 1e-6 * K * np.abs(a).max() * np.abs(w).max() + 1e-5
+    err = np.abs(C - ref).max()
+    print(f"[gemm] {dtype} {M}x{N}x{K} max|d| = {err:.3e} (bound {bound:.2e})", flush=True)
+    assert err <= bound
