@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Throughput of the gfx950 Conformer CTC encoder: encoder audio-seconds per second
+(x realtime) on one GPU, with the fraction of the fp16 MFMA roofline.
+
+One step = one gigaam_encode call over the whole workload batch: log-mel frontend,
+subsampling, all Conformer blocks, CTC log-softmax, argmax and greedy collapse. The PCM
+is already resident in HBM when the timed region starts. Inputs and weights are
+synthetic (seeded), with the shapes of the workload.
+
+Prints ONE JSON line. Besides the throughput it carries
+  roofline      the dominant kernel's algorithmic FLOPs (or bytes) per launch divided by
+                its average launch time, measured here with HIP events recorded around
+                each launch on the encode stream (library profiler), against the MI355X
+                dense peak of its operand type;
+  cpu_baseline  the CPU oracle (float64 NumPy) timed on a bounded sample of the same
+                workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "w8f16": 2516.6, "f32": 157.3}   # dense MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "encoder audio-sec/sec (x realtime) at 1 GPU + % of fp16 MFMA roofline"
+
+
+def frames(n):
+    T = (n - 320) // 160 + 1
+    S = (T - 1) // 2 + 1
+    U = (S - 1) // 2 + 1
+    return T, S, U
+
+
+def role_flops(cfg, lens):
+    """Algorithmic FLOPs per launch of each kernel role (valid frames only)."""
+    d, f, k, C = cfg["d_model"], cfg["d_ff"], cfg["conv_kernel"], cfg["n_classes"]
+    fr = [frames(int(n)) for n in lens]
+    S = sum(x[1] for x in fr)
+    U = sum(x[2] for x in fr)
+    U2 = sum(x[2] ** 2 for x in fr)
+    return {
+        "gemm.conv1": 2 * S * 320 * d,
+        "gemm.conv2": 2 * U * 5 * d * d,
+        "gemm.ffn_up": 2 * U * d * f,
+        "gemm.ffn_down": 2 * U * f * d,
+        "gemm.qkv": 2 * U * d * 3 * d,
+        "gemm.out_proj": 2 * U * d * d,
+        "gemm.pw1_glu": 2 * U * d * 2 * d,
+        "gemm.pw2": 2 * U * d * d,
+        "gemm.head": 2 * U * d * C,
+        "attention": 4 * U2 * d,
+        "dwconv_bn_silu": 2 * U * d * k,
+    }
+
+
+def total_flops(cfg, lens):
+    r = role_flops(cfg, lens)
+    per_layer = (2 * r["gemm.ffn_up"] + 2 * r["gemm.ffn_down"] + r["gemm.qkv"] + r["gemm.out_proj"]
+                 + r["gemm.pw1_glu"] + r["gemm.pw2"] + r["attention"] + r["dwconv_bn_silu"])
+    return cfg["n_layers"] * per_layer + r["gemm.conv1"] + r["gemm.conv2"] + r["gemm.head"]
+
+
+def role_bytes(cfg, lens):
+    """Algorithmic HBM bytes per launch of the bandwidth-bound roles (16-bit operands,
+    fp32 residual stream): read what the step needs once, write its result once."""
+    d, C = cfg["d_model"], cfg["n_classes"]
+    es = 4 if cfg["dtype"] == "f32" else 2
+    fr = [frames(int(n)) for n in lens]
+    T = sum(x[0] for x in fr)
+    U = sum(x[2] for x in fr)
+    B, Umax = len(lens), max(x[2] for x in fr)
+    return {
+        "frontend": int(sum(int(n) for n in lens)) * 4 + T * 64 * 4,
+        "layernorm": U * d * (4 + es),
+        "layernorm_rope": U * d * (4 + 2 * es),
+        "layernorm_two": U * d * (8 + es),
+        "dwconv_bn_silu": U * d * 2 * es,
+        "logsoftmax_argmax": U * C * 4 + B * Umax * (C * 4 + 4),
+    }
+
+
+def cpu_baseline(name, budget_s):
+    """The oracle as it stands (float64 NumPy, this host's BLAS threads) on the first
+    clips of the workload until about budget_s seconds of CPU time are spent."""
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count()
+    cfg, pcm, lens, w = synth.workload(name)
+    P = oracle.materialize(w)
+    done, audio, t0 = [], 0.0, time.perf_counter()
+    order = np.argsort(lens)          # shortest clips first keeps the sample bounded
+    for b in order:
+        oracle.encode_clip(pcm[b, : int(lens[b])], w, cfg, P=P)
+        done.append(int(b))
+        audio += lens[b] / 16000.0
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(audio / dt, 3), "unit": "audio-s/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"float64 oracle on {len(done)} of {len(lens)} clips of workload {name} "
+                      f"({audio:.2f} s of audio in {dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="batch32")
+    ap.add_argument("--profile-steps", type=int, default=5)
+    ap.add_argument("--graph", action="store_true", help="replay the encode as a captured graph")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {a.gpus}); the "
+              "encoder shards as independent clips per GPU with no exchange, and no multi-GPU "
+              "figure is produced here.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import conformer_speech_recognition_amd as gg
+    import synth
+
+    cfg, pcm, lens, w = synth.workload(a.workload)
+    model = gg.Model(cfg, w)
+    pcm_d = torch.from_numpy(pcm).cuda()
+    audio_s = float(lens.sum()) / 16000.0
+    stream = torch.cuda.current_stream()
+
+    def step():
+        return model.encode(pcm_d, lens, want_frame_ids=False)
+
+    if a.graph:
+        for _ in range(2):
+            step()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        run = g.replay
+    else:
+        run = step
+    for _ in range(a.warmup):
+        run()
+    torch.cuda.synchronize()
+
+    # ---- timed region
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(a.steps):
+        run()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    step_ms = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(a.steps)])
+
+    # ---- per-kernel launch times (HIP events around every launch, eager encodes)
+    gg.profile_start()
+    for _ in range(a.profile_steps):
+        step()
+    torch.cuda.synchronize()
+    gg.profile_stop()
+    prof = gg.profile_report()
+
+    flops = total_flops(cfg, lens)
+    rf = role_flops(cfg, lens)
+    rb = role_bytes(cfg, lens)
+    dom = max(prof, key=lambda r: r["total_ms"])
+    name = dom["name"]
+    if name in rf and (name.startswith("gemm") or name == "attention"):
+        achieved = rf[name] / (dom["avg_us"] * 1e-6) / 1e12
+        peak = PEAK_TFLOPS[cfg["dtype"]]
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4)}
+    else:
+        achieved = rb[name] / (dom["avg_us"] * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roof.update({"kernel": name, "avg_launch_us": dom["avg_us"], "launches": dom["launches"],
+                 "traffic": None})
+
+    ms = 1e3 * elapsed / a.steps
+    value = a.steps * audio_s / elapsed
+    tflops = flops / (ms * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "audio-s/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg["dtype"],
+        "data": "synthetic",
+        "config": {"workload": a.workload, "clips": int(len(lens)), "audio_seconds": round(audio_s, 3),
+                   "encoder_frames": int(sum(frames(int(n))[2] for n in lens)),
+                   "global_batch": int(len(lens)), "graph_replay": bool(a.graph)},
+        "encoder_tflops": round(tflops, 2),
+        "fp16_mfma_roofline_frac": round(tflops / PEAK_TFLOPS["f16"], 4),
+        "step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 4) for q in (10, 50, 90)],
+        "roofline": roof,
+        "kernels": sorted(({"name": r["name"], "launches": r["launches"], "avg_us": r["avg_us"],
+                            "total_ms": round(r["total_ms"] / a.profile_steps, 4)} for r in prof),
+                          key=lambda r: -r["total_ms"]),
+    }
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(a.workload, a.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -77,6 +77,9 @@ _SIGNATURES = {
     "gigaam_encode": (ctypes.c_int, [_P, _P, _IP, _I, _I, _P, _SZ, _P, _P, _P, _P, _P, _IP, _P]),
     "gigaam_encode_stage": (ctypes.c_int, [_P, _P, _IP, _I, _I, _P, _SZ, _I, _P, _SZ, _P]),
     "gigaam_debug_gemm": (ctypes.c_int, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
+    "gigaam_profile_start": (ctypes.c_int, []),
+    "gigaam_profile_stop": (ctypes.c_int, []),
+    "gigaam_profile_report": (ctypes.c_int, [ctypes.c_char_p, _SZ]),
 }
 
 
@@ -277,3 +280,19 @@ def debug_gemm(dtype: str, A, W, bias=None, scale=None, stream=None):
     _check(lib().gigaam_debug_gemm(DTYPES[dtype], M, N, K, A.data_ptr(), W.data_ptr(), _ptr(scale),
                                    _ptr(bias), C.data_ptr(), s))
     return C
+
+
+def profile_start():
+    _check(lib().gigaam_profile_start())
+
+
+def profile_stop():
+    _check(lib().gigaam_profile_stop())
+
+
+def profile_report() -> list[dict]:
+    """Per-kernel-role launch statistics of the encodes issued while profiling."""
+    import json
+    buf = ctypes.create_string_buffer(1 << 16)
+    _check(lib().gigaam_profile_report(buf, len(buf)))
+    return json.loads(buf.value.decode())

@@ -35,6 +35,82 @@ static int fail(int code, const char* fmt, ...) {
       return fail(GIGAAM_E_HIP, "%s failed: %s", #expr, hipGetErrorString(e_));       \
   } while (0)
 
+// --------------------------------------------------------------------------- profiler
+// Diagnostics only: when on, every launch of an encode is bracketed by HIP events on the
+// caller's stream; gigaam_profile_report aggregates them per kernel role.
+namespace {
+struct ProfRec { const char* name; hipEvent_t a, b; };
+struct Profiler {
+  bool on = false;
+  std::vector<hipEvent_t> pool;
+  size_t used = 0;
+  std::vector<ProfRec> recs;
+  hipEvent_t next() {
+    if (used == pool.size()) {
+      hipEvent_t e = nullptr;
+      if (hipEventCreate(&e) != hipSuccess) return nullptr;
+      pool.push_back(e);
+    }
+    return pool[used++];
+  }
+};
+Profiler g_prof;
+}  // namespace
+
+// Launch `expr` (a hipError_t expression), timing it when the profiler is on.
+#define LAUNCH(name, expr)                                                              \
+  do {                                                                                  \
+    hipEvent_t a_ = nullptr;                                                            \
+    if (g_prof.on && (a_ = g_prof.next())) hipEventRecord(a_, s);                       \
+    HIP_TRY(expr);                                                                      \
+    if (a_) {                                                                           \
+      hipEvent_t b_ = g_prof.next();                                                    \
+      if (b_) { hipEventRecord(b_, s); g_prof.recs.push_back({name, a_, b_}); }         \
+    }                                                                                   \
+  } while (0)
+
+extern "C" int gigaam_profile_start(void) {
+  g_prof.used = 0;
+  g_prof.recs.clear();
+  g_prof.on = true;
+  return GIGAAM_OK;
+}
+
+extern "C" int gigaam_profile_stop(void) {
+  g_prof.on = false;
+  return GIGAAM_OK;
+}
+
+extern "C" int gigaam_profile_report(char* buf, size_t cap) {
+  if (!buf || cap == 0) return fail(GIGAAM_E_INVAL, "NULL report buffer");
+  struct Agg { std::string name; int n; double tot, mn, mx; };
+  std::vector<Agg> agg;
+  for (const ProfRec& r : g_prof.recs) {
+    float ms = 0.f;
+    HIP_TRY(hipEventSynchronize(r.b));
+    HIP_TRY(hipEventElapsedTime(&ms, r.a, r.b));
+    Agg* a = nullptr;
+    for (Agg& x : agg) if (x.name == r.name) a = &x;
+    if (!a) { agg.push_back({r.name, 0, 0.0, 1e30, 0.0}); a = &agg.back(); }
+    a->n += 1; a->tot += ms; a->mn = ms < a->mn ? ms : a->mn; a->mx = ms > a->mx ? ms : a->mx;
+  }
+  std::string js = "[";
+  for (size_t i = 0; i < agg.size(); ++i) {
+    char line[256];
+    snprintf(line, sizeof line, "%s{\"name\": \"%s\", \"launches\": %d, \"total_ms\": %.6f, "
+             "\"avg_us\": %.3f, \"min_us\": %.3f, \"max_us\": %.3f}", i ? ", " : "",
+             agg[i].name.c_str(), agg[i].n, agg[i].tot, 1e3 * agg[i].tot / agg[i].n,
+             1e3 * agg[i].mn, 1e3 * agg[i].mx);
+    js += line;
+  }
+  js += "]";
+  g_prof.used = 0;
+  g_prof.recs.clear();
+  if (js.size() + 1 > cap) return fail(GIGAAM_E_INVAL, "report needs %zu bytes", js.size() + 1);
+  std::memcpy(buf, js.c_str(), js.size() + 1);
+  return GIGAAM_OK;
+}
+
 extern "C" int32_t gigaam_version(void) { return 100; }
 extern "C" const char* gigaam_last_error(void) { return g_err.c_str(); }
 
@@ -583,8 +659,8 @@ int run(gigaam_model* m, const float* pcm, const int32_t* lengths, int32_t B, in
     HIP_TRY(hipMemcpyAsync(stage_out, src, n * 4, hipMemcpyDeviceToDevice, s));
     return GIGAAM_OK;
   };
-  auto G = [&](AMode am, Epi ep, bool wq, const GemmParams& gp) -> int {
-    HIP_TRY(launch_gemm(dt, wq, am, ep, gp, s));
+  auto G = [&](const char* name, AMode am, Epi ep, bool wq, const GemmParams& gp) -> int {
+    LAUNCH(name, launch_gemm(dt, wq, am, ep, gp, s));
     return GIGAAM_OK;
   };
   auto lin = [&](const Lin& l, int M, int N, int K, const void* A, int lda, void* Cp, int ldc,
@@ -594,22 +670,22 @@ int run(gigaam_model* m, const float* pcm, const int32_t* lengths, int32_t B, in
   int rc;
 
   // ---- geometry to the device
-  HIP_TRY(launch_meta(meta, md, T_tot, S_tot, U_tot, s));
+  LAUNCH("meta", launch_meta(meta, md, T_tot, S_tot, U_tot, s));
   // ---- a1 frontend
-  HIP_TRY(launch_frontend(pcm, stride, m->window, m->fb, md, T_tot, mel, s));
+  LAUNCH("frontend", launch_frontend(pcm, stride, m->window, m->fb, md, T_tot, mel, s));
   if (stage == GIGAAM_STAGE_MEL) return copy_out(mel, (size_t)T_tot * 64);
   // ---- a2, a3 subsampling (implicit-GEMM Conv1d k5 s2 p2 + ReLU)
   {
     GemmParams g1 = gemm(S_tot, d, 5 * 64, mel, 0, P + L.conv1_w, nullptr, (const float*)(P + L.conv1_b), h1, d);
     g1.rowclip = md.rowS; g1.cu_in = md.cuT; g1.cu_out = md.cuS; g1.cin = 64;
-    if ((rc = G(A_CONV_F32, E_RELU, false, g1))) return rc;
+    if ((rc = G("gemm.conv1", A_CONV_F32, E_RELU, false, g1))) return rc;
     GemmParams g2 = gemm(U_tot, d, 5 * d, h1, 0, P + L.conv2_w, nullptr, (const float*)(P + L.conv2_b), x, d);
     g2.rowclip = md.rowU; g2.cu_in = md.cuS; g2.cu_out = md.cuU; g2.cin = d;
-    if ((rc = G(A_CONV, E_RELU_F32, false, g2))) return rc;
+    if ((rc = G("gemm.conv2", A_CONV, E_RELU_F32, false, g2))) return rc;
   }
   if (stage == GIGAAM_STAGE_SUB) return copy_out(x, (size_t)U_tot * d);
   // ---- a4 rotary tables for positions 0..U_max-1
-  HIP_TRY(launch_rope_table(cos_t, sin_t, U_max, dk, c.rope_base, s));
+  LAUNCH("rope_table", launch_rope_table(cos_t, sin_t, U_max, dk, c.rope_base, s));
 
   LnParams ln;
   std::memset(&ln, 0, sizeof ln);
@@ -620,7 +696,8 @@ int run(gigaam_model* m, const float* pcm, const int32_t* lengths, int32_t B, in
     LnParams q = ln;
     q.g1 = (const float*)(P + g1); q.b1 = (const float*)(P + b1);
     q.g2 = g2; q.b2 = b2; q.y = yo; q.r = ro;
-    HIP_TRY(launch_layernorm(dt, mode, q, s));
+    LAUNCH(mode == LN_ROPE ? "layernorm_rope" : mode == LN_TWO ? "layernorm_two" : "layernorm",
+           launch_layernorm(dt, mode, q, s));
     return GIGAAM_OK;
   };
   AttnParams ap{qkv, ao, d, H, nQ, md.cuU, md.cuQ, md.tileQ, (float)(1.4426950408889634 / std::sqrt((double)dk))};
@@ -633,32 +710,32 @@ int run(gigaam_model* m, const float* pcm, const int32_t* lengths, int32_t B, in
     const LayerOff& o = L.layers[li];
     const int tap = 1000 + 10 * li;
     // a5 FFN1 (half step)
-    if ((rc = G(A_PLAIN, E_SILU, o.ff1_1.q8, lin(o.ff1_1, U_tot, f, d, y, d, hid, f)))) return rc;
-    if ((rc = G(A_PLAIN, E_RESID, o.ff1_2.q8, lin(o.ff1_2, U_tot, d, f, hid, f, x, d, 0.5f)))) return rc;
+    if ((rc = G("gemm.ffn_up", A_PLAIN, E_SILU, o.ff1_1.q8, lin(o.ff1_1, U_tot, f, d, y, d, hid, f)))) return rc;
+    if ((rc = G("gemm.ffn_down", A_PLAIN, E_RESID, o.ff1_2.q8, lin(o.ff1_2, U_tot, d, f, hid, f, x, d, 0.5f)))) return rc;
     if (stage == tap + 0) return copy_out(x, (size_t)U_tot * d);
     // a6-a9 attention: LN + rope(y) -> [Q|K] from r, V from y -> flash attention -> out proj
     if ((rc = LN(LN_ROPE, o.att_g, o.att_b, nullptr, nullptr, y, r))) return rc;
     {
       GemmParams gq = lin(o.qkv, U_tot, 3 * d, d, r, d, qkv, 3 * d);
       gq.A2 = y; gq.nsplit = 2 * d;
-      if ((rc = G(A_DUAL, E_STORE, o.qkv.q8, gq))) return rc;
+      if ((rc = G("gemm.qkv", A_DUAL, E_STORE, o.qkv.q8, gq))) return rc;
     }
-    HIP_TRY(launch_attention(dt, dk, ap, s));
-    if ((rc = G(A_PLAIN, E_RESID, o.out.q8, lin(o.out, U_tot, d, d, ao, d, x, d)))) return rc;
+    LAUNCH("attention", launch_attention(dt, dk, ap, s));
+    if ((rc = G("gemm.out_proj", A_PLAIN, E_RESID, o.out.q8, lin(o.out, U_tot, d, d, ao, d, x, d)))) return rc;
     if (stage == tap + 1) return copy_out(x, (size_t)U_tot * d);
     // a10-a12 conv module
     if ((rc = LN(LN_PLAIN, o.cv_g, o.cv_b, nullptr, nullptr, y, nullptr))) return rc;
-    if ((rc = G(A_PLAIN, E_GLU, o.pw1.q8, lin(o.pw1, U_tot, 2 * d, d, y, d, hid, d)))) return rc;
+    if ((rc = G("gemm.pw1_glu", A_PLAIN, E_GLU, o.pw1.q8, lin(o.pw1, U_tot, 2 * d, d, y, d, hid, d)))) return rc;
     dp.w = (const float*)(P + o.dw_w); dp.b = (const float*)(P + o.dw_b);
     dp.bn_g = (const float*)(P + o.bn_g); dp.bn_b = (const float*)(P + o.bn_b);
     dp.bn_m = (const float*)(P + o.bn_m); dp.bn_v = (const float*)(P + o.bn_v);
-    HIP_TRY(launch_dwconv(dt, c.conv_kernel, dp, s));
-    if ((rc = G(A_PLAIN, E_RESID, o.pw2.q8, lin(o.pw2, U_tot, d, d, hid2, d, x, d)))) return rc;
+    LAUNCH("dwconv_bn_silu", launch_dwconv(dt, c.conv_kernel, dp, s));
+    if ((rc = G("gemm.pw2", A_PLAIN, E_RESID, o.pw2.q8, lin(o.pw2, U_tot, d, d, hid2, d, x, d)))) return rc;
     if (stage == tap + 2) return copy_out(x, (size_t)U_tot * d);
     // a13 FFN2 (half step) + final norm fused with the next block's first pre-norm
     if ((rc = LN(LN_PLAIN, o.ff2_g, o.ff2_b, nullptr, nullptr, y, nullptr))) return rc;
-    if ((rc = G(A_PLAIN, E_SILU, o.ff2_1.q8, lin(o.ff2_1, U_tot, f, d, y, d, hid, f)))) return rc;
-    if ((rc = G(A_PLAIN, E_RESID, o.ff2_2.q8, lin(o.ff2_2, U_tot, d, f, hid, f, x, d, 0.5f)))) return rc;
+    if ((rc = G("gemm.ffn_up", A_PLAIN, E_SILU, o.ff2_1.q8, lin(o.ff2_1, U_tot, f, d, y, d, hid, f)))) return rc;
+    if ((rc = G("gemm.ffn_down", A_PLAIN, E_RESID, o.ff2_2.q8, lin(o.ff2_2, U_tot, d, f, hid, f, x, d, 0.5f)))) return rc;
     if (stage == tap + 3) return copy_out(x, (size_t)U_tot * d);
     if (li + 1 < c.n_layers) {
       const LayerOff& nx = L.layers[li + 1];
@@ -671,11 +748,11 @@ int run(gigaam_model* m, const float* pcm, const int32_t* lengths, int32_t B, in
   // ---- a14 CTC head + log-softmax + argmax, a15 greedy collapse
   {
     GemmParams gh = gemm(U_tot, C, d, x, d, P + L.head_w, nullptr, (const float*)(P + L.head_b), logits, C);
-    if ((rc = G(A_F32, E_F32, false, gh))) return rc;
+    if ((rc = G("gemm.head", A_F32, E_F32, false, gh))) return rc;
   }
-  HIP_TRY(launch_logsoftmax_argmax(logits, C, B, U_max, md.cuU, log_probs, fids, s));
-  HIP_TRY(launch_collapse(fids, B, U_max, md.cuU, C - 1, token_ids, n_tokens, s));
-  if (enc_out) HIP_TRY(launch_scatter_rows(x, d, B, U_max, md.cuU, enc_out, s));
+  LAUNCH("logsoftmax_argmax", launch_logsoftmax_argmax(logits, C, B, U_max, md.cuU, log_probs, fids, s));
+  LAUNCH("ctc_collapse", launch_collapse(fids, B, U_max, md.cuU, C - 1, token_ids, n_tokens, s));
+  if (enc_out) LAUNCH("scatter_enc_out", launch_scatter_rows(x, d, B, U_max, md.cuU, enc_out, s));
   return GIGAAM_OK;
 }
 

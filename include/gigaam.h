@@ -203,6 +203,16 @@ int gigaam_debug_gemm(int32_t dtype, int32_t M, int32_t N, int32_t K, const void
                       const void* W_dev, const void* scale_dev, const float* bias_dev,
                       float* C_dev, void* hip_stream);
 
+/* Diagnostics: per-kernel timing. Between gigaam_profile_start and _stop every launch
+ * of gigaam_encode is bracketed by HIP events recorded on the caller's stream (the
+ * events add a little stream overhead). gigaam_profile_report waits for those events
+ * and writes a JSON array of {name, launches, total_ms, avg_us, min_us, max_us} per
+ * kernel role into buf (cap bytes), then clears the record. Process-wide state, one
+ * profiling thread at a time. Errors: GIGAAM_E_INVAL (buffer too small), GIGAAM_E_HIP. */
+int gigaam_profile_start(void);
+int gigaam_profile_stop(void);
+int gigaam_profile_report(char* buf, size_t cap);
+
 #ifdef __cplusplus
 }
 #endif
