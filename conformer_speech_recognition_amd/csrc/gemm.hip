@@ -73,6 +73,110 @@ __device__ __forceinline__ void dequant16(u32x4 q, float s, u32x4& lo, u32x4& hi
   hi = __builtin_bit_cast(u32x4, b);
 }
 
+// Tile order. Workgroups are dispatched round-robin over the 8 XCDs (workgroup i runs on
+// XCD i % 8), each XCD with its own L2. Give every XCD a contiguous range of tiles, and
+// walk each range in groups of GM tile-rows, so the workgroups that are resident on one
+// XCD at the same time share their A rows and W rows through that XCD's L2.
+constexpr int kXcds = 8;
+constexpr int kGroupM = 8;
+
+__device__ __forceinline__ void tile_coords(int bid, int nM, int nN, int& tm, int& tn) {
+  const int total = nM * nN;
+  const int q = total / kXcds, r = total % kXcds;
+  const int x = bid % kXcds, j = bid / kXcds;
+  const int t = x * q + (x < r ? x : r) + j;          // bijective: XCD x owns a contiguous range
+  const int group = kGroupM * nN;
+  const int g = t / group, first = g * kGroupM;
+  const int rows = (nM - first) < kGroupM ? (nM - first) : kGroupM;
+  const int w = t - g * group;
+  tm = first + w % rows;
+  tn = w / rows;
+}
+
+// Epilogue of a wave's (32 MI) x (32 NI) accumulator tile whose first row is rm and first
+// column cn. 32x32 MFMA accumulator: lane holds column (lane & 31) and rows
+// 8 * (r / 4) + 4 * (lane / 32) + (r % 4), r = 0..15. GLU pairs column block 2q (value)
+// with 2q + 1 (gate); their output column starts at cglu / 2.
+template <typename T, int MI, int NI, int EP>
+__device__ __forceinline__ void epilogue(const GemmParams& p, f32x16 (&acc)[MI][NI], int rm, int cn,
+                                         int cglu, int lane) {
+  const int rbase = rm + 4 * (lane >> 5);
+  const int cbase = cn + (lane & 31);
+  if constexpr (EP == E_GLU) {
+#pragma unroll
+    for (int q = 0; q < NI / 2; ++q) {
+      const int cv = cbase + 2 * q * 32, cg = cv + 32;
+      const int co = cglu / 2 + q * 32 + (lane & 31);
+      if (cv >= p.N) continue;
+      const float bv = p.bias ? p.bias[cv] : 0.f, bg = p.bias ? p.bias[cg] : 0.f;
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = rbase + mi * 32 + 8 * (r >> 2) + (r & 3);
+          if (row < p.M) {
+            const float v = acc[mi][2 * q][r] + bv, g = acc[mi][2 * q + 1][r] + bg;
+            ((T*)p.C)[(long)row * p.ldc + co] = from_f32<T>(v * sigmoidf_(g));
+          }
+        }
+    }
+  } else if constexpr (EP == E_RESID) {
+    // x += alpha * (acc + b): issue every residual load of the lane first, then the stores,
+    // so the read-modify-write costs one memory round trip instead of MI * NI * 16.
+    float* X = (float*)p.C;
+    float old[MI][NI][16];
+    const bool full = rm + 32 * MI <= p.M;
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      const int col = cbase + ni * 32;
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = rbase + mi * 32 + 8 * (r >> 2) + (r & 3);
+          old[mi][ni][r] = (col < p.N && (full || row < p.M)) ? X[(long)row * p.ldc + col] : 0.f;
+        }
+    }
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      const int col = cbase + ni * 32;
+      if (col >= p.N) continue;
+      const float bb = p.bias ? p.bias[col] : 0.f;
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = rbase + mi * 32 + 8 * (r >> 2) + (r & 3);
+          if (full || row < p.M)
+            X[(long)row * p.ldc + col] = old[mi][ni][r] + p.alpha * (acc[mi][ni][r] + bb);
+        }
+    }
+  } else {
+    const bool full = rm + 32 * MI <= p.M;
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      const int col = cbase + ni * 32;
+      if (col >= p.N) continue;
+      const float bb = p.bias ? p.bias[col] : 0.f;
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = rbase + mi * 32 + 8 * (r >> 2) + (r & 3);
+          if (full || row < p.M) {
+            const float v = acc[mi][ni][r] + bb;
+            const long o = (long)row * p.ldc + col;
+            if constexpr (EP == E_STORE) ((T*)p.C)[o] = from_f32<T>(v);
+            else if constexpr (EP == E_SILU) ((T*)p.C)[o] = from_f32<T>(siluf_(v));
+            else if constexpr (EP == E_RELU) ((T*)p.C)[o] = from_f32<T>(fmaxf(v, 0.f));
+            else if constexpr (EP == E_RELU_F32) ((float*)p.C)[o] = fmaxf(v, 0.f);
+            else ((float*)p.C)[o] = v;
+          }
+        }
+    }
+  }
+}
+
 template <typename T, int BM, int BN, int WGM, int WGN, int AM, bool Q8, int EP>
 __global__ void __launch_bounds__(256) k_gemm(GemmParams p) {
   constexpr int ES = sizeof(T);
@@ -94,7 +198,9 @@ __global__ void __launch_bounds__(256) k_gemm(GemmParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
-  const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
+  int tm, tn;
+  tile_coords(blockIdx.x, (p.M + BM - 1) / BM, (p.N + BN - 1) / BN, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
   const int KT = p.K / BKE;
 
   const char* Abase = (const char*)((AM == A_DUAL && n0 >= p.nsplit) ? p.A2 : p.A);
@@ -230,51 +336,121 @@ __global__ void __launch_bounds__(256) k_gemm(GemmParams p) {
     __syncthreads();
   }
 
-  // ---- epilogue. 32x32 accumulator: lane holds column (lane & 31) and rows
-  // 8 * (r / 4) + 4 * (lane / 32) + (r % 4) for r = 0..15.
-  const int rbase = m0 + wm * WTM + 4 * (lane >> 5);
-  const int cbase = n0 + wn * WTN + (lane & 31);
-  if constexpr (EP == E_GLU) {
+  epilogue<T, MI, NI, EP>(p, acc, m0 + wm * WTM, n0 + wn * WTN, n0 + wn * WTN, lane);
+}
+
+// ---------------------------------------------------------------------------------------
+// Pipelined fp16/bf16 GEMM with direct global->LDS loads (gfx950 global_load_lds_dwordx4):
+// one 64-lane load instruction drops 1 KiB straight into LDS (lane i -> bytes 16i..16i+15),
+// with no staging registers and no LDS store instructions. S k-tiles are in flight; a
+// k-tile is consumed after `s_waitcnt vmcnt` (own loads) and a barrier (everyone's).
+// LDS rows hold one k-tile (64 or 32 k-elements); their 16-byte chunks are XOR-swizzled by a
+// row key so the fragment reads of 16 consecutive rows hit 16 different bank groups.
+//
+// The loads are issued from inline asm because the compiler, not knowing which LDS stage
+// a DMA targets, waits for all of them (vmcnt(0)) before any LDS read; the waits below
+// are exact instead. The asm has no register outputs.
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ void dma16(uint32_t lds, const void* g) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory");
+}
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <typename T, int BM, int BN, int WGM, int WGN, int S, int KB, int AM, int EP>
+__global__ void __launch_bounds__(64 * WGM * WGN) k_gemm_dl(GemmParams p) {
+  constexpr int NW = WGM * WGN;                 // waves per block
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int MI = WTM / 32, NI = WTN / 32;
+  constexpr int RB = KB * 2;                    // bytes of one LDS row (KB k-elements)
+  constexpr int CPR = RB / 16;                  // 16-byte chunks per row (4 or 8)
+  constexpr int RPI = 1024 / RB;                // rows filled by one 1-KiB load instruction
+  // LDS serves a ds_read_b128 16 lanes at a time over 64 four-byte banks (256 B): the 16
+  // rows a fragment read touches per cycle must land on 16 different 16-byte slots of a
+  // 256-byte window. Rows of RB bytes repeat that window every 256 / RB rows, so the
+  // chunk XOR key is (row / (256 / RB)) mod CPR.
+  constexpr int SWS = (RB == 128) ? 1 : 2;      // swizzle key: (row >> SWS) & (CPR - 1)
+  constexpr int ROWS = BM + BN;
+  constexpr int STAGE = ROWS * RB;
+  constexpr int LPW = ROWS / RPI / NW;          // load instructions per wave per k-tile
+  static_assert(KB == 32 || KB == 64, "k-tile");
+  static_assert(MI >= 1 && NI >= 1 && LPW * RPI * NW == ROWS && S >= 2, "tile");
+  static_assert(LPW * (S - 2) <= 63, "vmcnt range");
+  static_assert(EP != E_GLU || NI % 2 == 0, "GLU needs value/gate block pairs");
+  __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WGN, wn = wave % WGN;
+  int tm, tn;
+  tile_coords(blockIdx.x, (p.M + BM - 1) / BM, (p.N + BN - 1) / BN, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int KT = p.K / KB;
+  const char* Ab = (const char*)((AM == A_DUAL && n0 >= p.nsplit) ? p.A2 : p.A);
+
+  // load plan: instruction i of this wave fills stage rows RPI * (wave * LPW + i) + ...;
+  // lane -> row R = base + lane / CPR, physical chunk lane % CPR = logical chunk ^ key(R)
+  const char* src[LPW];
 #pragma unroll
-    for (int q = 0; q < NI / 2; ++q) {
-      const int cv = cbase + 2 * q * 32, cg = cv + 32;
-      const int co = (n0 + wn * WTN) / 2 + q * 32 + (lane & 31);
-      const float bv = p.bias ? p.bias[cv] : 0.f, bg = p.bias ? p.bias[cg] : 0.f;
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = rbase + mi * 32 + 8 * (r >> 2) + (r & 3);
-          if (row < p.M && cv < p.N) {
-            const float v = acc[mi][2 * q][r] + bv, g = acc[mi][2 * q + 1][r] + bg;
-            ((T*)p.C)[(long)row * p.ldc + co] = from_f32<T>(v * sigmoidf_(g));
-          }
-        }
-    }
-  } else {
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni) {
-      const int col = cbase + ni * 32;
-      const bool cok = col < p.N;
-      const float bb = (p.bias && cok) ? p.bias[col] : 0.f;
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = rbase + mi * 32 + 8 * (r >> 2) + (r & 3);
-          if (row < p.M && cok) {
-            const float v = acc[mi][ni][r] + bb;
-            const long o = (long)row * p.ldc + col;
-            if constexpr (EP == E_STORE) ((T*)p.C)[o] = from_f32<T>(v);
-            else if constexpr (EP == E_SILU) ((T*)p.C)[o] = from_f32<T>(siluf_(v));
-            else if constexpr (EP == E_RELU) ((T*)p.C)[o] = from_f32<T>(fmaxf(v, 0.f));
-            else if constexpr (EP == E_RELU_F32) ((float*)p.C)[o] = fmaxf(v, 0.f);
-            else if constexpr (EP == E_RESID) ((float*)p.C)[o] += p.alpha * v;
-            else ((float*)p.C)[o] = v;
-          }
-        }
+  for (int i = 0; i < LPW; ++i) {
+    const int R = RPI * (wave * LPW + i) + lane / CPR;
+    const int lc = (lane % CPR) ^ ((R >> SWS) & (CPR - 1));
+    if (R < BM) {
+      const int gm = m0 + R < p.M ? m0 + R : p.M - 1;
+      src[i] = Ab + ((long)gm * p.lda + lc * 8) * sizeof(T);
+    } else {
+      const int gn = n0 + R - BM < p.N ? n0 + R - BM : p.N - 1;
+      src[i] = (const char*)p.W + ((long)gn * p.ldw + lc * 8) * sizeof(T);
     }
   }
+  const uint32_t sbase = lds_u32(smem) + wave * LPW * 1024;
+  auto issue = [&](int kt, int st) {
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) dma16(sbase + st * STAGE + i * 1024, src[i] + kt * RB);
+  };
+
+  f32x16 acc[MI][NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
+
+#pragma unroll
+  for (int st = 0; st < S - 1; ++st)
+    if (st < KT) issue(st, st);
+
+  // fragment rows are (lane & 31) + multiples of 32, so the swizzle key depends on lane only
+  const int frow = (lane & 31) * RB;
+  const int fkey = ((lane & 31) >> SWS) & (CPR - 1);
+  for (int kt = 0; kt < KT; ++kt) {
+    const int ahead = (KT - 1 - kt) < (S - 2) ? (KT - 1 - kt) : (S - 2);
+    if constexpr (S >= 4) { if (ahead >= 2) wait_vmcnt<2 * LPW>(); else if (ahead == 1) wait_vmcnt<LPW>(); else wait_vmcnt<0>(); }
+    else if constexpr (S == 3) { if (ahead >= 1) wait_vmcnt<LPW>(); else wait_vmcnt<0>(); }
+    else wait_vmcnt<0>();
+    __syncthreads();
+    if (kt + S - 1 < KT) issue(kt + S - 1, (kt + S - 1) % S);
+    const char* base = smem + (kt % S) * STAGE;
+#pragma unroll
+    for (int kc = 0; kc < KB / 16; ++kc) {
+      const int off = frow + ((((kc * 2) + (lane >> 5)) ^ fkey) << 4);
+      u32x4 af[MI], bfr[NI];
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) af[mi] = *(const u32x4*)(base + (wm * WTM + mi * 32) * RB + off);
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) bfr[ni] = *(const u32x4*)(base + (BM + wn * WTN + ni * 32) * RB + off);
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) Mma<T>::run(acc[mi][ni], af[mi], bfr[ni]);
+    }
+  }
+  epilogue<T, MI, NI, EP>(p, acc, m0 + wm * WTM, n0 + wn * WTN, n0 + wn * WTN, lane);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -282,7 +458,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmParams p) {
 
 template <typename T, int BM, int BN, int WGM, int WGN, bool Q8>
 static hipError_t run_epi(AMode am, Epi ep, const GemmParams& p, hipStream_t s) {
-  dim3 grid((p.M + BM - 1) / BM, (p.N + BN - 1) / BN);
+  dim3 grid(((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN));
 #define GG_L(AMv, EPv)                                                                   \
   if (am == AMv && ep == EPv) {                                                          \
     hipLaunchKernelGGL((k_gemm<T, BM, BN, WGM, WGN, AMv, Q8, EPv>), grid, dim3(256), 0, s, p); \
@@ -310,6 +486,30 @@ static hipError_t run_tiles(AMode am, Epi ep, const GemmParams& p, hipStream_t s
   return run_epi<T, 128, 128, 2, 2, Q8>(am, ep, p, s);
 }
 
+// Direct-load pipeline for fp16/bf16 operands already in T (plain or dual A). Two shapes,
+// both 8 waves of 64x64 accumulators, picked by N (measured on the encoder's GEMMs):
+//   N > 1024: 256 x 128 tile, 3 stages of 32 k-elements (72 KiB LDS, 2 blocks per CU)
+//   else    : 128 x 256 tile, 2 stages of 64 k-elements (96 KiB LDS)
+template <typename T, int BM, int BN, int WGM, int WGN, int S, int KB>
+static hipError_t run_dl(AMode am, Epi ep, const GemmParams& p, hipStream_t s) {
+  dim3 grid(((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN)), blk(64 * WGM * WGN);
+#define GG_DL(AMv, EPv)                                                                          \
+  if (am == AMv && ep == EPv) {                                                                  \
+    hipLaunchKernelGGL((k_gemm_dl<T, BM, BN, WGM, WGN, S, KB, AMv, EPv>), grid, blk, 0, s, p);  \
+    return hipGetLastError();                                                                    \
+  }
+  GG_DL(A_PLAIN, E_STORE) GG_DL(A_PLAIN, E_SILU) GG_DL(A_PLAIN, E_RESID) GG_DL(A_PLAIN, E_GLU)
+  GG_DL(A_PLAIN, E_F32) GG_DL(A_DUAL, E_STORE)
+#undef GG_DL
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+static hipError_t run_dl_shape(AMode am, Epi ep, const GemmParams& p, hipStream_t s) {
+  if (p.N > 1024) return run_dl<T, 256, 128, 4, 2, 3, 32>(am, ep, p, s);
+  return run_dl<T, 128, 256, 2, 4, 2, 64>(am, ep, p, s);
+}
+
 hipError_t launch_gemm(DType dt, bool w_int8, AMode am, Epi ep, const GemmParams& p,
                        hipStream_t s) {
   if (p.M <= 0) return hipSuccess;
@@ -318,12 +518,16 @@ hipError_t launch_gemm(DType dt, bool w_int8, AMode am, Epi ep, const GemmParams
     if (am == A_F32) am = A_PLAIN;
     if (am == A_CONV_F32) am = A_CONV;
   }
+  const bool direct = !w_int8 && (am == A_PLAIN || am == A_DUAL) && p.K % 64 == 0 &&
+                      (ep == E_STORE || ep == E_SILU || ep == E_RESID || ep == E_GLU || ep == E_F32) &&
+                      (am == A_PLAIN || ep == E_STORE);
   switch (dt) {
     case DT_F32: return run_tiles<float, false>(am, ep, p, s);
-    case DT_F16: return run_tiles<f16, false>(am, ep, p, s);
-    case DT_BF16: return run_tiles<bf16, false>(am, ep, p, s);
+    case DT_F16: return direct ? run_dl_shape<f16>(am, ep, p, s) : run_tiles<f16, false>(am, ep, p, s);
+    case DT_BF16: return direct ? run_dl_shape<bf16>(am, ep, p, s) : run_tiles<bf16, false>(am, ep, p, s);
     case DT_W8F16:
-      return w_int8 ? run_tiles<f16, true>(am, ep, p, s) : run_tiles<f16, false>(am, ep, p, s);
+      if (w_int8) return run_tiles<f16, true>(am, ep, p, s);
+      return direct ? run_dl_shape<f16>(am, ep, p, s) : run_tiles<f16, false>(am, ep, p, s);
   }
   return hipErrorInvalidValue;
 }
