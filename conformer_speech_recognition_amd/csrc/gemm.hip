@@ -361,6 +361,95 @@ template <int N> __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Epilogue through LDS: the finished accumulators (bias and activation applied) are
+// written to LDS in the output type, then every thread copies whole 16-byte row segments
+// to global memory, so the stores are fully coalesced. fp32 tiles that do not fit are
+// done in chunks of whole wave-rows. The residual form adds the staged alpha * (acc + b)
+// to 16-byte vectors of x.
+template <typename T, int BM, int BN, int WGM, int WGN, int EP, int LDSB>
+__device__ __forceinline__ void epilogue_lds(const GemmParams& p,
+                                             f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32],
+                                             char* smem, int m0, int n0, int wm, int wn, int lane,
+                                             int tid) {
+  constexpr int WTM = BM / WGM, WTN = BN / WGN, MI = WTM / 32, NI = WTN / 32;
+  constexpr bool F32OUT = (EP == E_RESID || EP == E_F32 || EP == E_RELU_F32);
+  constexpr int OES = F32OUT ? 4 : (int)sizeof(T);
+  constexpr int BNO = (EP == E_GLU) ? BN / 2 : BN;             // output columns of the tile
+  constexpr int PITCH = BNO * OES + 16;                         // LDS bytes per staged row
+  constexpr int CHM = LDSB / PITCH;
+  constexpr int CH = (CHM >= BM) ? BM : (CHM / WTM) * WTM;     // rows per chunk
+  constexpr int NT = 64 * WGM * WGN;
+  constexpr int EPS = 16 / OES;                                 // elements per 16-byte segment
+  constexpr int SEGS = BNO / EPS;                               // segments per staged row
+  static_assert(CH >= WTM && BM % CH == 0, "epilogue chunking");
+  const int n0o = (EP == E_GLU) ? n0 / 2 : n0;
+  const int Nout = (EP == E_GLU) ? p.N / 2 : p.N;
+  const bool vec = ((long)p.ldc * OES) % 16 == 0;
+  const int c = lane & 31, h4 = 4 * (lane >> 5);
+#pragma unroll
+  for (int c0 = 0; c0 < BM; c0 += CH) {
+    __syncthreads();
+    if (wm * WTM >= c0 && wm * WTM < c0 + CH) {
+      if constexpr (EP == E_GLU) {
+#pragma unroll
+        for (int q = 0; q < NI / 2; ++q) {
+          const int cv = n0 + wn * WTN + 2 * q * 32 + c, cg = cv + 32;
+          const float bv = (p.bias && cv < p.N) ? p.bias[cv] : 0.f;
+          const float bg = (p.bias && cg < p.N) ? p.bias[cg] : 0.f;
+          const int co = (wn * WTN) / 2 + q * 32 + c;
+#pragma unroll
+          for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int rl = wm * WTM - c0 + mi * 32 + 8 * (r >> 2) + h4 + (r & 3);
+              const float v = acc[mi][2 * q][r] + bv, g = acc[mi][2 * q + 1][r] + bg;
+              *(T*)(smem + rl * PITCH + co * OES) = from_f32<T>(v * sigmoidf_(g));
+            }
+        }
+      } else {
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          const int ct = wn * WTN + ni * 32 + c;
+          const float bb = (p.bias && n0 + ct < p.N) ? p.bias[n0 + ct] : 0.f;
+#pragma unroll
+          for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int rl = wm * WTM - c0 + mi * 32 + 8 * (r >> 2) + h4 + (r & 3);
+              const float v = acc[mi][ni][r] + bb;
+              char* d = smem + rl * PITCH + ct * OES;
+              if constexpr (EP == E_STORE) *(T*)d = from_f32<T>(v);
+              else if constexpr (EP == E_SILU) *(T*)d = from_f32<T>(siluf_(v));
+              else if constexpr (EP == E_RELU) *(T*)d = from_f32<T>(fmaxf(v, 0.f));
+              else if constexpr (EP == E_RELU_F32) *(float*)d = fmaxf(v, 0.f);
+              else if constexpr (EP == E_RESID) *(float*)d = p.alpha * v;
+              else *(float*)d = v;
+            }
+        }
+      }
+    }
+    __syncthreads();
+    for (int e = tid; e < CH * SEGS; e += NT) {
+      const int rl = e / SEGS, sg = e - rl * SEGS;
+      const int row = m0 + c0 + rl;
+      const int col = n0o + sg * EPS;
+      if (row >= p.M || col >= Nout) continue;
+      const char* ls = smem + rl * PITCH + sg * 16;
+      char* gd = (char*)p.C + ((long)row * p.ldc + col) * OES;
+      if (vec && col + EPS <= Nout) {
+        if constexpr (EP == E_RESID) *(f32x4*)gd = *(const f32x4*)gd + *(const f32x4*)ls;
+        else *(u32x4*)gd = *(const u32x4*)ls;
+      } else {
+        for (int j = 0; j < EPS && col + j < Nout; ++j) {
+          if constexpr (EP == E_RESID) ((float*)gd)[j] += ((const float*)ls)[j];
+          else if constexpr (F32OUT) ((float*)gd)[j] = ((const float*)ls)[j];
+          else ((T*)gd)[j] = ((const T*)ls)[j];
+        }
+      }
+    }
+  }
+}
+
 template <typename T, int BM, int BN, int WGM, int WGN, int S, int KB, int AM, int EP>
 __global__ void __launch_bounds__(64 * WGM * WGN) k_gemm_dl(GemmParams p) {
   constexpr int NW = WGM * WGN;                 // waves per block
@@ -450,7 +539,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) k_gemm_dl(GemmParams p) {
         for (int ni = 0; ni < NI; ++ni) Mma<T>::run(acc[mi][ni], af[mi], bfr[ni]);
     }
   }
-  epilogue<T, MI, NI, EP>(p, acc, m0 + wm * WTM, n0 + wn * WTN, n0 + wn * WTN, lane);
+  epilogue_lds<T, BM, BN, WGM, WGN, EP, S * STAGE>(p, acc, smem, m0, n0, wm, wn, lane, tid);
 }
 
 // ---------------------------------------------------------------------------------------
