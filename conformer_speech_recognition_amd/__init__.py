@@ -77,6 +77,7 @@ _SIGNATURES = {
     "gigaam_encode": (ctypes.c_int, [_P, _P, _IP, _I, _I, _P, _SZ, _P, _P, _P, _P, _P, _IP, _P]),
     "gigaam_encode_stage": (ctypes.c_int, [_P, _P, _IP, _I, _I, _P, _SZ, _I, _P, _SZ, _P]),
     "gigaam_debug_gemm": (ctypes.c_int, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
+    "gigaam_debug_attention": (ctypes.c_int, [_I, _I, _I, _I, _IP, _P, _P, _P, _SZ, _P]),
     "gigaam_profile_start": (ctypes.c_int, []),
     "gigaam_profile_stop": (ctypes.c_int, []),
     "gigaam_profile_report": (ctypes.c_int, [ctypes.c_char_p, _SZ]),
@@ -296,3 +297,18 @@ def profile_report() -> list[dict]:
     buf = ctypes.create_string_buffer(1 << 16)
     _check(lib().gigaam_profile_report(buf, len(buf)))
     return json.loads(buf.value.decode())
+
+
+def debug_attention(dtype: str, qkv, frames, n_heads: int = 16, stream=None):
+    """softmax(q k^T / sqrt(d_k)) v per clip and head with the encoder's attention kernel;
+    qkv: device tensor [sum U_b, 3 d] in the storage type of ``dtype``."""
+    import torch
+    fr = np.ascontiguousarray(np.asarray(frames, dtype=np.int32))
+    d = qkv.shape[1] // 3
+    out = torch.empty(qkv.shape[0], d, dtype=qkv.dtype, device=qkv.device)
+    nb = 16 * (len(fr) + 1) + 16 * int(fr.sum()) + 4096
+    ws = torch.empty(nb, dtype=torch.uint8, device=qkv.device)
+    s = (stream or torch.cuda.current_stream(qkv.device)).cuda_stream
+    _check(lib().gigaam_debug_attention(DTYPES[dtype], d, n_heads, len(fr), fr.ctypes.data_as(_IP),
+                                        qkv.data_ptr(), out.data_ptr(), ws.data_ptr(), nb, s))
+    return out

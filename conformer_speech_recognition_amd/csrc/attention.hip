@@ -4,7 +4,7 @@
 // section "Where the time goes").
 //
 // Block = 4 waves = 64 queries of one clip and one head; each wave owns 16 queries.
-// Per 64-key tile (K and V^T staged in LDS):
+// Per 64-key tile (K and V^T staged in LDS, the next tile prefetched into registers):
 //   S^T[key][query] = K . Q^T   with 16x16 MFMAs (A = K rows from LDS, B = the wave's Q
 //                               fragment kept in registers)
 //   lane l then holds 16 scores of ONE query (l % 16): keys kb*16 + 4*(l/16) + r,
@@ -13,6 +13,7 @@
 //   O^T[dim][query] += V^T . P^T with the probabilities used straight from the score
 //   registers as the B operand (the lane's k slots are exactly its keys).
 // Scores, max, sum and the output accumulator are fp32; P is rounded to T for the MFMA.
+// d_k = 48 runs the score contraction as two 16x16x32 MFMAs with the top 16 k slots zero.
 #include "kernels.h"
 
 namespace gg {
@@ -28,19 +29,11 @@ template <> struct AttnMma<f16> {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
-  static __device__ __forceinline__ f32x4 k16(u32x2 a, u32x2 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
-                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
-  }
 };
 template <> struct AttnMma<bf16> {
   static __device__ __forceinline__ f32x4 k32(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ f32x4 k16(u32x2 a, u32x2 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
-                                                     __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
   }
 };
 
@@ -53,13 +46,20 @@ template <typename T> __device__ __forceinline__ u32x4 pack8f(const float* v) {
 }
 
 // ---------------------------------------------------------------- fp16 / bf16 kernel
+// K and V^T tiles are double-buffered in LDS: the next 64-key tile is loaded into
+// registers while the current one is consumed, and stored after it (one barrier per
+// tile). V is transposed in 4-key x 8-dim register blocks, written as 8-byte LDS stores.
 template <typename T, int DK>
 __global__ void __launch_bounds__(256) k_attn(AttnParams p) {
-  constexpr int KP = DK + 8;         // LDS row pitch (elements) of K
+  constexpr int KP = DK + 8;         // LDS row pitch (elements) of K: 16 rows -> 16 bank groups
   constexpr int VP = AT_KV + 8;      // LDS row pitch of V^T
   constexpr int NDB = DK / 16;       // 16-wide dim blocks of the output
-  __shared__ T sK[AT_KV][KP];
-  __shared__ T sVt[DK][VP];
+  constexpr int KCH = AT_KV * DK / 8;          // 16-byte K chunks per tile
+  constexpr int VBL = (AT_KV / 4) * (DK / 8);  // 4-key x 8-dim V blocks per tile
+  constexpr int KPT = (KCH + 255) / 256;       // K chunks per thread
+  static_assert(VBL <= 256, "one V block per thread");
+  __shared__ T sK[2][AT_KV][KP];
+  __shared__ T sVt[2][DK][VP];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
@@ -75,43 +75,73 @@ __global__ void __launch_bounds__(256) k_attn(AttnParams p) {
   // Q fragment (B operand of S^T): query qi, dims [8g, 8g+8) and the remainder block
   const int qrow = qi < U ? qi : U - 1;
   const T* qp = Qg + (long)qrow * ld;
+  // dims 32.. go through a second 16x16x32 MFMA; for d_k = 48 its lanes g >= 2 (dims 48..63)
+  // are zero on both operands
+  const bool hi_ok = DK == 64 || g < 2;
   const u32x4 qa = *(const u32x4*)(qp + 8 * g);
-  u32x4 qb4;
-  u32x2 qb2;
-  if constexpr (DK == 64) qb4 = *(const u32x4*)(qp + 32 + 8 * g);
-  else qb2 = *(const u32x2*)(qp + 32 + 4 * g);
+  const u32x4 qb = hi_ok ? *(const u32x4*)(qp + 32 + 8 * g) : u32x4{0, 0, 0, 0};
+
+  // tile loads into registers
+  u32x4 rk[KPT];
+  u32x4 rv[4];
+  const int vq = tid / (DK / 8), vch = tid - vq * (DK / 8);   // V block: keys 4vq.., dims 8vch..
+  auto load = [&](int kv0) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int e = tid + 256 * i;
+      const int key = e / (DK / 8), ch = e - key * (DK / 8);
+      rk[i] = u32x4{0, 0, 0, 0};
+      if (e < KCH && kv0 + key < U) rk[i] = *(const u32x4*)(Kg + (long)(kv0 + key) * ld + ch * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int key = kv0 + 4 * vq + j;
+      rv[j] = u32x4{0, 0, 0, 0};
+      if (tid < VBL && key < U) rv[j] = *(const u32x4*)(Vg + (long)key * ld + vch * 8);
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int e = tid + 256 * i;
+      if (e < KCH) {
+        const int key = e / (DK / 8), ch = e - key * (DK / 8);
+        *(u32x4*)&sK[buf][key][ch * 8] = rk[i];
+      }
+    }
+    if (tid < VBL) {
+      typedef uint16_t h8 __attribute__((ext_vector_type(8)));
+      typedef uint16_t h4 __attribute__((ext_vector_type(4)));
+      const h8 v0 = __builtin_bit_cast(h8, rv[0]), v1 = __builtin_bit_cast(h8, rv[1]);
+      const h8 v2 = __builtin_bit_cast(h8, rv[2]), v3 = __builtin_bit_cast(h8, rv[3]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        *(h4*)&sVt[buf][vch * 8 + i][4 * vq] = h4{v0[i], v1[i], v2[i], v3[i]};
+    }
+  };
 
   float m_run = -INFINITY, l_part = 0.f;
   f32x4 o[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) o[db] = f32x4{0, 0, 0, 0};
 
+  load(0);
+  store(0);
+  __syncthreads();
+  int buf = 0;
   for (int kv0 = 0; kv0 < U; kv0 += AT_KV) {
-    __syncthreads();
-    for (int e = tid; e < AT_KV * DK / 8; e += 256) {
-      const int key = e / (DK / 8), ch = e - key * (DK / 8);
-      u32x4 kv = u32x4{0, 0, 0, 0}, vv = u32x4{0, 0, 0, 0};
-      if (kv0 + key < U) {
-        kv = *(const u32x4*)(Kg + (long)(kv0 + key) * ld + ch * 8);
-        vv = *(const u32x4*)(Vg + (long)(kv0 + key) * ld + ch * 8);
-      }
-      *(u32x4*)&sK[key][ch * 8] = kv;
-      typedef T t8 __attribute__((ext_vector_type(8)));
-      const t8 vt = __builtin_bit_cast(t8, vv);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sVt[ch * 8 + i][key] = vt[i];
-    }
-    __syncthreads();
+    const bool more = kv0 + AT_KV < U;
+    if (more) load(kv0 + AT_KV);
 
     // S^T blocks: s[kb][r] = score(key kv0 + kb*16 + 4g + r, query qi)
     f32x4 s[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      const T* kr = &sK[kb * 16 + c16][0];
+      const T* kr = &sK[buf][kb * 16 + c16][0];
       f32x4 acc = f32x4{0, 0, 0, 0};
       acc = AttnMma<T>::k32(*(const u32x4*)(kr + 8 * g), qa, acc);
-      if constexpr (DK == 64) acc = AttnMma<T>::k32(*(const u32x4*)(kr + 32 + 8 * g), qb4, acc);
-      else acc = AttnMma<T>::k16(*(const u32x2*)(kr + 32 + 4 * g), qb2, acc);
+      const u32x4 kh = hi_ok ? *(const u32x4*)(kr + 32 + 8 * g) : u32x4{0, 0, 0, 0};
+      acc = AttnMma<T>::k32(kh, qb, acc);
       s[kb] = acc;
     }
     float mx = -INFINITY;
@@ -150,12 +180,15 @@ __global__ void __launch_bounds__(256) k_attn(AttnParams p) {
       const u32x4 pb = pack8f<T>(pp);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const T* vr = &sVt[db * 16 + c16][32 * hk + 4 * g];
+        const T* vr = &sVt[buf][db * 16 + c16][32 * hk + 4 * g];
         const u32x2 lo = *(const u32x2*)vr;
         const u32x2 hi = *(const u32x2*)(vr + 16);
         o[db] = AttnMma<T>::k32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb, o[db]);
       }
     }
+    if (more) store(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
   }
 
   float l = l_part + __shfl_xor(l_part, 16, 64);

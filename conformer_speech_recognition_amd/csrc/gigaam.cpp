@@ -789,3 +789,39 @@ extern "C" int gigaam_debug_gemm(int32_t dtype, int32_t M, int32_t N, int32_t K,
   HIP_TRY(launch_gemm((DType)dtype, dtype == GIGAAM_W8F16, A_PLAIN, E_F32, p, (hipStream_t)hip_stream));
   return GIGAAM_OK;
 }
+
+extern "C" int gigaam_debug_attention(int32_t dtype, int32_t d_model, int32_t n_heads, int32_t batch,
+                                      const int32_t* frames_host, const void* qkv_dev, void* out_dev,
+                                      void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (dtype < GIGAAM_F32 || dtype > GIGAAM_W8F16) return fail(GIGAAM_E_INVAL, "dtype %d", dtype);
+  if (batch < 1 || batch > GIGAAM_MAX_BATCH) return fail(GIGAAM_E_INVAL, "batch %d", batch);
+  if (!frames_host || !qkv_dev || !out_dev || !workspace) return fail(GIGAAM_E_INVAL, "NULL pointer");
+  if ((uintptr_t)workspace & 255) return fail(GIGAAM_E_INVAL, "workspace not 256-B aligned");
+  if (n_heads < 1 || d_model % n_heads) return fail(GIGAAM_E_INVAL, "d_model %d / n_heads %d", d_model, n_heads);
+  const int dk = d_model / n_heads;
+  if (dk != 48 && dk != 64) return fail(GIGAAM_E_UNSUPPORTED, "head size %d", dk);
+  MetaArgs meta;
+  std::memset(&meta, 0, sizeof meta);
+  meta.B = batch;
+  int nQ = 0;
+  for (int b = 0; b < batch; ++b) {
+    if (frames_host[b] < 1) return fail(GIGAAM_E_INVAL, "frames[%d] = %d", b, frames_host[b]);
+    meta.cuU[b + 1] = meta.cuU[b] + frames_host[b];
+    nQ += (frames_host[b] + kQTile - 1) / kQTile;
+  }
+  const int U_tot = meta.cuU[batch];
+  std::memcpy(meta.cuT, meta.cuU, sizeof meta.cuU);
+  std::memcpy(meta.cuS, meta.cuU, sizeof meta.cuU);
+  const size_t need = 16 * (size_t)(batch + 1) + 16 * (size_t)U_tot + 4096;
+  if (workspace_bytes < need) return fail(GIGAAM_E_WORKSPACE, "workspace %zu < %zu", workspace_bytes, need);
+  int* w = (int*)workspace;
+  MetaDev md{w, w + (batch + 1), w + 2 * (batch + 1), w + 3 * (batch + 1), w + 4 * (batch + 1),
+             w + 4 * (batch + 1) + U_tot, w + 4 * (batch + 1) + 2 * U_tot,
+             w + 4 * (batch + 1) + 3 * U_tot};
+  hipStream_t s = (hipStream_t)hip_stream;
+  HIP_TRY(launch_meta(meta, md, U_tot, U_tot, U_tot, s));
+  AttnParams ap{qkv_dev, out_dev, d_model, n_heads, nQ, md.cuU, md.cuQ, md.tileQ,
+                (float)(1.4426950408889634 / std::sqrt((double)dk))};
+  HIP_TRY(launch_attention((DType)dtype, dk, ap, s));
+  return GIGAAM_OK;
+}

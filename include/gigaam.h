@@ -203,6 +203,17 @@ int gigaam_debug_gemm(int32_t dtype, int32_t M, int32_t N, int32_t K, const void
                       const void* W_dev, const void* scale_dev, const float* bias_dev,
                       float* C_dev, void* hip_stream);
 
+/* Diagnostics: the encoder's attention kernel on its own, over packed clips.
+ * frames_host int32 [batch]: frames U_b of each clip (>= 1); qkv_dev [sum U_b][3 d_model]
+ * holds q | k | v per frame in the storage type of `dtype` (fp32, fp16, bf16;
+ * GIGAAM_W8F16 = fp16); out_dev [sum U_b][d_model] the same type. d_model / n_heads must
+ * be 48 or 64. workspace: device memory of at least
+ *   16 * (batch + 1) + 16 * sum U_b + 4096 bytes (256-B aligned).
+ * Errors: GIGAAM_E_INVAL, GIGAAM_E_WORKSPACE, GIGAAM_E_UNSUPPORTED, GIGAAM_E_HIP.        */
+int gigaam_debug_attention(int32_t dtype, int32_t d_model, int32_t n_heads, int32_t batch,
+                           const int32_t* frames_host, const void* qkv_dev, void* out_dev,
+                           void* workspace, size_t workspace_bytes, void* hip_stream);
+
 /* Diagnostics: per-kernel timing. Between gigaam_profile_start and _stop every launch
  * of gigaam_encode is bracketed by HIP events recorded on the caller's stream (the
  * events add a little stream overhead). gigaam_profile_report waits for those events
