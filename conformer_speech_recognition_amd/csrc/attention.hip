@@ -48,18 +48,43 @@ template <typename T> __device__ __forceinline__ u32x4 pack8f(const float* v) {
 // ---------------------------------------------------------------- fp16 / bf16 kernel
 // K and V^T tiles are double-buffered in LDS: the next 64-key tile is loaded into
 // registers while the current one is consumed, and stored after it (one barrier per
-// tile). V is transposed in 4-key x 8-dim register blocks, written as 8-byte LDS stores.
+// tile). V is transposed in 4-key x 8-dim register blocks, written as 8-byte LDS stores
+// (16 consecutive lanes take 16 consecutive key blocks of one dim block: 32 distinct banks).
+//
+// The softmax is kept in base 2 with the scale folded into one FMA per score:
+// p = 2^(s*c - m*c), c = log2(e)/sqrt(d_k), m the running max of the raw scores.  The
+// key mask is applied only on a clip's last, partial tile; the accumulator is rescaled
+// only when some query's running max moved.
+// v_max3_f32 without the NaN-quieting canonicalisation the compiler adds around fmaxf
+__device__ __forceinline__ float max3_(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  return max3_(__uint_as_float(r[0]), __uint_as_float(r[1]), v);
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  return max3_(__uint_as_float(r[0]), __uint_as_float(r[1]), v);
+}
+
 template <typename T, int DK>
 __global__ void __launch_bounds__(256) k_attn(AttnParams p) {
   constexpr int KP = DK + 8;         // LDS row pitch (elements) of K: 16 rows -> 16 bank groups
   constexpr int VP = AT_KV + 8;      // LDS row pitch of V^T
   constexpr int NDB = DK / 16;       // 16-wide dim blocks of the output
-  constexpr int KCH = AT_KV * DK / 8;          // 16-byte K chunks per tile
-  constexpr int VBL = (AT_KV / 4) * (DK / 8);  // 4-key x 8-dim V blocks per tile
+  constexpr int NDBX = NDB + 1;      // + one block whose first V^T row is all ones: row sums
+  constexpr int CPR = DK / 8;        // 16-byte chunks per K / V row
+  constexpr int KCH = AT_KV * CPR;   // 16-byte K chunks per tile
+  constexpr int VBL = (AT_KV / 4) * CPR;       // 4-key x 8-dim V blocks per tile
   constexpr int KPT = (KCH + 255) / 256;       // K chunks per thread
   static_assert(VBL <= 256, "one V block per thread");
   __shared__ T sK[2][AT_KV][KP];
-  __shared__ T sVt[2][DK][VP];
+  __shared__ T sVt[2][DK + 16][VP];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
@@ -71,6 +96,7 @@ __global__ void __launch_bounds__(256) k_attn(AttnParams p) {
   const T* Qg = (const T*)p.qkv + (long)base * ld + h * DK;
   const T* Kg = Qg + p.d;
   const T* Vg = Qg + 2 * p.d;
+  const float c = p.scale_log2;
 
   // Q fragment (B operand of S^T): query qi, dims [8g, 8g+8) and the remainder block
   const int qrow = qi < U ? qi : U - 1;
@@ -81,34 +107,43 @@ __global__ void __launch_bounds__(256) k_attn(AttnParams p) {
   const u32x4 qa = *(const u32x4*)(qp + 8 * g);
   const u32x4 qb = hi_ok ? *(const u32x4*)(qp + 32 + 8 * g) : u32x4{0, 0, 0, 0};
 
-  // tile loads into registers
+  // this thread's tile loads: 16-byte K chunks (e = tid + 256 i: key e / CPR, chunk e % CPR)
+  // and one V block (keys 4vq.. 4vq+3, dims 8vch.. 8vch+7), as raw buffer loads against a
+  // per-tile resource that ends at the clip's last row: rows past the clip read as zero
+  int koff[KPT], kls[KPT];            // global byte offset in the tile, LDS element offset
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int e = tid + 256 * i, key = e / CPR, ch = e - key * CPR;
+    koff[i] = (key * ld + ch * 8) * (int)sizeof(T);
+    kls[i] = key * KP + ch * 8;
+  }
+  const int vq = tid & 15, vch = tid >> 4;
+  const int voff = ((4 * vq) * ld + vch * 8) * (int)sizeof(T);
+  const int vstep = ld * (int)sizeof(T);
   u32x4 rk[KPT];
   u32x4 rv[4];
-  const int vq = tid / (DK / 8), vch = tid - vq * (DK / 8);   // V block: keys 4vq.., dims 8vch..
   auto load = [&](int kv0) {
+    const int bytes = (U - kv0) * ld * (int)sizeof(T);
+    const __amdgpu_buffer_rsrc_t rK =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Kg + (long)kv0 * ld), 0, bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rV =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Vg + (long)kv0 * ld), 0, bytes, 0x00020000);
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int e = tid + 256 * i;
-      const int key = e / (DK / 8), ch = e - key * (DK / 8);
-      rk[i] = u32x4{0, 0, 0, 0};
-      if (e < KCH && kv0 + key < U) rk[i] = *(const u32x4*)(Kg + (long)(kv0 + key) * ld + ch * 8);
-    }
+    for (int i = 0; i < KPT; ++i)
+      if (KCH % 256 == 0 || tid + 256 * i < KCH)
+        rk[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rK, koff[i], 0, 0));
+    if (tid < VBL) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = kv0 + 4 * vq + j;
-      rv[j] = u32x4{0, 0, 0, 0};
-      if (tid < VBL && key < U) rv[j] = *(const u32x4*)(Vg + (long)key * ld + vch * 8);
+      for (int j = 0; j < 4; ++j)
+        rv[j] = __builtin_bit_cast(u32x4,
+                                   __builtin_amdgcn_raw_buffer_load_b128(rV, voff + j * vstep, 0, 0));
     }
   };
   auto store = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int e = tid + 256 * i;
-      if (e < KCH) {
-        const int key = e / (DK / 8), ch = e - key * (DK / 8);
-        *(u32x4*)&sK[buf][key][ch * 8] = rk[i];
-      }
-    }
+    for (int i = 0; i < KPT; ++i)
+      if (KCH % 256 == 0 || tid + 256 * i < KCH)
+        *(u32x4*)(&sK[buf][0][0] + kls[i]) = rk[i];
     if (tid < VBL) {
       typedef uint16_t h8 __attribute__((ext_vector_type(8)));
       typedef uint16_t h4 __attribute__((ext_vector_type(4)));
@@ -119,58 +154,73 @@ __global__ void __launch_bounds__(256) k_attn(AttnParams p) {
         *(h4*)&sVt[buf][vch * 8 + i][4 * vq] = h4{v0[i], v1[i], v2[i], v3[i]};
     }
   };
+  // d_k = 48: the score MFMA's upper 16 k slots read the zero pad columns [48, 56) of the
+  // K rows (set once here, never overwritten by the tile stores)
+  if (DK == 48 && tid < 2 * AT_KV)
+    *(u32x4*)&sK[tid / AT_KV][tid % AT_KV][DK] = u32x4{0, 0, 0, 0};
+  const int khi = hi_ok ? 32 + 8 * g : DK;
 
-  float m_run = -INFINITY, l_part = 0.f;
-  f32x4 o[NDB];
+  // rows DK.. DK+15 of both V^T buffers: a row of ones then zeros, so that the P.V
+  // product also accumulates each query's probability sum (in the rounded P the MFMA uses)
+  {
+    const int vb = tid >> 7, row = (tid >> 3) & 15, col = (tid & 7) * 8;
+    const uint32_t one2 = row == 0 ? (uint32_t)__builtin_bit_cast(uint16_t, (T)1.0f) * 0x10001u : 0u;
+    *(u32x4*)&sVt[vb][DK + row][col] = u32x4{one2, one2, one2, one2};
+  }
+  float m_run = -INFINITY;
+  f32x4 o[NDBX];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) o[db] = f32x4{0, 0, 0, 0};
+  for (int db = 0; db < NDBX; ++db) o[db] = f32x4{0, 0, 0, 0};
 
   load(0);
   store(0);
+  // every load issued so far (Q fragments, first tile) is complete here, so the loop's
+  // wait-count bookkeeping starts clean and only the store waits for the prefetch
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   __syncthreads();
   int buf = 0;
   for (int kv0 = 0; kv0 < U; kv0 += AT_KV) {
     const bool more = kv0 + AT_KV < U;
     if (more) load(kv0 + AT_KV);
 
-    // S^T blocks: s[kb][r] = score(key kv0 + kb*16 + 4g + r, query qi)
+    // S^T blocks: s[kb][r] = raw score(key kv0 + kb*16 + 4g + r, query qi)
     f32x4 s[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const T* kr = &sK[buf][kb * 16 + c16][0];
       f32x4 acc = f32x4{0, 0, 0, 0};
       acc = AttnMma<T>::k32(*(const u32x4*)(kr + 8 * g), qa, acc);
-      const u32x4 kh = hi_ok ? *(const u32x4*)(kr + 32 + 8 * g) : u32x4{0, 0, 0, 0};
-      acc = AttnMma<T>::k32(kh, qb, acc);
+      acc = AttnMma<T>::k32(*(const u32x4*)(kr + khi), qb, acc);
       s[kb] = acc;
     }
-    float mx = -INFINITY;
+    if (!more) {                     // the clip's last tile: keys >= U get probability 0
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = kv0 + kb * 16 + 4 * g + r;
-        const float v = key < U ? s[kb][r] * p.scale_log2 : -INFINITY;
-        s[kb][r] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
+        for (int r = 0; r < 4; ++r)
+          if (kv0 + kb * 16 + 4 * g + r >= U) s[kb][r] = -INFINITY;
+    }
+    float mx = max3_(s[0][0], s[0][1], s[0][2]);
+    mx = max3_(mx, s[0][3], s[1][0]);
+    mx = max3_(mx, s[1][1], s[1][2]);
+    mx = max3_(mx, s[1][3], s[2][0]);
+    mx = max3_(mx, s[2][1], s[2][2]);
+    mx = max3_(mx, s[2][3], s[3][0]);
+    mx = max3_(mx, s[3][1], s[3][2]);
+    mx = max3_(mx, s[3][3], m_run);
+    const float m_new = max_xor32(max_xor16(mx));
+    if (__builtin_amdgcn_ballot_w64(m_new != m_run)) {
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+#pragma unroll
+      for (int db = 0; db < NDBX; ++db) o[db] *= alpha;
+      m_run = m_new;
+    }
+    const float mc = m_run * c;
     float pv[4][4];
-    float ls = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pv[kb][r] = exp2f(s[kb][r] - m_new);
-        ls += pv[kb][r];
-      }
-    l_part = l_part * alpha + ls;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+      for (int r = 0; r < 4; ++r) pv[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -mc));
 
 #pragma unroll
     for (int hk = 0; hk < 2; ++hk) {
@@ -179,7 +229,7 @@ __global__ void __launch_bounds__(256) k_attn(AttnParams p) {
       for (int r = 0; r < 4; ++r) { pp[r] = pv[2 * hk][r]; pp[4 + r] = pv[2 * hk + 1][r]; }
       const u32x4 pb = pack8f<T>(pp);
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
+      for (int db = 0; db < NDBX; ++db) {
         const T* vr = &sVt[buf][db * 16 + c16][32 * hk + 4 * g];
         const u32x2 lo = *(const u32x2*)vr;
         const u32x2 hi = *(const u32x2*)(vr + 16);
@@ -191,8 +241,8 @@ __global__ void __launch_bounds__(256) k_attn(AttnParams p) {
     buf ^= 1;
   }
 
-  float l = l_part + __shfl_xor(l_part, 16, 64);
-  l += __shfl_xor(l, 32, 64);
+  // the probability sum sits in dim DK of the extra block: lane c16 (g = 0), element 0
+  const float l = __shfl(o[NDB][0], c16, 64);
   if (qi < U) {
     const float inv = 1.0f / l;
     T* op = (T*)p.out + (long)(base + qi) * p.d + h * DK;

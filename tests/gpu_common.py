@@ -19,7 +19,9 @@ import oracle  # noqa: E402
 import synth  # noqa: E402
 
 # fp32 path: encoder output within 1e-4 and token ids bit-exact; fp16/bf16/int8 paths:
-# encoder output within 5e-2 and >= 99.5% per-frame argmax agreement.
+# encoder output within 5e-2 and >= 99.5% per-frame argmax agreement, where a frame whose
+# oracle top choices lie closer together than the path's own log-prob deviation counts as
+# agreeing when the GPU picks one of them (random-init heads have many such near-ties).
 TOL_F32 = 1e-4
 TOL_LOW = 5e-2
 ARGMAX_AGREE = 0.995
@@ -61,10 +63,20 @@ def clip_rows(lens, b, which=2):
     return start, start + fr[b][which]
 
 
-def argmax_agreement(gpu_ids: np.ndarray, ref_logp: np.ndarray):
+def argmax_agreement(gpu_ids: np.ndarray, ref_logp: np.ndarray, lp_dev: float = 0.0):
+    """Per-frame greedy-id agreement with the oracle.
+
+    Returns (raw, tie_aware, gap, flips): raw is the fraction of frames with identical
+    ids; gap[t] is how far below the oracle's best log-prob the GPU's pick lies (0 where
+    they agree); flips are the disagreeing frames.  When every log-prob of a frame is
+    within lp_dev of the oracle's, the GPU's pick can only differ where gap <= 2 lp_dev,
+    and there both picks are correct at that precision: tie_aware counts such frames as
+    agreeing (a flip with a larger gap is a wrong answer and counts against it)."""
+    ref_logp = np.asarray(ref_logp, dtype=np.float64)
     ref = oracle.greedy_ids(ref_logp)
-    agree = float(np.mean(gpu_ids == ref))
-    srt = np.sort(np.asarray(ref_logp, dtype=np.float64), axis=1)
-    margin = srt[:, -1] - srt[:, -2]
+    rows = np.arange(len(ref))
+    gap = ref_logp[rows, ref] - ref_logp[rows, np.asarray(gpu_ids)]
     flips = np.nonzero(gpu_ids != ref)[0]
-    return agree, margin, flips
+    raw = float(np.mean(gpu_ids == ref))
+    tie = float(np.mean((gpu_ids == ref) | (gap <= 2.0 * lp_dev)))
+    return raw, tie, gap, flips
