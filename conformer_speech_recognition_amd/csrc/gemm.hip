@@ -355,7 +355,7 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 __device__ __forceinline__ void dma16(uint32_t lds, const void* g) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory");
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory");
 }
 template <int N> __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -450,8 +450,8 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p,
   }
 }
 
-template <typename T, int BM, int BN, int WGM, int WGN, int S, int KB, int AM, int EP>
-__global__ void __launch_bounds__(64 * WGM * WGN) k_gemm_dl(GemmParams p) {
+template <typename T, int BM, int BN, int WGM, int WGN, int S, int KB, int AM, int EP, int OCC = 1>
+__global__ void __launch_bounds__(64 * WGM * WGN, OCC) k_gemm_dl(GemmParams p) {
   constexpr int NW = WGM * WGN;                 // waves per block
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int MI = WTM / 32, NI = WTN / 32;
@@ -517,6 +517,9 @@ __global__ void __launch_bounds__(64 * WGM * WGN) k_gemm_dl(GemmParams p) {
   // fragment rows are (lane & 31) + multiples of 32, so the swizzle key depends on lane only
   const int frow = (lane & 31) * RB;
   const int fkey = ((lane & 31) >> SWS) & (CPR - 1);
+  // 32-row blocks of the wave that lie wholly past M (the last row tile of a ragged M)
+  // read and multiply nothing
+  const int live = (p.M - m0 - wm * WTM + 31) / 32;
   for (int kt = 0; kt < KT; ++kt) {
     const int ahead = (KT - 1 - kt) < (S - 2) ? (KT - 1 - kt) : (S - 2);
     if constexpr (S >= 4) { if (ahead >= 2) wait_vmcnt<2 * LPW>(); else if (ahead == 1) wait_vmcnt<LPW>(); else wait_vmcnt<0>(); }
@@ -525,18 +528,36 @@ __global__ void __launch_bounds__(64 * WGM * WGN) k_gemm_dl(GemmParams p) {
     __syncthreads();
     if (kt + S - 1 < KT) issue(kt + S - 1, (kt + S - 1) % S);
     const char* base = smem + (kt % S) * STAGE;
+    if (live >= MI) {
 #pragma unroll
-    for (int kc = 0; kc < KB / 16; ++kc) {
-      const int off = frow + ((((kc * 2) + (lane >> 5)) ^ fkey) << 4);
-      u32x4 af[MI], bfr[NI];
+      for (int kc = 0; kc < KB / 16; ++kc) {
+        const int off = frow + ((((kc * 2) + (lane >> 5)) ^ fkey) << 4);
+        u32x4 af[MI], bfr[NI];
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) af[mi] = *(const u32x4*)(base + (wm * WTM + mi * 32) * RB + off);
+        for (int mi = 0; mi < MI; ++mi) af[mi] = *(const u32x4*)(base + (wm * WTM + mi * 32) * RB + off);
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni) bfr[ni] = *(const u32x4*)(base + (BM + wn * WTN + ni * 32) * RB + off);
+        for (int ni = 0; ni < NI; ++ni) bfr[ni] = *(const u32x4*)(base + (BM + wn * WTN + ni * 32) * RB + off);
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
+        for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni) Mma<T>::run(acc[mi][ni], af[mi], bfr[ni]);
+          for (int ni = 0; ni < NI; ++ni) Mma<T>::run(acc[mi][ni], af[mi], bfr[ni]);
+      }
+    } else if (live > 0) {
+#pragma unroll
+      for (int kc = 0; kc < KB / 16; ++kc) {
+        const int off = frow + ((((kc * 2) + (lane >> 5)) ^ fkey) << 4);
+        u32x4 bfr[NI];
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) bfr[ni] = *(const u32x4*)(base + (BM + wn * WTN + ni * 32) * RB + off);
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+          if (mi < live) {
+            const u32x4 af = *(const u32x4*)(base + (wm * WTM + mi * 32) * RB + off);
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni) Mma<T>::run(acc[mi][ni], af, bfr[ni]);
+          }
+        }
+      }
     }
   }
   epilogue_lds<T, BM, BN, WGM, WGN, EP, S * STAGE>(p, acc, smem, m0, n0, wm, wn, lane, tid);
