@@ -28,7 +28,8 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "w8f16": 2516.6, "f32": 157.3}   # dense MFMA
+PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "w8f16": 2516.6, "w6f16": 2516.6, "w4f16": 2516.6,
+               "f32": 157.3}   # dense MFMA (the quantised dtypes multiply in fp16)
 PEAK_HBM_GBS = 8000.0
 METRIC = "encoder audio-sec/sec (x realtime) at 1 GPU + % of fp16 MFMA roofline"
 

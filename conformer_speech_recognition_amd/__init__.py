@@ -20,7 +20,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgigaam.so")
 
 OK, E_INVAL, E_WORKSPACE, E_UNSUPPORTED, E_HIP = 0, -1, -2, -3, -4
-DTYPES = {"f32": 0, "f16": 1, "bf16": 2, "w8f16": 3}
+DTYPES = {"f32": 0, "f16": 1, "bf16": 2, "w8f16": 3, "w6f16": 4, "w4f16": 5}
 STAGE_MEL, STAGE_SUB, STAGE_LAYER = 0, 1, 2
 MAX_BATCH = 256
 
@@ -272,7 +272,8 @@ def tokens_list(out: dict) -> list[list[int]]:
 
 def debug_gemm(dtype: str, A, W, bias=None, scale=None, stream=None):
     """C = A @ W.T + bias with the encoder's GEMM kernel (A, W device tensors in the
-    storage type of ``dtype``; int8 W with fp16 ``scale`` for 'w8f16')."""
+    storage type of ``dtype``; for 'w8f16' / 'w6f16' / 'w4f16' W is the packed uint8
+    rows [N][K * bits / 8] of the header's layout, with fp16 ``scale`` [N][K / 64])."""
     import torch
     M, K = A.shape
     N = W.shape[0]

@@ -16,7 +16,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 namespace gg {
 
 // Element storage types of the GEMM/attention operands.
-enum DType { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_W8F16 = 3 };
+enum DType { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_W8F16 = 3, DT_W6F16 = 4, DT_W4F16 = 5 };
 
 // Per-call batch geometry, written into the workspace by the meta kernel.
 // Row r of the packed mel / sub / encoder spaces belongs to clip rowclip_X[r];

@@ -18,6 +18,7 @@
 namespace gg {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <typename T> struct Mma;
 template <> struct Mma<f16> {
@@ -57,17 +58,31 @@ template <> __device__ __forceinline__ u32x4 pack8<bf16>(f32x4 lo, f32x4 hi) {
   return __builtin_bit_cast(u32x4, h);
 }
 
-// 16 int8 weights times one fp16 scale -> 16 fp16 (two 16-byte chunks).
+// 16 packed QB-bit weights times one fp16 scale -> 16 fp16 (two 16-byte chunks). The 16
+// weights are 2*QB bytes: QB = 8 one byte each; QB = 4 two per byte, low nibble first;
+// QB = 6 four per 3 bytes (a little-endian 24-bit word, weight j at bits 6j..6j+5). Every
+// value is a two's-complement integer in [-(2^(QB-1) - 1), 2^(QB-1) - 1].
+template <int QB> __device__ __forceinline__ int qval(u32x4 q, int i);
+template <> __device__ __forceinline__ int qval<8>(u32x4 q, int i) {
+  return (int)(int8_t)((q[i >> 2] >> (8 * (i & 3))) & 0xff);
+}
+template <> __device__ __forceinline__ int qval<4>(u32x4 q, int i) {
+  return ((int)(q[i >> 3] << (28 - 4 * (i & 7)))) >> 28;
+}
+template <> __device__ __forceinline__ int qval<6>(u32x4 q, int i) {
+  const int g = i >> 2, j = i & 3;                  // 24-bit group g at byte 3g
+  const int bit = 24 * g + 6 * j;                   // bit offset in the 96-bit string
+  const int w = bit >> 5, o = bit & 31;
+  uint64_t two = (uint64_t)q[w] | ((w + 1 < 3) ? (uint64_t)q[w + 1] << 32 : 0ull);
+  return ((int)((uint32_t)(two >> o) << 26)) >> 26;
+}
+template <int QB>
 __device__ __forceinline__ void dequant16(u32x4 q, float s, u32x4& lo, u32x4& hi) {
   f16x8 a, b;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int v = (int)(int8_t)((q[w] >> (8 * i)) & 0xff);
-      f16 h = (f16)((float)v * s);
-      if (w < 2) a[w * 4 + i] = h; else b[(w - 2) * 4 + i] = h;
-    }
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (f16)((float)qval<QB>(q, i) * s);
+    b[i] = (f16)((float)qval<QB>(q, 8 + i) * s);
   }
   lo = __builtin_bit_cast(u32x4, a);
   hi = __builtin_bit_cast(u32x4, b);
@@ -177,7 +192,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x16 (&acc)[MI][
   }
 }
 
-template <typename T, int BM, int BN, int WGM, int WGN, int AM, bool Q8, int EP>
+template <typename T, int BM, int BN, int WGM, int WGN, int AM, int QB, int EP>
 __global__ void __launch_bounds__(256) k_gemm(GemmParams p) {
   constexpr int ES = sizeof(T);
   constexpr int EPC = 16 / ES;                  // elements per 16-byte chunk
@@ -186,6 +201,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmParams p) {
   constexpr int MI = WTM / 32, NI = WTN / 32;
   constexpr int LDR = 9;                        // 16-byte slots per LDS row (8 + pad)
   constexpr int A_CH = BM * 8 / 256;
+  constexpr bool Q8 = QB != 0;                 // quantised weights (QB bits each)
   constexpr int B_CH = Q8 ? BN * 4 / 256 : BN * 8 / 256;
   constexpr bool AF = (AM == A_F32 || AM == A_CONV_F32) && ES == 2;   // float source
   constexpr bool CONV = (AM == A_CONV || AM == A_CONV_F32);
@@ -273,7 +289,11 @@ __global__ void __launch_bounds__(256) k_gemm(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) {
       if constexpr (Q8) {
-        rb[i] = *(const u32x4*)((const int8_t*)p.W + b_off[i] + kk + b_col[i] * 16);
+        // 16 weights = 2 QB bytes at byte (k * QB / 8) of the packed row
+        const uint8_t* q = (const uint8_t*)p.W + (b_off[i] + kk + b_col[i] * 16) * QB / 8;
+        if constexpr (QB == 8) rb[i] = *(const u32x4*)q;
+        else if constexpr (QB == 4) { const u32x2 v = *(const u32x2*)q; rb[i] = u32x4{v[0], v[1], 0, 0}; }
+        else rb[i] = u32x4{((const uint32_t*)q)[0], ((const uint32_t*)q)[1], ((const uint32_t*)q)[2], 0};
         int gn = n0 + b_row[i];
         gn = gn < p.N ? gn : p.N - 1;
         rs[i] = (float)p.Wscale[(long)gn * (p.K / 64) + kt];
@@ -295,7 +315,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmParams p) {
     for (int i = 0; i < B_CH; ++i) {
       if constexpr (Q8) {
         u32x4 lo, hi;
-        dequant16(rb[i], rs[i], lo, hi);
+        dequant16<QB>(rb[i], rs[i], lo, hi);
         sB[buf][b_row[i]][b_col[i] * 2] = lo;
         sB[buf][b_row[i]][b_col[i] * 2 + 1] = hi;
       } else {
@@ -566,15 +586,15 @@ __global__ void __launch_bounds__(64 * WGM * WGN, OCC) k_gemm_dl(GemmParams p) {
 // ---------------------------------------------------------------------------------------
 // dispatch
 
-template <typename T, int BM, int BN, int WGM, int WGN, bool Q8>
+template <typename T, int BM, int BN, int WGM, int WGN, int QB>
 static hipError_t run_epi(AMode am, Epi ep, const GemmParams& p, hipStream_t s) {
   dim3 grid(((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN));
 #define GG_L(AMv, EPv)                                                                   \
   if (am == AMv && ep == EPv) {                                                          \
-    hipLaunchKernelGGL((k_gemm<T, BM, BN, WGM, WGN, AMv, Q8, EPv>), grid, dim3(256), 0, s, p); \
+    hipLaunchKernelGGL((k_gemm<T, BM, BN, WGM, WGN, AMv, QB, EPv>), grid, dim3(256), 0, s, p); \
     return hipGetLastError();                                                            \
   }
-  if constexpr (Q8) {
+  if constexpr (QB != 0) {
     GG_L(A_PLAIN, E_SILU) GG_L(A_PLAIN, E_RESID) GG_L(A_DUAL, E_STORE) GG_L(A_PLAIN, E_GLU)
     GG_L(A_PLAIN, E_F32)
   } else {
@@ -590,10 +610,10 @@ static hipError_t run_epi(AMode am, Epi ep, const GemmParams& p, hipStream_t s) 
   return hipErrorInvalidValue;
 }
 
-template <typename T, bool Q8>
+template <typename T, int QB>
 static hipError_t run_tiles(AMode am, Epi ep, const GemmParams& p, hipStream_t s) {
-  if (p.N <= 512 && ep != E_GLU) return run_epi<T, 128, 64, 4, 1, Q8>(am, ep, p, s);
-  return run_epi<T, 128, 128, 2, 2, Q8>(am, ep, p, s);
+  if (p.N <= 512 && ep != E_GLU) return run_epi<T, 128, 64, 4, 1, QB>(am, ep, p, s);
+  return run_epi<T, 128, 128, 2, 2, QB>(am, ep, p, s);
 }
 
 // Direct-load pipeline for fp16/bf16 operands already in T (plain or dual A). Two shapes,
@@ -620,7 +640,7 @@ static hipError_t run_dl_shape(AMode am, Epi ep, const GemmParams& p, hipStream_
   return run_dl<T, 128, 256, 2, 4, 2, 64>(am, ep, p, s);
 }
 
-hipError_t launch_gemm(DType dt, bool w_int8, AMode am, Epi ep, const GemmParams& p,
+hipError_t launch_gemm(DType dt, int qbits, AMode am, Epi ep, const GemmParams& p,
                        hipStream_t s) {
   if (p.M <= 0) return hipSuccess;
   // fp32 A sources are native for the fp32 GEMM
@@ -628,16 +648,21 @@ hipError_t launch_gemm(DType dt, bool w_int8, AMode am, Epi ep, const GemmParams
     if (am == A_F32) am = A_PLAIN;
     if (am == A_CONV_F32) am = A_CONV;
   }
-  const bool direct = !w_int8 && (am == A_PLAIN || am == A_DUAL) && p.K % 64 == 0 &&
+  const bool direct = qbits == 0 && (am == A_PLAIN || am == A_DUAL) && p.K % 64 == 0 &&
                       (ep == E_STORE || ep == E_SILU || ep == E_RESID || ep == E_GLU || ep == E_F32) &&
                       (am == A_PLAIN || ep == E_STORE);
   switch (dt) {
-    case DT_F32: return run_tiles<float, false>(am, ep, p, s);
-    case DT_F16: return direct ? run_dl_shape<f16>(am, ep, p, s) : run_tiles<f16, false>(am, ep, p, s);
-    case DT_BF16: return direct ? run_dl_shape<bf16>(am, ep, p, s) : run_tiles<bf16, false>(am, ep, p, s);
+    case DT_F32: return run_tiles<float, 0>(am, ep, p, s);
+    case DT_F16: return direct ? run_dl_shape<f16>(am, ep, p, s) : run_tiles<f16, 0>(am, ep, p, s);
+    case DT_BF16: return direct ? run_dl_shape<bf16>(am, ep, p, s) : run_tiles<bf16, 0>(am, ep, p, s);
     case DT_W8F16:
-      if (w_int8) return run_tiles<f16, true>(am, ep, p, s);
-      return direct ? run_dl_shape<f16>(am, ep, p, s) : run_tiles<f16, false>(am, ep, p, s);
+    case DT_W6F16:
+    case DT_W4F16:
+      if (qbits == 8) return run_tiles<f16, 8>(am, ep, p, s);
+      if (qbits == 6) return run_tiles<f16, 6>(am, ep, p, s);
+      if (qbits == 4) return run_tiles<f16, 4>(am, ep, p, s);
+      if (qbits != 0) return hipErrorInvalidValue;
+      return direct ? run_dl_shape<f16>(am, ep, p, s) : run_tiles<f16, 0>(am, ep, p, s);
   }
   return hipErrorInvalidValue;
 }

@@ -146,10 +146,15 @@ extern "C" int gigaam_check_config(const gigaam_config* c) {
   if (c->conv_kernel != 31 && c->conv_kernel != 15 && c->conv_kernel != 5)
     return fail(GIGAAM_E_UNSUPPORTED, "conv_kernel %d (5, 15, 31 built)", c->conv_kernel);
   if (c->n_classes < 2 || c->n_classes > 8192) return fail(GIGAAM_E_INVAL, "n_classes %d", c->n_classes);
-  if (c->dtype < GIGAAM_F32 || c->dtype > GIGAAM_W8F16) return fail(GIGAAM_E_INVAL, "dtype %d", c->dtype);
+  if (c->dtype < GIGAAM_F32 || c->dtype > GIGAAM_W4F16) return fail(GIGAAM_E_INVAL, "dtype %d", c->dtype);
   if (!(c->rope_base > 0.f) || !(c->ln_eps > 0.f) || !(c->bn_eps > 0.f))
     return fail(GIGAAM_E_INVAL, "rope_base / eps must be positive");
   return GIGAAM_OK;
+}
+
+// bits of the packed quantised linears of a dtype (0: stored in the operand type)
+static int qbits_of(int dtype) {
+  return dtype == GIGAAM_W8F16 ? 8 : dtype == GIGAAM_W6F16 ? 6 : dtype == GIGAAM_W4F16 ? 4 : 0;
 }
 
 // --------------------------------------------------------------------------- canonical list
@@ -175,11 +180,11 @@ std::vector<Entry> canonical(const gigaam_config& c) {
     off += x.count;
     e.push_back(x);
   };
-  const bool q8 = c.dtype == GIGAAM_W8F16;
+  const bool qd = qbits_of(c.dtype) != 0;
   auto lin = [&](const std::string& pre, const char* local, int N, int K) {
     bool q = false;
     for (const char* s : kQuantized) q |= (std::strcmp(s, local) == 0);
-    if (q && q8) {
+    if (q && qd) {
       add(pre + local + ".weight_q", 2, N, K);
       add(pre + local + ".weight_scale", 2, N, K / 64);
     } else {
@@ -227,7 +232,7 @@ std::vector<Entry> canonical(const gigaam_config& c) {
 }
 
 // --------------------------------------------------------------------------- packed layout
-struct Lin { size_t w = 0, s = 0, b = 0; bool q8 = false; };
+struct Lin { size_t w = 0, s = 0, b = 0; int qb = 0; };   // qb: bits of packed weights, 0 = T
 struct LayerOff {
   size_t ff1_g, ff1_b; Lin ff1_1, ff1_2;
   size_t att_g, att_b; Lin qkv, out;
@@ -248,14 +253,14 @@ Layout layout(const gigaam_config& c) {
   Layout L;
   const int es = c.dtype == GIGAAM_F32 ? 4 : 2;
   L.wsize = es;
-  const bool q8 = c.dtype == GIGAAM_W8F16;
+  const int qbits = qbits_of(c.dtype);
   const size_t d = c.d_model, f = c.d_ff;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
   auto lin = [&](size_t N, size_t K, bool quant) {
     Lin l;
-    l.q8 = quant && q8;
-    if (l.q8) { l.w = take(N * K); l.s = take(N * (K / 64) * 2); }
+    l.qb = quant ? qbits : 0;
+    if (l.qb) { l.w = take(N * K * l.qb / 8); l.s = take(N * (K / 64) * 2); }
     else l.w = take(N * K * es);
     l.b = take(N * 4);
     return l;
@@ -352,13 +357,19 @@ struct Packer {
     for (size_t r = 0; r < row_map.size(); ++r) {
       const std::string& base = names[row_map[r].first];
       const size_t sr = row_map[r].second;
-      if (l.q8) {
+      if (l.qb) {
         const float* q = get(base + ".weight_q");
         const float* s = get(base + ".weight_scale");
+        const float qmax = (float)((1 << (l.qb - 1)) - 1);
+        uint8_t* row = (uint8_t*)dst + l.w + r * K * l.qb / 8;
+        std::memset(row, 0, K * l.qb / 8);
         for (size_t k = 0; k < K; ++k) {
           const float v = q[sr * K + k];
-          if (!(v >= -127.f && v <= 127.f) || v != std::nearbyint(v)) err = 1;
-          dst[l.w + r * K + k] = (char)(int8_t)v;
+          if (!(v >= -qmax && v <= qmax) || v != std::nearbyint(v)) err = 1;
+          const uint32_t u = (uint32_t)(int)v & ((1u << l.qb) - 1);
+          const size_t bit = k * l.qb;               // little-endian bit string of the row
+          for (int j = 0; j < l.qb; ++j)
+            if (u >> j & 1) row[(bit + j) >> 3] |= (uint8_t)(1u << ((bit + j) & 7));
         }
         for (size_t g = 0; g < K / 64; ++g) {
           const uint16_t h = f32_to_f16_bits(s[sr * (K / 64) + g]);
@@ -479,7 +490,7 @@ extern "C" int gigaam_pack_weights(const gigaam_config* cfg, const float* canoni
     for (size_t i = 0; i < (size_t)c.n_classes * d; ++i) P.put_w(L.head_w, i, w[i]);
     P.copy_f(L.head_b, "head.bias", c.n_classes);
   }
-  if (P.err) return fail(GIGAAM_E_INVAL, "an int8 weight is not an integer in [-127, 127]");
+  if (P.err) return fail(GIGAAM_E_INVAL, "a quantised weight is not an integer in [-(2^(b-1)-1), 2^(b-1)-1]");
   return GIGAAM_OK;
 }
 
@@ -597,7 +608,6 @@ int run(gigaam_model* m, const float* pcm, const int32_t* lengths, int32_t B, in
   const gigaam_config& c = m->cfg;
   const int d = c.d_model, f = c.d_ff, H = c.n_heads, dk = d / H, C = c.n_classes;
   const DType dt = (DType)c.dtype;
-  const bool q8 = dt == DT_W8F16;
   const size_t es = dt == DT_F32 ? 4 : 2;
   hipStream_t s = (hipStream_t)stream_v;
 
@@ -659,13 +669,13 @@ int run(gigaam_model* m, const float* pcm, const int32_t* lengths, int32_t B, in
     HIP_TRY(hipMemcpyAsync(stage_out, src, n * 4, hipMemcpyDeviceToDevice, s));
     return GIGAAM_OK;
   };
-  auto G = [&](const char* name, AMode am, Epi ep, bool wq, const GemmParams& gp) -> int {
+  auto G = [&](const char* name, AMode am, Epi ep, int wq, const GemmParams& gp) -> int {
     LAUNCH(name, launch_gemm(dt, wq, am, ep, gp, s));
     return GIGAAM_OK;
   };
   auto lin = [&](const Lin& l, int M, int N, int K, const void* A, int lda, void* Cp, int ldc,
                  float alpha = 1.f) {
-    return gemm(M, N, K, A, lda, P + l.w, l.q8 ? P + l.s : nullptr, (const float*)(P + l.b), Cp, ldc, alpha);
+    return gemm(M, N, K, A, lda, P + l.w, l.qb ? P + l.s : nullptr, (const float*)(P + l.b), Cp, ldc, alpha);
   };
   int rc;
 
@@ -710,32 +720,32 @@ int run(gigaam_model* m, const float* pcm, const int32_t* lengths, int32_t B, in
     const LayerOff& o = L.layers[li];
     const int tap = 1000 + 10 * li;
     // a5 FFN1 (half step)
-    if ((rc = G("gemm.ffn_up", A_PLAIN, E_SILU, o.ff1_1.q8, lin(o.ff1_1, U_tot, f, d, y, d, hid, f)))) return rc;
-    if ((rc = G("gemm.ffn_down", A_PLAIN, E_RESID, o.ff1_2.q8, lin(o.ff1_2, U_tot, d, f, hid, f, x, d, 0.5f)))) return rc;
+    if ((rc = G("gemm.ffn_up", A_PLAIN, E_SILU, o.ff1_1.qb, lin(o.ff1_1, U_tot, f, d, y, d, hid, f)))) return rc;
+    if ((rc = G("gemm.ffn_down", A_PLAIN, E_RESID, o.ff1_2.qb, lin(o.ff1_2, U_tot, d, f, hid, f, x, d, 0.5f)))) return rc;
     if (stage == tap + 0) return copy_out(x, (size_t)U_tot * d);
     // a6-a9 attention: LN + rope(y) -> [Q|K] from r, V from y -> flash attention -> out proj
     if ((rc = LN(LN_ROPE, o.att_g, o.att_b, nullptr, nullptr, y, r))) return rc;
     {
       GemmParams gq = lin(o.qkv, U_tot, 3 * d, d, r, d, qkv, 3 * d);
       gq.A2 = y; gq.nsplit = 2 * d;
-      if ((rc = G("gemm.qkv", A_DUAL, E_STORE, o.qkv.q8, gq))) return rc;
+      if ((rc = G("gemm.qkv", A_DUAL, E_STORE, o.qkv.qb, gq))) return rc;
     }
     LAUNCH("attention", launch_attention(dt, dk, ap, s));
-    if ((rc = G("gemm.out_proj", A_PLAIN, E_RESID, o.out.q8, lin(o.out, U_tot, d, d, ao, d, x, d)))) return rc;
+    if ((rc = G("gemm.out_proj", A_PLAIN, E_RESID, o.out.qb, lin(o.out, U_tot, d, d, ao, d, x, d)))) return rc;
     if (stage == tap + 1) return copy_out(x, (size_t)U_tot * d);
     // a10-a12 conv module
     if ((rc = LN(LN_PLAIN, o.cv_g, o.cv_b, nullptr, nullptr, y, nullptr))) return rc;
-    if ((rc = G("gemm.pw1_glu", A_PLAIN, E_GLU, o.pw1.q8, lin(o.pw1, U_tot, 2 * d, d, y, d, hid, d)))) return rc;
+    if ((rc = G("gemm.pw1_glu", A_PLAIN, E_GLU, o.pw1.qb, lin(o.pw1, U_tot, 2 * d, d, y, d, hid, d)))) return rc;
     dp.w = (const float*)(P + o.dw_w); dp.b = (const float*)(P + o.dw_b);
     dp.bn_g = (const float*)(P + o.bn_g); dp.bn_b = (const float*)(P + o.bn_b);
     dp.bn_m = (const float*)(P + o.bn_m); dp.bn_v = (const float*)(P + o.bn_v);
     LAUNCH("dwconv_bn_silu", launch_dwconv(dt, c.conv_kernel, dp, s));
-    if ((rc = G("gemm.pw2", A_PLAIN, E_RESID, o.pw2.q8, lin(o.pw2, U_tot, d, d, hid2, d, x, d)))) return rc;
+    if ((rc = G("gemm.pw2", A_PLAIN, E_RESID, o.pw2.qb, lin(o.pw2, U_tot, d, d, hid2, d, x, d)))) return rc;
     if (stage == tap + 2) return copy_out(x, (size_t)U_tot * d);
     // a13 FFN2 (half step) + final norm fused with the next block's first pre-norm
     if ((rc = LN(LN_PLAIN, o.ff2_g, o.ff2_b, nullptr, nullptr, y, nullptr))) return rc;
-    if ((rc = G("gemm.ffn_up", A_PLAIN, E_SILU, o.ff2_1.q8, lin(o.ff2_1, U_tot, f, d, y, d, hid, f)))) return rc;
-    if ((rc = G("gemm.ffn_down", A_PLAIN, E_RESID, o.ff2_2.q8, lin(o.ff2_2, U_tot, d, f, hid, f, x, d, 0.5f)))) return rc;
+    if ((rc = G("gemm.ffn_up", A_PLAIN, E_SILU, o.ff2_1.qb, lin(o.ff2_1, U_tot, f, d, y, d, hid, f)))) return rc;
+    if ((rc = G("gemm.ffn_down", A_PLAIN, E_RESID, o.ff2_2.qb, lin(o.ff2_2, U_tot, d, f, hid, f, x, d, 0.5f)))) return rc;
     if (stage == tap + 3) return copy_out(x, (size_t)U_tot * d);
     if (li + 1 < c.n_layers) {
       const LayerOff& nx = L.layers[li + 1];
@@ -780,20 +790,21 @@ extern "C" int gigaam_encode_stage(gigaam_model* model, const float* pcm_dev, co
 extern "C" int gigaam_debug_gemm(int32_t dtype, int32_t M, int32_t N, int32_t K, const void* A_dev,
                                  const void* W_dev, const void* scale_dev, const float* bias_dev,
                                  float* C_dev, void* hip_stream) {
-  if (dtype < GIGAAM_F32 || dtype > GIGAAM_W8F16) return fail(GIGAAM_E_INVAL, "dtype %d", dtype);
+  if (dtype < GIGAAM_F32 || dtype > GIGAAM_W4F16) return fail(GIGAAM_E_INVAL, "dtype %d", dtype);
   if (M < 1 || N < 1 || K < 1) return fail(GIGAAM_E_INVAL, "bad shape %d x %d x %d", M, N, K);
   if (K % (dtype == GIGAAM_F32 ? 32 : 64)) return fail(GIGAAM_E_INVAL, "K %d not a multiple of the k-tile", K);
-  if (!A_dev || !W_dev || !C_dev || (dtype == GIGAAM_W8F16 && !scale_dev))
+  const int qb = qbits_of(dtype);
+  if (!A_dev || !W_dev || !C_dev || (qb && !scale_dev))
     return fail(GIGAAM_E_INVAL, "NULL pointer");
   GemmParams p = gemm(M, N, K, A_dev, K, W_dev, scale_dev, bias_dev, C_dev, N);
-  HIP_TRY(launch_gemm((DType)dtype, dtype == GIGAAM_W8F16, A_PLAIN, E_F32, p, (hipStream_t)hip_stream));
+  HIP_TRY(launch_gemm((DType)dtype, qb, A_PLAIN, E_F32, p, (hipStream_t)hip_stream));
   return GIGAAM_OK;
 }
 
 extern "C" int gigaam_debug_attention(int32_t dtype, int32_t d_model, int32_t n_heads, int32_t batch,
                                       const int32_t* frames_host, const void* qkv_dev, void* out_dev,
                                       void* workspace, size_t workspace_bytes, void* hip_stream) {
-  if (dtype < GIGAAM_F32 || dtype > GIGAAM_W8F16) return fail(GIGAAM_E_INVAL, "dtype %d", dtype);
+  if (dtype < GIGAAM_F32 || dtype > GIGAAM_W4F16) return fail(GIGAAM_E_INVAL, "dtype %d", dtype);
   if (batch < 1 || batch > GIGAAM_MAX_BATCH) return fail(GIGAAM_E_INVAL, "batch %d", batch);
   if (!frames_host || !qkv_dev || !out_dev || !workspace) return fail(GIGAAM_E_INVAL, "NULL pointer");
   if ((uintptr_t)workspace & 255) return fail(GIGAAM_E_INVAL, "workspace not 256-B aligned");

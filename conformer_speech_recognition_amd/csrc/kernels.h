@@ -26,8 +26,8 @@ struct GemmParams {
   int M, N, K;
   const void* A; int lda;
   const void* A2; int nsplit;
-  const void* W; int ldw;          // [N][ldw], T or int8
-  const f16* Wscale;               // int8 weights: [N][K/64] fp16 scales
+  const void* W; int ldw;          // [N][ldw] in T, or packed qbits-bit rows (ldw in weights)
+  const f16* Wscale;               // quantised weights: [N][K/64] fp16 scales
   const float* bias;               // [N] or nullptr
   void* C; int ldc;
   float alpha;
@@ -37,7 +37,9 @@ struct GemmParams {
   int cin;                         // conv modes: input channels (row length of source)
 };
 
-hipError_t launch_gemm(DType dt, bool w_int8, AMode am, Epi ep, const GemmParams& p,
+// qbits: 0 = weights stored in the operand type; 8 / 6 / 4 = packed quantised rows with
+// fp16 group scales (dequantised to fp16 in the kernel)
+hipError_t launch_gemm(DType dt, int qbits, AMode am, Epi ep, const GemmParams& p,
                        hipStream_t s);
 
 // ---- meta -------------------------------------------------------------------------

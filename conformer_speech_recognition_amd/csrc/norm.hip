@@ -124,7 +124,9 @@ hipError_t launch_layernorm(DType dt, LnMode mode, const LnParams& p, hipStream_
   switch (dt) {
     case DT_F32: return ln_widths<float>(mode, p, s);
     case DT_F16:
-    case DT_W8F16: return ln_widths<f16>(mode, p, s);
+    case DT_W8F16:
+    case DT_W6F16:
+    case DT_W4F16: return ln_widths<f16>(mode, p, s);
     case DT_BF16: return ln_widths<bf16>(mode, p, s);
   }
   return hipErrorInvalidValue;

@@ -55,10 +55,17 @@ enum {
   GIGAAM_F32 = 0,    /* fp32 weights and operands (fp32 MFMA)                         */
   GIGAAM_F16 = 1,    /* fp16 weights and GEMM/attention operands, fp32 accumulate     */
   GIGAAM_BF16 = 2,   /* bf16 weights and operands, fp32 accumulate                    */
-  GIGAAM_W8F16 = 3   /* FFN, attention and pointwise-conv linears stored as int8 with
+  GIGAAM_W8F16 = 3,  /* FFN, attention and pointwise-conv linears stored as int8 with
                         one fp16 scale per group of 64 input weights, dequantised
                         in-kernel to fp16; everything else as GIGAAM_F16             */
+  GIGAAM_W6F16 = 4,  /* as GIGAAM_W8F16 with 6-bit weights in [-31, 31]             */
+  GIGAAM_W4F16 = 5   /* as GIGAAM_W8F16 with 4-bit weights in [-7, 7]               */
 };
+/* Weight-only quantisation ("GigaAM MLX port for Mac", section "How precision affects
+ * size and speed": a shared scale per group of 64 weights; INT8, INT6 and INT4 variants).
+ * Packed device rows: weight k of a row occupies bits [k*b, k*b + b) of the row's
+ * little-endian bit string (b = 8, 6, 4; two's complement), rows of K*b/8 bytes; scales
+ * fp16 [N][K/64]. A weight is q * scale[n][k / 64].                                    */
 
 /* Largest batch one gigaam_encode call accepts. */
 #define GIGAAM_MAX_BATCH 256
@@ -76,7 +83,7 @@ typedef struct gigaam_config {
   int32_t hop_length;   /* 160  (fixed)                                                */
   int32_t sub_kernel;   /* 5    (fixed; padding 2)                                     */
   int32_t sub_stride;   /* 2    (fixed)                                                */
-  int32_t dtype;        /* GIGAAM_F32 ... GIGAAM_W8F16                                 */
+  int32_t dtype;        /* GIGAAM_F32 ... GIGAAM_W4F16                                 */
   float rope_base;      /* 5000                                                        */
   float ln_eps;         /* LayerNorm epsilon (1e-5)                                    */
   float bn_eps;         /* BatchNorm epsilon (1e-5)                                    */
@@ -104,8 +111,10 @@ int gigaam_check_config(const gigaam_config* cfg);
  * listed by gigaam_canonical_entry, concatenated in that order, each in PyTorch layout
  * (Linear [out, in]; Conv1d [out, in, K]; pointwise convs [out, in]; depthwise
  * [channels, K]), holding the checkpoint values exactly (fp16/bf16 values for those
- * dtypes; for GIGAAM_W8F16 the quantised linears appear as "<name>.weight_q" holding
- * integers in [-127, 127] and "<name>.weight_scale" [out, in/64] holding fp16 values).
+ * dtypes; for GIGAAM_W8F16 / W6F16 / W4F16 the quantised linears appear as
+ * "<name>.weight_q" holding integers in [-(2^(b-1)-1), 2^(b-1)-1] and
+ * "<name>.weight_scale" [out, in/64] holding fp16 values; out-of-range or non-integer
+ * values make gigaam_pack_weights fail with GIGAAM_E_INVAL).
  * gigaam_pack_weights turns it into the device layout (host -> host); the caller
  * copies the packed bytes to the device and passes that pointer to gigaam_create.
  * ------------------------------------------------------------------------------- */
@@ -196,8 +205,9 @@ int gigaam_encode_stage(gigaam_model* model, const float* pcm_dev, const int32_t
  * Diagnostics: the encoder's GEMM kernel on its own,
  *   C[m][n] = sum_k A[m][k] * W[n][k] + bias[n]      (fp32 accumulate, fp32 out)
  * A_dev [M][K] and W_dev [N][K] in the storage type of `dtype` (GIGAAM_F32: float,
- * GIGAAM_F16: fp16, GIGAAM_BF16: bf16; GIGAAM_W8F16: A fp16, W int8 with scale_dev
- * [N][K/64] fp16 scales); bias_dev float[N] or NULL; C_dev float [M][N].
+ * GIGAAM_F16: fp16, GIGAAM_BF16: bf16; GIGAAM_W8F16 / W6F16 / W4F16: A fp16, W the
+ * packed b-bit rows described above with scale_dev [N][K/64] fp16 scales); bias_dev
+ * float[N] or NULL; C_dev float [M][N].
  * K must be a multiple of 64 (32 for GIGAAM_F32). Errors: GIGAAM_E_INVAL, GIGAAM_E_HIP. */
 int gigaam_debug_gemm(int32_t dtype, int32_t M, int32_t N, int32_t K, const void* A_dev,
                       const void* W_dev, const void* scale_dev, const float* bias_dev,
@@ -206,7 +216,7 @@ int gigaam_debug_gemm(int32_t dtype, int32_t M, int32_t N, int32_t K, const void
 /* Diagnostics: the encoder's attention kernel on its own, over packed clips.
  * frames_host int32 [batch]: frames U_b of each clip (>= 1); qkv_dev [sum U_b][3 d_model]
  * holds q | k | v per frame in the storage type of `dtype` (fp32, fp16, bf16;
- * GIGAAM_W8F16 = fp16); out_dev [sum U_b][d_model] the same type. d_model / n_heads must
+ * the quantised dtypes = fp16); out_dev [sum U_b][d_model] the same type. d_model / n_heads must
  * be 48 or 64. workspace: device memory of at least
  *   16 * (batch + 1) + 16 * sum U_b + 4096 bytes (256-B aligned).
  * Errors: GIGAAM_E_INVAL, GIGAAM_E_WORKSPACE, GIGAAM_E_UNSUPPORTED, GIGAAM_E_HIP.        */

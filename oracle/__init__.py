@@ -335,23 +335,27 @@ def ctc_collapse(ids, blank: int) -> list[int]:
 # weights and the whole encoder
 # ==================================================================================
 
-def dequantize_int8_g64(q: np.ndarray, s: np.ndarray, group: int = 64) -> np.ndarray:
-    """w[n, k] = q[n, k] * s[n, k // 64] (one shared scale per group of 64 weights;
-    [ML-port] "How precision affects size and speed")."""
+def dequantize_g64(q: np.ndarray, s: np.ndarray, group: int = 64) -> np.ndarray:
+    """w[n, k] = q[n, k] * s[n, k // 64] (one shared scale per group of 64 weights, for
+    the INT8, INT6 and INT4 variants alike; [ML-port] "How precision affects size and
+    speed")."""
     q = np.asarray(q, dtype=np.float64)
     s = np.asarray(s, dtype=np.float64)
     return q * np.repeat(s, group, axis=1)
 
 
+dequantize_int8_g64 = dequantize_g64
+
+
 def materialize(weights: dict, dtype=np.float64) -> dict:
-    """Cast the checkpoint to the compute dtype; int8 linears are dequantized."""
+    """Cast the checkpoint to the compute dtype; quantised linears are dequantized."""
     P = {}
     for name, a in weights.items():
         if name.endswith(".weight_scale"):
             continue
         if name.endswith(".weight_q"):
             base = name[: -len(".weight_q")]
-            P[base + ".weight"] = dequantize_int8_g64(a, weights[base + ".weight_scale"]).astype(dtype)
+            P[base + ".weight"] = dequantize_g64(a, weights[base + ".weight_scale"]).astype(dtype)
         else:
             P[name] = np.asarray(a, dtype=dtype)
     return P

@@ -41,7 +41,7 @@ def round_to_bf16(a: np.ndarray) -> np.ndarray:
 def round_storage(a: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "f32":
         return np.asarray(a, dtype=np.float32)
-    if dtype in ("f16", "w8f16"):
+    if dtype in ("f16",) + tuple(QUANT_BITS):
         return round_to_f16(a)
     if dtype == "bf16":
         return round_to_bf16(a)
@@ -90,6 +90,9 @@ def model_config(n_layers: int, d_model: int, n_heads: int, d_ff: int, conv_kern
                 n_mels=64, n_fft=320, win_length=320, hop_length=160,
                 sub_kernel=5, sub_stride=2, rope_base=5000.0, ln_eps=1e-5, bn_eps=1e-5)
 
+
+# weight-only quantised checkpoints: bits per linear weight of each dtype
+QUANT_BITS = {"w8f16": 8, "w6f16": 6, "w4f16": 4}
 
 QUANTIZED_SUFFIXES = ("ff1.linear1", "ff1.linear2", "att.linear_q", "att.linear_k",
                       "att.linear_v", "att.linear_out", "conv.pointwise1",
@@ -148,9 +151,9 @@ def make_weights(cfg: dict, seed: int, head_seed: int | None = None) -> dict[str
 
     All arrays are returned as float32 holding the rounded values. With
     ``head_seed`` the CTC head is redrawn from its own stream (same draw rule).
-    For ``dtype == 'w8f16'`` the linears in QUANTIZED_SUFFIXES are replaced by an
-    int8 checkpoint: ``<name>.weight_q`` (int8 [N, K]) and ``<name>.weight_scale``
-    (float16 [N, K/64]); see ``quantize_int8_g64``.
+    For the quantised dtypes (QUANT_BITS) the linears in QUANTIZED_SUFFIXES are replaced
+    by a b-bit checkpoint: ``<name>.weight_q`` (int8 [N, K] holding b-bit integers) and
+    ``<name>.weight_scale`` (float16 [N, K/64]); see ``quantize_g64``.
     """
     rng = np.random.default_rng(seed)
     out: dict[str, np.ndarray] = {}
@@ -161,33 +164,40 @@ def make_weights(cfg: dict, seed: int, head_seed: int | None = None) -> dict[str
         C, d = cfg["n_classes"], cfg["d_model"]
         out["head.weight"] = round_storage(_draw(hr, (C, d), "w"), cfg["dtype"])
         out["head.bias"] = round_storage(_draw(hr, (C,), "b"), cfg["dtype"])
-    if cfg["dtype"] == "w8f16":
+    if cfg["dtype"] in QUANT_BITS:
+        bits = QUANT_BITS[cfg["dtype"]]
         for name in list(out):
             if name.endswith(".weight") and name[: -len(".weight")].endswith(QUANTIZED_SUFFIXES):
-                q, s = quantize_int8_g64(out.pop(name))
+                q, s = quantize_g64(out.pop(name), bits)
                 base = name[: -len(".weight")]
                 out[base + ".weight_q"] = q
                 out[base + ".weight_scale"] = s
     return out
 
 
-def quantize_int8_g64(w: np.ndarray, group: int = 64) -> tuple[np.ndarray, np.ndarray]:
-    """Checkpoint conversion to weight-only INT8 with one fp16 scale per group of 64
-    consecutive input-dim weights of one output row (symmetric):
-        s = fp16(max|w_group| / 127),  q = clamp(rint(w / s), -127, 127).
-    This is how the int8 checkpoint is produced (a one-off conversion, like the fp16
-    rounding above); the encoder itself only ever reads q and s.
+def quantize_g64(w: np.ndarray, bits: int = 8, group: int = 64) -> tuple[np.ndarray, np.ndarray]:
+    """Checkpoint conversion to weight-only b-bit integers with one fp16 scale per group
+    of 64 consecutive input-dim weights of one output row (symmetric, qmax = 2^(b-1) - 1):
+        s = fp16(max|w_group| / qmax),  q = clamp(rint(w / s), -qmax, qmax).
+    This is how the quantised checkpoints are produced (a one-off conversion, like the
+    fp16 rounding above); the encoder itself only ever reads q and s.
     """
+    qmax = (1 << (bits - 1)) - 1
     w = np.asarray(w, dtype=np.float64)
     N, K = w.shape
     assert K % group == 0
     g = w.reshape(N, K // group, group)
-    s = (np.abs(g).max(axis=2) / 127.0).astype(np.float16)
+    s = (np.abs(g).max(axis=2) / qmax).astype(np.float16)
     s64 = s.astype(np.float64)[:, :, None]
     with np.errstate(divide="ignore", invalid="ignore"):
         q = np.where(s64 > 0, np.rint(g / np.where(s64 > 0, s64, 1.0)), 0.0)
-    q = np.clip(q, -127, 127).astype(np.int8).reshape(N, K)
+    q = np.clip(q, -qmax, qmax).astype(np.int8).reshape(N, K)
     return q, s
+
+
+def quantize_int8_g64(w: np.ndarray, group: int = 64) -> tuple[np.ndarray, np.ndarray]:
+    """quantize_g64 with 8 bits."""
+    return quantize_g64(w, 8, group)
 
 
 from .workloads import (WORKLOADS, workload, workload_config,  # noqa: E402,F401

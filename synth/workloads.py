@@ -6,6 +6,7 @@ Shapes and precisions:
   batch32  32 clips of 1..20 s (lengths seed 2), 16 blocks d768, 257 classes, fp16 or bf16
   ml_long  300 s signal cut into ten 30 s chunks, 24 blocks d1024, 129 classes, fp16 (seed 4)
   int8_b64 64 clips of 10 s, 16 blocks d768, 34 classes, int8 g64 linears (signals seed 5)
+  int6_b64, int4_b64  the same with 6-bit / 4-bit g64 linears (the pages' INT6 / INT4)
 
 The pages measure real speech (200 short clips with a 3.9 s median, 20 s segments,
 a 5-minute recording, 30 s chunks for long audio; see "GigaAM on MLX ...", section
@@ -18,7 +19,9 @@ import numpy as np
 
 from . import make_signal, make_weights, model_config, pad_batch
 
-WORKLOADS = ("tiny", "v3_20s", "batch32", "batch32_bf16", "ml_long", "int8_b64")
+WORKLOADS = ("tiny", "v3_20s", "batch32", "batch32_bf16", "ml_long", "int8_b64", "int6_b64",
+             "int4_b64")
+_QUANT = {"int8_b64": "w8f16", "int6_b64": "w6f16", "int4_b64": "w4f16"}
 
 
 def _v3(n_classes: int, dtype: str, n_layers: int = 16) -> dict:
@@ -36,8 +39,8 @@ def workload_config(name: str) -> dict:
         return _v3(257, "bf16")
     if name == "ml_long":
         return model_config(24, 1024, 16, 4096, 31, 129, "f16")
-    if name == "int8_b64":
-        return _v3(34, "w8f16")
+    if name in _QUANT:
+        return _v3(34, _QUANT[name])
     raise KeyError(name)
 
 
@@ -53,7 +56,7 @@ def workload_signals(name: str) -> list[np.ndarray]:
     if name == "ml_long":
         x = make_signal(np.random.default_rng(4), 4_800_000)
         return [x[i * 480_000:(i + 1) * 480_000].copy() for i in range(10)]
-    if name == "int8_b64":
+    if name in _QUANT:
         rng = np.random.default_rng(5)
         return [make_signal(rng, 160_000) for _ in range(64)]
     raise KeyError(name)
@@ -63,7 +66,7 @@ def workload_weights(name: str, cfg: dict | None = None) -> dict[str, np.ndarray
     cfg = cfg or workload_config(name)
     if name == "tiny":
         return make_weights(cfg, 0)
-    if name in ("v3_20s", "int8_b64"):
+    if name == "v3_20s" or name in _QUANT:
         return make_weights(cfg, 1)
     if name in ("batch32", "batch32_bf16"):
         return make_weights(cfg, 1, head_seed=2)

@@ -55,13 +55,13 @@ def test_config_validation(gg, field, value, code):
     assert gg.lib().gigaam_check_config(ctypes.byref(c)) == code
 
 
-@pytest.mark.parametrize("name", ["tiny", "batch32", "ml_long", "int8_b64"])
+@pytest.mark.parametrize("name", ["tiny", "batch32", "ml_long", "int8_b64", "int6_b64", "int4_b64"])
 def test_canonical_names_cover_checkpoint(gg, name):
     cfg = synth.workload_config(name)
     ents = gg.canonical_entries(cfg)
     names = {n: s for n, s, _ in ents}
     want = {n: s for n, s, _ in synth.canonical_entries(cfg)}
-    if cfg["dtype"] == "w8f16":
+    if cfg["dtype"] in synth.QUANT_BITS:
         for n in list(want):
             base = n[: -len(".weight")]
             if n.endswith(".weight") and base.endswith(synth.QUANTIZED_SUFFIXES):
@@ -120,6 +120,42 @@ def test_pack_rounds_like_numpy(gg):
     with np.errstate(over="ignore"):
         want = np.transpose(w["pre.conv1.weight"], (0, 2, 1)).astype(np.float16)
     np.testing.assert_array_equal(got.view(np.uint16), want.view(np.uint16))
+
+
+@pytest.mark.parametrize("dtype,bits", [("w8f16", 8), ("w6f16", 6), ("w4f16", 4)])
+def test_pack_quantised_rows_bit_layout(gg, dtype, bits):
+    """Packed linear rows hold weight k at bits [k*b, k*b+b) of the row's little-endian bit
+    string (two's complement) with fp16 scales after them, as the header documents;
+    checked on layer 0's first FFN linear by unpacking with numpy."""
+    cfg = synth.model_config(1, 768, 16, 256, 5, 10, dtype)
+    w = synth.make_weights(cfg, 3)
+    packed = gg.pack_weights(cfg, w)
+    d, f = 768, 256
+    al = lambda x: (x + 255) // 256 * 256
+    off = 0
+    for nbytes in (d * 5 * 64 * 2, d * 4, d * 5 * d * 2, d * 4, d * 4, d * 4):
+        off = al(off + nbytes)                  # conv1 w/b, conv2 w/b, ff1 norm g/b
+    rowb = d * bits // 8
+    rows = packed[off: off + f * rowb].reshape(f, rowb)
+    bitsarr = np.unpackbits(rows, axis=1, bitorder="little")[:, : d * bits].reshape(f, d, bits)
+    u = (bitsarr.astype(np.int64) << np.arange(bits)).sum(axis=2)
+    q = np.where(u >= 1 << (bits - 1), u - (1 << bits), u)
+    np.testing.assert_array_equal(q, w["layers.0.ff1.linear1.weight_q"])
+    so = al(off + f * rowb)
+    sc = packed[so: so + f * (d // 64) * 2].view(np.float16).reshape(f, d // 64)
+    np.testing.assert_array_equal(sc, w["layers.0.ff1.linear1.weight_scale"])
+
+
+@pytest.mark.parametrize("dtype,bad", [("w6f16", 32.0), ("w4f16", 8.0), ("w4f16", -8.0),
+                                       ("w4f16", 2.5)])
+def test_pack_rejects_out_of_range_low_bit(gg, dtype, bad):
+    cfg = synth.model_config(1, 768, 16, 256, 5, 10, dtype)
+    w = synth.make_weights(cfg, 3)
+    gg.pack_weights(cfg, w)
+    q = w["layers.0.ff2.linear2.weight_q"].astype(np.float32).copy()
+    q[3, 5] = bad
+    with pytest.raises(gg.GigaamError):
+        gg.pack_weights(cfg, dict(w, **{"layers.0.ff2.linear2.weight_q": q}))
 
 
 def test_pack_rejects_bad_int8(gg):

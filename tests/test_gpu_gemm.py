@@ -11,6 +11,15 @@ SHAPES = [(1, 34, 64), (77, 200, 320), (300, 768, 768), (129, 1536, 256), (513, 
           (64, 64, 3840)]
 
 
+def _pack_rows(q, bits):
+    """The header's packed row layout, written independently with numpy: weight k at bits
+    [k*b, k*b+b) of the row's little-endian bit string, two's complement."""
+    N, K = q.shape
+    u = (q.astype(np.int64) & ((1 << bits) - 1))
+    bitsarr = ((u[:, :, None] >> np.arange(bits)) & 1).astype(np.uint8).reshape(N, K * bits)
+    return np.packbits(bitsarr, axis=1, bitorder="little")
+
+
 def _operands(dtype, M, N, K, seed):
     import torch
     rng = np.random.default_rng(seed)
@@ -29,11 +38,12 @@ def _operands(dtype, M, N, K, seed):
         w = synth.round_to_bf16(w)
         A, W = torch.from_numpy(a).bfloat16(), torch.from_numpy(w).bfloat16()
         w_eff = w.astype(np.float64)
-    else:  # int8 weights with one fp16 scale per 64 inputs, dequantised to fp16 in-kernel
+    else:  # b-bit weights with one fp16 scale per 64 inputs, dequantised to fp16 in-kernel
+        bits = synth.QUANT_BITS[dtype]
         A = torch.from_numpy(a).half()
         a = A.float().numpy()
-        q, s = synth.quantize_int8_g64(synth.round_to_f16(w))
-        W = torch.from_numpy(q)
+        q, s = synth.quantize_g64(synth.round_to_f16(w), bits)
+        W = torch.from_numpy(_pack_rows(q, bits))
         scale = torch.from_numpy(s)
         deq = q.astype(np.float32) * np.repeat(s.astype(np.float32), 64, axis=1)
         w_eff = deq.astype(np.float16).astype(np.float64)
@@ -41,12 +51,12 @@ def _operands(dtype, M, N, K, seed):
         torch.from_numpy(b).cuda(), a.astype(np.float64), w_eff, b.astype(np.float64)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "w8f16"])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "w8f16", "w6f16", "w4f16"])
 @pytest.mark.parametrize("M,N,K", SHAPES)
 def test_gemm_matches_float64(dtype, M, N, K):
     import conformer_speech_recognition_amd as gg
-    if dtype == "w8f16" and K % 64:
-        pytest.skip("int8 groups need K % 64 == 0")
+    if dtype in synth.QUANT_BITS and K % 64:
+        pytest.skip("quantisation groups need K % 64 == 0")
     print(f"[gemm] {dtype} M={M} N={N} K={K}", flush=True)
     A, W, S, bias, a, w, b = _operands(dtype, M, N, K, seed=M * 7 + N + K)
     C = gg.debug_gemm(dtype, A, W, bias=bias, scale=S).cpu().numpy().astype(np.float64)

@@ -4,7 +4,7 @@ sample of clips one by one (shortest, longest and one in between); every clip is
 checked for shape, padding and CTC-collapse consistency.
 
 Acceptance: encoder output and log-probs max|d| <= 5e-2 and >= 99.5% per-frame argmax
-agreement for the fp16 / bf16 / int8 paths, a disagreement counting as agreement only
+agreement for the fp16 / bf16 / int8 / int6 / int4 paths, a disagreement counting as agreement only
 where the oracle's log-prob of the GPU's pick is within twice the clip's log-prob
 deviation of its best (a near-tie both precisions resolve correctly); the raw agreement
 is reported and must stay >= 98%."""
@@ -24,6 +24,8 @@ CASES = {
     "batch32_bf16": None,
     "ml_long": [0],
     "int8_b64": [0, 63],
+    "int6_b64": [0, 63],
+    "int4_b64": [0, 63],
 }
 
 

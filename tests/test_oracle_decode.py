@@ -85,6 +85,32 @@ def test_int8_dequant_exact_idempotent_bounded():
     assert oracle.dequantize_int8_g64(q3, s3)[0, 64] == 3.0
 
 
+@pytest.mark.parametrize("bits", [6, 4])
+def test_low_bit_dequant_exact_bounded_and_in_range(bits):
+    """The INT6 / INT4 g64 variants: integers within +-(2^(b-1)-1), one fp16 scale per 64
+    weights, products exact in fp32, error at most half a step, fixed point under
+    re-quantisation, and a 2^(b-1)-1 multiple of the scale reaching the group's max."""
+    qmax = (1 << (bits - 1)) - 1
+    rng = np.random.default_rng(bits)
+    w = synth.round_to_f16(rng.normal(0, 0.02, (8, 192)))
+    q, s = synth.quantize_g64(w, bits)
+    assert q.dtype == np.int8 and np.abs(q).max() == qmax and s.shape == (8, 3)
+    deq = oracle.dequantize_g64(q, s)
+    assert np.array_equal(deq.astype(np.float32).astype(np.float64), deq)
+    step = np.repeat(s.astype(np.float64), 64, axis=1)
+    assert np.all(np.abs(deq - w) <= 0.5 * step + 1e-3 * np.abs(w) + 1e-12)
+    q2, s2 = synth.quantize_g64(deq, bits)
+    np.testing.assert_array_equal(oracle.dequantize_g64(q2, s2), deq)
+    # every group's largest |w| maps to +-qmax
+    g = np.abs(w).reshape(8, 3, 64)
+    qa = np.abs(q.astype(int)).reshape(8, 3, 64)
+    assert np.all(qa[np.arange(8)[:, None], np.arange(3)[None, :], g.argmax(axis=2)] == qmax)
+    # fewer bits never quantise more finely than more bits
+    q8, s8 = synth.quantize_g64(w, 8)
+    e8 = np.abs(oracle.dequantize_g64(q8, s8) - w).max()
+    assert np.abs(deq - w).max() >= e8
+
+
 # ------------------------------------------------------------------ whole forward
 
 def test_tiny_workload_shapes_and_fp32_self_bound():
