@@ -5,8 +5,9 @@
 // Mac", section "Where the time goes": the convolution module is ~17% of a block.
 //
 // Block = 64 frames x 64 channels of one clip. The (64 + K - 1) x 64 input window is
-// staged once in LDS (zeros outside the clip); each thread then slides its channel
-// over 16 consecutive frames with the whole window in registers.
+// staged once in LDS in the storage type (zeros outside the clip); each thread then
+// slides its channel over 16 consecutive frames with the whole window in fp32
+// registers. The taps are stored tap-major so a wave's lanes read consecutive channels.
 #include "kernels.h"
 
 namespace gg {
@@ -14,38 +15,38 @@ namespace gg {
 template <typename T, int K>
 __global__ void __launch_bounds__(256) k_dw(DwParams p) {
   constexpr int TT = 64, CH = 64, HALF = (K - 1) / 2, R = TT + K - 1, TPT = 16;
-  __shared__ float sx[R][CH + 1];
+  // the window is staged in the storage type (12 KiB for 16-bit types: 8 blocks per CU)
+  __shared__ __attribute__((aligned(16))) T sx[R][CH + 16 / sizeof(T)];
   const int tid = threadIdx.x;
   const int tile = blockIdx.x, c0 = blockIdx.y * CH;
   const int b = p.tileQ[tile];
   const int base = p.cuU[b], U = p.cuU[b + 1] - base;
   const int t0 = (tile - p.cuQ[b]) * TT;
 
-  typedef T t8 __attribute__((ext_vector_type(8)));
-  for (int e = tid; e < R * (CH / 8); e += 256) {
-    const int row = e / (CH / 8), c8 = e - row * (CH / 8);
-    const int t = t0 - HALF + row;
-    float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (t >= 0 && t < U) {
-      const t8 x = *(const t8*)((const T*)p.in + (long)(base + t) * p.d + c0 + c8 * 8);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = (float)x[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) sx[row][c8 * 8 + i] = v[i];
-  }
-  __syncthreads();
-
+  // per-channel taps and folded BatchNorm first, so their loads overlap the staging
   const int c = tid & 63, tg = tid >> 6;
   const int ch = c0 + c;
   float w[K];
 #pragma unroll
-  for (int j = 0; j < K; ++j) w[j] = p.w[(long)ch * K + j];
-  float win[TPT + K - 1];
-#pragma unroll
-  for (int i = 0; i < TPT + K - 1; ++i) win[i] = sx[tg * TPT + i][c];
+  for (int j = 0; j < K; ++j) w[j] = p.w[(long)j * p.d + ch];
   const float alpha = p.bn_g[ch] / sqrtf(p.bn_v[ch] + p.eps);
   const float beta = p.bn_b[ch] + (p.b[ch] - p.bn_m[ch]) * alpha;
+
+  typedef T t8 __attribute__((ext_vector_type(8)));
+  for (int e = tid; e < R * (CH / 8); e += 256) {
+    const int row = e / (CH / 8), c8 = e - row * (CH / 8);
+    const int t = t0 - HALF + row;
+    t8 x;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = (T)0.0f;
+    if (t >= 0 && t < U) x = *(const t8*)((const T*)p.in + (long)(base + t) * p.d + c0 + c8 * 8);
+    *(t8*)&sx[row][c8 * 8] = x;
+  }
+  __syncthreads();
+
+  float win[TPT + K - 1];
+#pragma unroll
+  for (int i = 0; i < TPT + K - 1; ++i) win[i] = (float)sx[tg * TPT + i][c];
 #pragma unroll
   for (int i = 0; i < TPT; ++i) {
     const int t = t0 + tg * TPT + i;

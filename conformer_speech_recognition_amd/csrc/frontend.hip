@@ -4,14 +4,19 @@
 // power 2.0; "GigaAM v3 RNNT - MLX" card, "Notes for other runtimes": the window and
 // filterbank are stored model buffers and the features are log(clip(x, 1e-9, 1e9)).
 //
-// One block turns 32 frames into 32 x 64 log-mel values entirely on chip:
-//   framing + window (LDS) -> 161-bin DFT power (fp32, twiddles from an fp64 table in
-//   LDS, 3 bins x 8 frames per thread) -> mel projection -> log-clip -> one store.
+// One block turns FE_FT frames into FE_FT x 64 log-mel values entirely on chip. The
+// 320-point DFT of each windowed frame is factored as 320 = 16 x 20 (Cooley-Tukey with
+// n = 20 n1 + n2, k = k1 + 16 k2):
+//   Y[n2][k1] = sum_{n1<16} x[20 n1 + n2] W16^(n1 k1)           (16-point DFTs)
+//   Z[n2][k1] = Y[n2][k1] W320^(n2 k1)                           (twiddle)
+//   X[k1 + 16 k2] = sum_{n2<20} Z[n2][k1] W20^(n2 k2)            (20-point DFTs)
+// evaluated in fp32 with twiddles rounded from fp64, for bins k <= 160 only; then
+// power, mel projection and log-clip. The small DFTs keep their twiddles in registers.
 #include "kernels.h"
 
 namespace gg {
 
-constexpr int FE_FT = 32;     // frames per block
+constexpr int FE_FT = 12;     // frames per block
 constexpr int FE_N = 320;     // FFT size = window length
 constexpr int FE_K = 161;     // power bins 0..160
 constexpr int FE_M = 64;      // mel bins
@@ -21,16 +26,17 @@ __global__ void __launch_bounds__(256) k_frontend(const float* __restrict__ pcm,
                                                   const float* __restrict__ fb, MetaDev m,
                                                   int T_tot, float* __restrict__ mel) {
   __shared__ float xw[FE_FT][FE_N];
-  __shared__ float tc[FE_N], ts[FE_N];
-  __shared__ float P[FE_FT][FE_K];
+  __shared__ float tc[FE_N], ts[FE_N];           // W320^j = tc[j] - i ts[j]
+  __shared__ float zr[FE_FT][20][17], zi[FE_FT][20][17];
+  __shared__ float P[FE_FT][FE_K + 3];
   const int tid = threadIdx.x;
   const int f0 = blockIdx.x * FE_FT;
 
   for (int i = tid; i < FE_N; i += 256) {
-    double s, c;
-    sincospi(2.0 * i / FE_N, &s, &c);
-    tc[i] = (float)c;
-    ts[i] = (float)s;
+    double sn, cs;
+    sincospi(2.0 * i / FE_N, &sn, &cs);
+    tc[i] = (float)cs;
+    ts[i] = (float)sn;
   }
   for (int e = tid; e < FE_FT * FE_N; e += 256) {
     const int f = e / FE_N, n = e - f * FE_N, g = f0 + f;
@@ -44,52 +50,60 @@ __global__ void __launch_bounds__(256) k_frontend(const float* __restrict__ pcm,
   }
   __syncthreads();
 
-  // power spectrum: lane kl handles bins kl, kl + 64, kl + 128; wave fg frames 8fg..8fg+7
-  const int kl = tid & 63, fg = tid >> 6;
-  float re[3][8], im[3][8];
+  // stage 1: thread (f, n2) -> 16-point DFT over n1, then the W320^(n2 k1) twiddle
+  if (tid < FE_FT * 20) {
+    const int f = tid / 20, n2 = tid - f * 20;
+    float x[16];
 #pragma unroll
-  for (int j = 0; j < 3; ++j)
+    for (int n1 = 0; n1 < 16; ++n1) x[n1] = xw[f][20 * n1 + n2];
 #pragma unroll
-    for (int f = 0; f < 8; ++f) re[j][f] = im[j][f] = 0.f;
-  int idx[3] = {0, 0, 0};
-  const int kk[3] = {kl, kl + 64, kl + 128};
-  for (int n = 0; n < FE_N; ++n) {
-    float xv[8];
+    for (int k1 = 0; k1 < 16; ++k1) {
+      float yr = 0.f, yi = 0.f;
 #pragma unroll
-    for (int f = 0; f < 8; ++f) xv[f] = xw[fg * 8 + f][n];
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      const float c = tc[idx[j]], s = ts[idx[j]];
-#pragma unroll
-      for (int f = 0; f < 8; ++f) {
-        re[j][f] = fmaf(xv[f], c, re[j][f]);
-        im[j][f] = fmaf(-xv[f], s, im[j][f]);
+      for (int n1 = 0; n1 < 16; ++n1) {
+        const int j = 20 * ((n1 * k1) & 15);      // W16^(n1 k1) = W320^(20 (n1 k1 mod 16))
+        yr = fmaf(x[n1], tc[j], yr);
+        yi = fmaf(-x[n1], ts[j], yi);
       }
-      idx[j] += kk[j];
-      if (idx[j] >= FE_N) idx[j] -= FE_N;
+      const int j = (n2 * k1) % FE_N;
+      const float c = tc[j], sn = ts[j];           // (yr + i yi)(c - i sn)
+      zr[f][n2][k1] = yr * c + yi * sn;
+      zi[f][n2][k1] = yi * c - yr * sn;
     }
   }
-#pragma unroll
-  for (int j = 0; j < 3; ++j)
-    if (kk[j] < FE_K)
-#pragma unroll
-      for (int f = 0; f < 8; ++f) P[fg * 8 + f][kk[j]] = re[j][f] * re[j][f] + im[j][f] * im[j][f];
   __syncthreads();
 
-  // mel projection + log clip: lane = mel bin, wave fg = frames 8fg..8fg+7
-  const int mm = tid & 63;
-  float acc[8];
+  // stage 2: thread (f, k1) -> 20-point DFT over n2 for k2 = 0..10, power of bins <= 160
+  if (tid < FE_FT * 16) {
+    const int f = tid >> 4, k1 = tid & 15;
+    float ar[20], ai[20];
 #pragma unroll
-  for (int f = 0; f < 8; ++f) acc[f] = 0.f;
-  for (int k = 0; k < FE_K; ++k) {
-    const float w = fb[k * FE_M + mm];
+    for (int n2 = 0; n2 < 20; ++n2) { ar[n2] = zr[f][n2][k1]; ai[n2] = zi[f][n2][k1]; }
 #pragma unroll
-    for (int f = 0; f < 8; ++f) acc[f] = fmaf(w, P[fg * 8 + f][k], acc[f]);
+    for (int k2 = 0; k2 <= 10; ++k2) {
+      const int k = k1 + 16 * k2;
+      if (k < FE_K) {
+        float xr = 0.f, xi = 0.f;
+#pragma unroll
+        for (int n2 = 0; n2 < 20; ++n2) {
+          const int j = 16 * ((n2 * k2) % 20);    // W20^(n2 k2) = W320^(16 (n2 k2 mod 20))
+          const float c = tc[j], sn = ts[j];
+          xr = fmaf(ar[n2], c, fmaf(ai[n2], sn, xr));
+          xi = fmaf(ai[n2], c, fmaf(-ar[n2], sn, xi));
+        }
+        P[f][k] = xr * xr + xi * xi;
+      }
+    }
   }
-#pragma unroll
-  for (int f = 0; f < 8; ++f) {
-    const int g = f0 + fg * 8 + f;
-    if (g < T_tot) mel[(long)g * FE_M + mm] = logf(fminf(fmaxf(acc[f], 1e-9f), 1e9f));
+  __syncthreads();
+
+  // mel projection + log clip: thread (f, m)
+  for (int e = tid; e < FE_FT * FE_M; e += 256) {
+    const int f = e >> 6, mm = e & 63;
+    float acc = 0.f;
+    for (int k = 0; k < FE_K; ++k) acc = fmaf(fb[k * FE_M + mm], P[f][k], acc);
+    const int g = f0 + f;
+    if (g < T_tot) mel[(long)g * FE_M + mm] = logf(fminf(fmaxf(acc, 1e-9f), 1e9f));
   }
 }
 

@@ -475,7 +475,12 @@ extern "C" int gigaam_pack_weights(const gigaam_config* cfg, const float* canoni
       }
       P.linear(o.pw1, {p + "conv.pointwise1"}, d, rm);
     }
-    P.copy_f(o.dw_w, p + "conv.depthwise.weight", d * c.conv_kernel);
+    {   // depthwise taps tap-major [K][d]: a wave's lanes read consecutive channels
+      const float* w = P.get(p + "conv.depthwise.weight");
+      const int K = c.conv_kernel;
+      for (int ch = 0; ch < d; ++ch)
+        for (int j = 0; j < K; ++j) P.put_f(o.dw_w, (size_t)j * d + ch, w[(size_t)ch * K + j]);
+    }
     P.copy_f(o.dw_b, p + "conv.depthwise.bias", d);
     P.copy_f(o.bn_g, p + "conv.bn.weight", d); P.copy_f(o.bn_b, p + "conv.bn.bias", d);
     P.copy_f(o.bn_m, p + "conv.bn.running_mean", d); P.copy_f(o.bn_v, p + "conv.bn.running_var", d);

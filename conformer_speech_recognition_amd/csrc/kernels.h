@@ -81,7 +81,7 @@ hipError_t launch_attention(DType dt, int dk, const AttnParams& p, hipStream_t s
 // ---- conv module: depthwise + BatchNorm + SiLU --------------------------------------
 struct DwParams {
   const void* in; void* out;       // T [rows][d]
-  const float* w; const float* b;  // [d][K], [d]
+  const float* w; const float* b;  // taps [K][d] (tap-major), bias [d]
   const float* bn_g; const float* bn_b; const float* bn_m; const float* bn_v;
   int d, n_tiles;
   const int* cuU; const int* cuQ; const int* tileQ;

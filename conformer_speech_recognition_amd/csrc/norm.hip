@@ -6,8 +6,10 @@
 //              model was broken", Trap 2)
 //   LN_TWO   : x <- LN_out(x) in place (fp32), then y = LN_next(x) -> T (block's final
 //              norm fused with the next block's first pre-norm)
-// Lane l holds the d/64 contiguous features [l*EPL, (l+1)*EPL); with 16 heads a head is
-// 4 lanes, so rotate_half's partner (i +- d_k/2) lives in lane l ^ 2.
+// Lane l holds features 256 i + 4 l + q (i < d / 256, q < 4), so every load and store
+// instruction of a wave covers one contiguous 1 KiB (fp32) or 512 B (16-bit) span.
+// rotate_half's partner (the feature d_k / 2 away inside the same head) is read back
+// from the wave's own copy of the normed row in LDS.
 #include "kernels.h"
 
 namespace gg {
@@ -27,85 +29,100 @@ template <> __device__ __forceinline__ void store4<bf16>(bf16* dst, float a, flo
   *(bf16x4*)dst = bf16x4{(bf16)a, (bf16)b, (bf16)c, (bf16)d};
 }
 
-template <int EPL>
-__device__ __forceinline__ void ln_row(float (&v)[EPL], const float* g, const float* b, int lane,
+// v[4 i + q] = feature 256 i + 4 lane + q
+template <int NI>
+__device__ __forceinline__ void ln_row(float (&v)[4 * NI], const float* g, const float* b, int lane,
                                        float eps) {
-  constexpr int D = EPL * 64;
+  constexpr int D = NI * 256;
   float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) s += v[i];
+  for (int e = 0; e < 4 * NI; ++e) s += v[e];
   const float mean = wave_sum(s) * (1.0f / D);
   float ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    v[i] -= mean;
-    ss += v[i] * v[i];
+  for (int e = 0; e < 4 * NI; ++e) {
+    v[e] -= mean;
+    ss += v[e] * v[e];
   }
   const float rstd = 1.0f / sqrtf(wave_sum(ss) * (1.0f / D) + eps);
 #pragma unroll
-  for (int i = 0; i < EPL; i += 4) {
-    const f32x4 gg4 = *(const f32x4*)(g + lane * EPL + i);
-    const f32x4 bb4 = *(const f32x4*)(b + lane * EPL + i);
+  for (int i = 0; i < NI; ++i) {
+    const f32x4 gg4 = *(const f32x4*)(g + 256 * i + 4 * lane);
+    const f32x4 bb4 = *(const f32x4*)(b + 256 * i + 4 * lane);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) v[i + j] = v[i + j] * rstd * gg4[j] + bb4[j];
+    for (int q = 0; q < 4; ++q) v[4 * i + q] = v[4 * i + q] * rstd * gg4[q] + bb4[q];
   }
 }
 
-template <typename T, int EPL, int MODE>
+template <typename T, int NI, int MODE>
 __global__ void __launch_bounds__(256) k_ln(LnParams p) {
-  constexpr int D = EPL * 64;
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  constexpr int D = NI * 256;
+  __shared__ float srow[MODE == LN_ROPE ? 4 : 1][MODE == LN_ROPE ? D + D / 16 : 1];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int row = blockIdx.x * 4 + wv;
   if (row >= p.rows) return;
-  float v[EPL];
-  float* xr = p.x + (long)row * D + lane * EPL;
+  float v[4 * NI];
+  float* xr = p.x + (long)row * D + 4 * lane;
 #pragma unroll
-  for (int i = 0; i < EPL; i += 4) {
-    const f32x4 q = *(const f32x4*)(xr + i);
+  for (int i = 0; i < NI; ++i) {
+    const f32x4 q = *(const f32x4*)(xr + 256 * i);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) v[i + j] = q[j];
+    for (int j = 0; j < 4; ++j) v[4 * i + j] = q[j];
   }
-  ln_row<EPL>(v, p.g1, p.b1, lane, p.eps);
-  T* yr = (T*)p.y + (long)row * D + lane * EPL;
+  ln_row<NI>(v, p.g1, p.b1, lane, p.eps);
+  T* yr = (T*)p.y + (long)row * D + 4 * lane;
   if constexpr (MODE == LN_TWO) {
 #pragma unroll
-    for (int i = 0; i < EPL; i += 4) *(f32x4*)(xr + i) = f32x4{v[i], v[i + 1], v[i + 2], v[i + 3]};
+    for (int i = 0; i < NI; ++i)
+      *(f32x4*)(xr + 256 * i) = f32x4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
     if (p.g2 == nullptr) {          // last block: x only (optionally a T copy)
       if (p.y != nullptr)
 #pragma unroll
-        for (int i = 0; i < EPL; i += 4) store4<T>(yr + i, v[i], v[i + 1], v[i + 2], v[i + 3]);
+        for (int i = 0; i < NI; ++i)
+          store4<T>(yr + 256 * i, v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
       return;
     }
-    ln_row<EPL>(v, p.g2, p.b2, lane, p.eps);
+    ln_row<NI>(v, p.g2, p.b2, lane, p.eps);
   }
 #pragma unroll
-  for (int i = 0; i < EPL; i += 4) store4<T>(yr + i, v[i], v[i + 1], v[i + 2], v[i + 3]);
+  for (int i = 0; i < NI; ++i) store4<T>(yr + 256 * i, v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
   if constexpr (MODE == LN_ROPE) {
-    constexpr int HALF = 2 * EPL;           // d_k / 2
+    constexpr int DK = D / 16, HALF = DK / 2;      // 16 heads
+    float* sr = srow[wv];
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      *(f32x4*)(sr + 256 * i + 4 * lane) = f32x4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+    // this frame's cos / sin rows next to the normed row (one coalesced load each)
     const int b = p.rowclip[row];
     const int t = row - p.cu[b];
-    const float* cr = p.cos_t + (long)t * HALF + (lane & 1) * EPL;
-    const float* sr = p.sin_t + (long)t * HALF + (lane & 1) * EPL;
-    const float sgn = (lane & 2) ? 1.0f : -1.0f;
-    float r[EPL];
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const float partner = __shfl_xor(v[i], 2, 64);
-      r[i] = v[i] * cr[i] + sgn * partner * sr[i];
+    float* cs = sr + D;
+    if (lane < HALF) {
+      cs[lane] = p.cos_t[(long)t * HALF + lane];
+      cs[HALF + lane] = p.sin_t[(long)t * HALF + lane];
     }
-    T* rr = (T*)p.r + (long)row * D + lane * EPL;
+    float r[4 * NI];
 #pragma unroll
-    for (int i = 0; i < EPL; i += 4) store4<T>(rr + i, r[i], r[i + 1], r[i + 2], r[i + 3]);
+    for (int e = 0; e < 4 * NI; ++e) {
+      const int j = 256 * (e >> 2) + 4 * lane + (e & 3);     // feature index
+      const int pos = j % DK;                                // position inside the head
+      const bool lo = pos < HALF;
+      const int i2 = lo ? pos : pos - HALF;
+      const float partner = sr[lo ? j + HALF : j - HALF];
+      r[e] = v[e] * cs[i2] + (lo ? -partner : partner) * cs[HALF + i2];
+    }
+    T* rr = (T*)p.r + (long)row * D + 4 * lane;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) store4<T>(rr + 256 * i, r[4 * i], r[4 * i + 1], r[4 * i + 2], r[4 * i + 3]);
   }
 }
 
-template <typename T, int EPL>
+template <typename T, int NI>
 static hipError_t ln_modes(LnMode mode, const LnParams& p, hipStream_t s) {
   dim3 grid((p.rows + 3) / 4);
   switch (mode) {
-    case LN_PLAIN: hipLaunchKernelGGL((k_ln<T, EPL, LN_PLAIN>), grid, dim3(256), 0, s, p); break;
-    case LN_ROPE: hipLaunchKernelGGL((k_ln<T, EPL, LN_ROPE>), grid, dim3(256), 0, s, p); break;
-    case LN_TWO: hipLaunchKernelGGL((k_ln<T, EPL, LN_TWO>), grid, dim3(256), 0, s, p); break;
+    case LN_PLAIN: hipLaunchKernelGGL((k_ln<T, NI, LN_PLAIN>), grid, dim3(256), 0, s, p); break;
+    case LN_ROPE: hipLaunchKernelGGL((k_ln<T, NI, LN_ROPE>), grid, dim3(256), 0, s, p); break;
+    case LN_TWO: hipLaunchKernelGGL((k_ln<T, NI, LN_TWO>), grid, dim3(256), 0, s, p); break;
   }
   return hipGetLastError();
 }
@@ -113,8 +130,8 @@ static hipError_t ln_modes(LnMode mode, const LnParams& p, hipStream_t s) {
 template <typename T>
 static hipError_t ln_widths(LnMode mode, const LnParams& p, hipStream_t s) {
   switch (p.d) {
-    case 768: return ln_modes<T, 12>(mode, p, s);
-    case 1024: return ln_modes<T, 16>(mode, p, s);
+    case 768: return ln_modes<T, 3>(mode, p, s);
+    case 1024: return ln_modes<T, 4>(mode, p, s);
   }
   return hipErrorInvalidValue;
 }
