@@ -44,6 +44,21 @@ class Config(ctypes.Structure):
                [(n, ctypes.c_float) for n in ("rope_base", "ln_eps", "bn_eps")]
 
 
+class RnntConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("d_model", "n_classes", "pred_hidden", "joint_hidden", "max_symbols", "dtype")]
+
+
+def make_rnnt_config(cfg: dict) -> RnntConfig:
+    c = RnntConfig()
+    for name, _ in RnntConfig._fields_:
+        v = cfg[name]
+        if name == "dtype":
+            v = DTYPES[v] if isinstance(v, str) else int(v)
+        setattr(c, name, v)
+    return c
+
+
 def make_config(cfg: dict) -> Config:
     c = Config()
     for name, _ in Config._fields_:
@@ -78,6 +93,16 @@ _SIGNATURES = {
     "gigaam_encode_stage": (ctypes.c_int, [_P, _P, _IP, _I, _I, _P, _SZ, _I, _P, _SZ, _P]),
     "gigaam_debug_gemm": (ctypes.c_int, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
     "gigaam_debug_attention": (ctypes.c_int, [_I, _I, _I, _I, _IP, _P, _P, _P, _SZ, _P]),
+    "gigaam_rnnt_check_config": (ctypes.c_int, [ctypes.POINTER(RnntConfig)]),
+    "gigaam_rnnt_canonical_count": (ctypes.c_int, [ctypes.POINTER(RnntConfig), _IP, ctypes.POINTER(_SZ)]),
+    "gigaam_rnnt_canonical_entry": (ctypes.c_int, [ctypes.POINTER(RnntConfig), _I, ctypes.c_char_p, _I,
+                                                   _IP, _IP, ctypes.POINTER(_SZ)]),
+    "gigaam_rnnt_packed_bytes": (ctypes.c_int, [ctypes.POINTER(RnntConfig), ctypes.POINTER(_SZ)]),
+    "gigaam_rnnt_pack_weights": (ctypes.c_int, [ctypes.POINTER(RnntConfig), _P, _SZ, _P, _SZ]),
+    "gigaam_rnnt_create": (ctypes.c_int, [ctypes.POINTER(RnntConfig), _P, ctypes.POINTER(_P)]),
+    "gigaam_rnnt_destroy": (None, [_P]),
+    "gigaam_rnnt_workspace_bytes": (ctypes.c_int, [_P, _I, _I, ctypes.POINTER(_SZ)]),
+    "gigaam_rnnt_decode": (ctypes.c_int, [_P, _P, _I, _IP, _I, _P, _SZ, _P, _P, _P, _I, _P]),
     "gigaam_profile_start": (ctypes.c_int, []),
     "gigaam_profile_stop": (ctypes.c_int, []),
     "gigaam_profile_report": (ctypes.c_int, [ctypes.c_char_p, _SZ]),
@@ -313,3 +338,91 @@ def debug_attention(dtype: str, qkv, frames, n_heads: int = 16, stream=None):
     _check(lib().gigaam_debug_attention(DTYPES[dtype], d, n_heads, len(fr), fr.ctypes.data_as(_IP),
                                         qkv.data_ptr(), out.data_ptr(), ws.data_ptr(), nb, s))
     return out
+
+
+# ------------------------------------------------------------------------------ RNNT head
+
+def rnnt_canonical_entries(cfg: dict) -> list[tuple[str, tuple[int, ...], int]]:
+    L = lib(False)
+    c = make_rnnt_config(cfg)
+    n, nf = _I(), _SZ()
+    _check(L.gigaam_rnnt_canonical_count(ctypes.byref(c), ctypes.byref(n), ctypes.byref(nf)))
+    out = []
+    buf = ctypes.create_string_buffer(256)
+    rank, shape, off = _I(), (_I * 3)(), _SZ()
+    for i in range(n.value):
+        _check(L.gigaam_rnnt_canonical_entry(ctypes.byref(c), i, buf, 256, ctypes.byref(rank), shape,
+                                             ctypes.byref(off)))
+        out.append((buf.value.decode(), tuple(shape[j] for j in range(rank.value)), off.value))
+    return out
+
+
+def rnnt_pack_weights(cfg: dict, weights: dict) -> np.ndarray:
+    L = lib(False)
+    c = make_rnnt_config(cfg)
+    ents = rnnt_canonical_entries(cfg)
+    total = ents[-1][2] + int(np.prod(ents[-1][1]))
+    canon = np.empty(total, dtype=np.float32)
+    for name, shape, off in ents:
+        a = np.asarray(weights[name])
+        if a.shape != shape:
+            raise ValueError(f"{name}: shape {a.shape}, expected {shape}")
+        canon[off: off + a.size] = a.astype(np.float32).ravel()
+    nb = _SZ()
+    _check(L.gigaam_rnnt_packed_bytes(ctypes.byref(c), ctypes.byref(nb)))
+    out = np.empty(nb.value, dtype=np.uint8)
+    _check(L.gigaam_rnnt_pack_weights(ctypes.byref(c), canon.ctypes.data, canon.size,
+                                      out.ctypes.data, out.size))
+    return out
+
+
+class RnntHead:
+    """The RNNT head (prediction network, joint, greedy decoding) on one GPU; decodes
+    the ``enc_out`` that Model.encode returns."""
+
+    def __init__(self, cfg: dict, weights: dict, device="cuda"):
+        import torch
+        L = lib()
+        self.cfg = dict(cfg)
+        self.device = torch.device(device)
+        self._c = make_rnnt_config(cfg)
+        self.packed = torch.from_numpy(rnnt_pack_weights(cfg, weights)).to(self.device)
+        h = _P()
+        _check(L.gigaam_rnnt_create(ctypes.byref(self._c), self.packed.data_ptr(), ctypes.byref(h)))
+        self._h = h
+        self._ws = None
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().gigaam_rnnt_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def decode(self, enc, n_frames, stream=None) -> dict:
+        """enc: float32 CUDA tensor [B, U_max, d]; n_frames: frames per clip (host).
+        Returns tokens [B, U_max * max_symbols] (-1 padded), token_frames (same shape)
+        and n_tokens [B] as device tensors."""
+        import torch
+        if not (enc.is_cuda and enc.dtype == torch.float32 and enc.dim() == 3 and enc.is_contiguous()):
+            raise ValueError("enc must be a contiguous float32 CUDA tensor [B, U_max, d]")
+        B, stride, _ = enc.shape
+        fr = np.ascontiguousarray(np.asarray(n_frames, dtype=np.int32))
+        max_tokens = stride * self.cfg["max_symbols"]
+        nb = _SZ()
+        _check(lib().gigaam_rnnt_workspace_bytes(self._h, B, stride, ctypes.byref(nb)))
+        if self._ws is None or self._ws.numel() < nb.value:
+            self._ws = torch.empty(nb.value, dtype=torch.uint8, device=self.device)
+        out = dict(tokens=torch.empty(B, max_tokens, dtype=torch.int32, device=self.device),
+                   token_frames=torch.empty(B, max_tokens, dtype=torch.int32, device=self.device),
+                   n_tokens=torch.empty(B, dtype=torch.int32, device=self.device))
+        s = (stream or torch.cuda.current_stream(self.device)).cuda_stream
+        _check(lib().gigaam_rnnt_decode(self._h, enc.data_ptr(), stride, fr.ctypes.data_as(_IP), B,
+                                        self._ws.data_ptr(), self._ws.numel(),
+                                        out["tokens"].data_ptr(), out["token_frames"].data_ptr(),
+                                        out["n_tokens"].data_ptr(), max_tokens, s))
+        return out

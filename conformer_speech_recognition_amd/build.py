@@ -17,8 +17,8 @@ LIB = os.path.join(HERE, "libgigaam.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["gigaam.cpp", "meta.hip", "frontend.hip", "gemm.hip", "norm.hip", "attention.hip",
-           "dwconv.hip", "ctc.hip"]
+SOURCES = ["gigaam.cpp", "rnnt_api.cpp", "meta.hip", "frontend.hip", "gemm.hip", "norm.hip",
+           "attention.hip", "dwconv.hip", "ctc.hip", "rnnt.hip"]
 
 CFLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-x", "hip",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC,

@@ -616,10 +616,11 @@ static hipError_t run_tiles(AMode am, Epi ep, const GemmParams& p, hipStream_t s
   return run_epi<T, 128, 128, 2, 2, QB>(am, ep, p, s);
 }
 
-// Direct-load pipeline for fp16/bf16 operands already in T (plain or dual A). Two shapes,
-// both 8 waves of 64x64 accumulators, picked by N (measured on the encoder's GEMMs):
-//   N > 1024: 256 x 128 tile, 3 stages of 32 k-elements (72 KiB LDS, 2 blocks per CU)
-//   else    : 128 x 256 tile, 2 stages of 64 k-elements (96 KiB LDS)
+// Direct-load pipeline for fp16/bf16 operands already in T (plain or dual A). Three
+// shapes of 8 waves, picked by N and K (measured on the encoder's GEMMs):
+//   N > 1024          : 256 x 128 tile, 64x64 per wave, 3 stages of 32 k (72 KiB LDS)
+//   N <= 1024, K <= 1024: 128 x 128 tile, 32x64 per wave, 3 stages of 32 k (48 KiB LDS)
+//   else              : 128 x 256 tile, 64x64 per wave, 2 stages of 64 k (96 KiB LDS)
 template <typename T, int BM, int BN, int WGM, int WGN, int S, int KB>
 static hipError_t run_dl(AMode am, Epi ep, const GemmParams& p, hipStream_t s) {
   dim3 grid(((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN)), blk(64 * WGM * WGN);
@@ -637,6 +638,8 @@ static hipError_t run_dl(AMode am, Epi ep, const GemmParams& p, hipStream_t s) {
 template <typename T>
 static hipError_t run_dl_shape(AMode am, Epi ep, const GemmParams& p, hipStream_t s) {
   if (p.N > 1024) return run_dl<T, 256, 128, 4, 2, 3, 32>(am, ep, p, s);
+  // narrow and short (the d x d projections): smaller tiles, twice as many blocks
+  if (p.K <= 1024) return run_dl<T, 128, 128, 4, 2, 3, 32>(am, ep, p, s);
   return run_dl<T, 128, 256, 2, 4, 2, 64>(am, ep, p, s);
 }
 

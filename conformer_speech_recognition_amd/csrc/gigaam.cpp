@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "gigaam.h"
+#include "host.h"
 #include "kernels.h"
 
 using namespace gg;
@@ -18,7 +19,7 @@ using namespace gg;
 // --------------------------------------------------------------------------- errors
 static thread_local std::string g_err;
 
-static int fail(int code, const char* fmt, ...) {
+int gg::fail(int code, const char* fmt, ...) {
   char buf[512];
   va_list ap;
   va_start(ap, fmt);
@@ -27,13 +28,6 @@ static int fail(int code, const char* fmt, ...) {
   g_err = buf;
   return code;
 }
-
-#define HIP_TRY(expr)                                                                   \
-  do {                                                                                  \
-    hipError_t e_ = (expr);                                                             \
-    if (e_ != hipSuccess)                                                               \
-      return fail(GIGAAM_E_HIP, "%s failed: %s", #expr, hipGetErrorString(e_));       \
-  } while (0)
 
 // --------------------------------------------------------------------------- profiler
 // Diagnostics only: when on, every launch of an encode is bracketed by HIP events on the
@@ -113,6 +107,39 @@ extern "C" int gigaam_profile_report(char* buf, size_t cap) {
 
 extern "C" int32_t gigaam_version(void) { return 100; }
 extern "C" const char* gigaam_last_error(void) { return g_err.c_str(); }
+
+// --------------------------------------------------------------------------- casts
+// Round-to-nearest-even fp32 -> fp16 / bf16 bit patterns (host packing).
+uint16_t gg::f32_to_f16_bits(float v) {
+  uint32_t x;
+  std::memcpy(&x, &v, 4);
+  const uint32_t sign = (x >> 16) & 0x8000u;
+  const uint32_t ax = x & 0x7fffffffu;
+  if (ax >= 0x7f800000u) return (uint16_t)(sign | 0x7c00u | (ax > 0x7f800000u ? 0x200u : 0u));
+  if (ax >= 0x477ff000u) return (uint16_t)(sign | 0x7c00u);          // rounds to >= 65520
+  if (ax < 0x38800000u) {                                             // fp16 subnormal or 0
+    if (ax < 0x33000000u) return (uint16_t)sign;                      // < 2^-25: rounds to 0
+    const uint32_t mant = (ax & 0x7fffffu) | 0x800000u;
+    const int e = (int)(ax >> 23);                                    // 102..112
+    const int shift = 126 - e;                                        // 14..24
+    uint32_t r = mant >> shift;
+    const uint32_t rem = mant & ((1u << shift) - 1u), halfway = 1u << (shift - 1);
+    if (rem > halfway || (rem == halfway && (r & 1u))) ++r;
+    return (uint16_t)(sign | r);
+  }
+  uint32_t r = ((ax >> 13) - (112u << 10));
+  const uint32_t rem = ax & 0x1fffu;
+  if (rem > 0x1000u || (rem == 0x1000u && (r & 1u))) ++r;
+  return (uint16_t)(sign | r);
+}
+
+uint16_t gg::f32_to_bf16_bits(float v) {
+  uint32_t x;
+  std::memcpy(&x, &v, 4);
+  if ((x & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((x >> 16) | 0x40u);
+  x += 0x7fffu + ((x >> 16) & 1u);
+  return (uint16_t)(x >> 16);
+}
 
 // --------------------------------------------------------------------------- frames
 static void frame_counts(int n, int& T, int& S, int& U) {
@@ -292,36 +319,6 @@ Layout layout(const gigaam_config& c) {
 }
 
 // ---- host conversions (round to nearest even)
-uint16_t f32_to_f16_bits(float v) {
-  uint32_t x;
-  std::memcpy(&x, &v, 4);
-  const uint32_t sign = (x >> 16) & 0x8000u;
-  const uint32_t ax = x & 0x7fffffffu;
-  if (ax >= 0x7f800000u) return (uint16_t)(sign | 0x7c00u | (ax > 0x7f800000u ? 0x200u : 0u));
-  if (ax >= 0x477ff000u) return (uint16_t)(sign | 0x7c00u);          // rounds to >= 65520
-  if (ax < 0x38800000u) {                                             // fp16 subnormal or 0
-    if (ax < 0x33000000u) return (uint16_t)sign;                      // < 2^-25: rounds to 0
-    const uint32_t mant = (ax & 0x7fffffu) | 0x800000u;
-    const int e = (int)(ax >> 23);                                    // 102..112
-    const int shift = 126 - e;                                        // 14..24
-    uint32_t r = mant >> shift;
-    const uint32_t rem = mant & ((1u << shift) - 1u), halfway = 1u << (shift - 1);
-    if (rem > halfway || (rem == halfway && (r & 1u))) ++r;
-    return (uint16_t)(sign | r);
-  }
-  uint32_t r = ((ax >> 13) - (112u << 10));
-  const uint32_t rem = ax & 0x1fffu;
-  if (rem > 0x1000u || (rem == 0x1000u && (r & 1u))) ++r;
-  return (uint16_t)(sign | r);
-}
-
-uint16_t f32_to_bf16_bits(float v) {
-  uint32_t x;
-  std::memcpy(&x, &v, 4);
-  if ((x & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((x >> 16) | 0x40u);
-  x += 0x7fffu + ((x >> 16) & 1u);
-  return (uint16_t)(x >> 16);
-}
 
 struct Packer {
   const gigaam_config& c;

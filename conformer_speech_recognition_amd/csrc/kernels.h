@@ -98,4 +98,20 @@ hipError_t launch_collapse(const int* frame_ids, int B, int U_max, const int* cu
 hipError_t launch_scatter_rows(const float* x, int d, int B, int U_max, const int* cuU,
                                float* out, hipStream_t s);
 
+// ---- RNNT greedy decoding (one workgroup per clip) ---------------------------------
+struct RnntParams {
+  const float* fenc;               // [batch * stride][J]: W_enc e_t + b_enc per frame
+  const float* gemb;               // [C][4P]: W_ih embed[k] + b_ih + b_hh per symbol
+  const void* whhT;                // T [P][4P]   (W_hh transposed)
+  const void* wpT;                 // T [P][J]    (W_pred transposed)
+  const float* bp;                 // [J]
+  const void* woT;                 // T [J][Cp]   (W_out transposed, columns padded)
+  const float* bo;                 // [C]
+  int P, J, C, Cp, max_symbols, stride, max_tokens;
+  int* tokens; int* tframes; int* ntok;
+  int frames[kMaxBatch];
+};
+size_t rnnt_lds_bytes(DType dt, int P, int J, int Cp);
+hipError_t launch_rnnt_decode(DType dt, const RnntParams& p, int batch, hipStream_t s);
+
 }  // namespace gg

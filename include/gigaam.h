@@ -224,6 +224,76 @@ int gigaam_debug_attention(int32_t dtype, int32_t d_model, int32_t n_heads, int3
                            const int32_t* frames_host, const void* qkv_dev, void* out_dev,
                            void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* ---------------------------------------------------------------------------------
+ * RNNT head ("GigaAM on MLX ...", section "What we're porting": a single-layer LSTM of
+ * size 320 plus a joint network; "GigaAM v3 RNNT - MLX" card: character model with 33
+ * letters + blank, sequential greedy decoding; "Notes for other runtimes": the LSTM
+ * bias is bias_ih + bias_hh and blank = len(vocabulary)). It decodes the encoder output
+ * that gigaam_encode writes to enc_out.
+ *
+ *   prediction network: x = embed[previous symbol] (blank at the start, zero state),
+ *                       PyTorch LSTM, gates (i, f, g, o) = W_ih x + W_hh h + b_ih + b_hh
+ *   joint:              logits = W_out relu(W_enc e_t + b_enc + W_pred h + b_pred) + b_out
+ *   greedy decoding:    per frame, argmax of the joint (lowest index on ties); blank
+ *                       moves to the next frame, another symbol is emitted, advances
+ *                       the prediction network and stays on the frame, at most
+ *                       max_symbols emissions per frame.
+ * ------------------------------------------------------------------------------- */
+typedef struct gigaam_rnnt_config {
+  int32_t d_model;       /* encoder width (768 / 1024); multiple of 64                 */
+  int32_t n_classes;     /* vocabulary + blank, blank id = n_classes - 1; 2 .. 8192    */
+  int32_t pred_hidden;   /* LSTM width (320); multiple of 64, <= 1024                  */
+  int32_t joint_hidden;  /* joint width (320); multiple of 64, <= 1024                 */
+  int32_t max_symbols;   /* emissions per encoder frame at most, 1 .. 64               */
+  int32_t dtype;         /* GIGAAM_F32 / F16 / BF16: storage of the head's matrices;
+                            every product accumulates in fp32, state stays fp32       */
+} gigaam_rnnt_config;
+
+typedef struct gigaam_rnnt gigaam_rnnt;
+
+int gigaam_rnnt_check_config(const gigaam_rnnt_config* cfg);
+
+/* Canonical host float32 buffer, as for the encoder, with the tensors (PyTorch layout)
+ * "rnnt.embed.weight" [n_classes, P], "rnnt.lstm.weight_ih_l0" [4P, P],
+ * "rnnt.lstm.weight_hh_l0" [4P, P], "rnnt.lstm.bias_ih_l0" [4P], "rnnt.lstm.bias_hh_l0"
+ * [4P], "rnnt.joint.enc.weight" [J, d], "rnnt.joint.enc.bias" [J],
+ * "rnnt.joint.pred.weight" [J, P], "rnnt.joint.pred.bias" [J], "rnnt.joint.out.weight"
+ * [n_classes, J], "rnnt.joint.out.bias" [n_classes], in that order.                  */
+int gigaam_rnnt_canonical_count(const gigaam_rnnt_config* cfg, int32_t* n_entries,
+                                size_t* n_floats);
+int gigaam_rnnt_canonical_entry(const gigaam_rnnt_config* cfg, int32_t i, char* name_buf,
+                                int32_t name_cap, int32_t* rank, int32_t* shape,
+                                size_t* offset_floats);
+int gigaam_rnnt_packed_bytes(const gigaam_rnnt_config* cfg, size_t* bytes);
+/* Host repacking: casts to the storage type (round-to-nearest-even), sums the two LSTM
+ * biases, stores W_hh, W_pred and W_out transposed. Errors: GIGAAM_E_INVAL on sizes.  */
+int gigaam_rnnt_pack_weights(const gigaam_rnnt_config* cfg, const float* canonical_host,
+                             size_t n_floats, void* packed_host, size_t packed_bytes);
+
+/* packed_dev: device copy of the packed blob (256-B aligned), borrowed by the handle. */
+int gigaam_rnnt_create(const gigaam_rnnt_config* cfg, const void* packed_dev,
+                       gigaam_rnnt** out);
+void gigaam_rnnt_destroy(gigaam_rnnt* head);
+
+/* Device workspace for `batch` clips whose encoder output rows are enc_stride apart. */
+int gigaam_rnnt_workspace_bytes(const gigaam_rnnt* head, int32_t batch, int32_t enc_stride,
+                                size_t* bytes);
+
+/* Greedy RNNT decoding of a padded batch of encoder outputs.
+ *   enc_dev          float [batch][enc_stride][d_model] (gigaam_encode's enc_out with
+ *                    enc_stride = U_max); clip b uses its first frames_host[b] rows.
+ *   frames_host      int32 [batch], each in [1, enc_stride].
+ *   tokens_dev       int32 [batch][max_tokens]: emitted symbols in order, -1 after them.
+ *   token_frames_dev int32 [batch][max_tokens]: frame of each symbol, -1 after; or NULL.
+ *   n_tokens_dev     int32 [batch].
+ *   max_tokens       >= enc_stride * max_symbols (the most a clip can emit).
+ * One workgroup per clip runs the whole sequential loop on the GPU (the stream is not
+ * synchronised). Errors: GIGAAM_E_INVAL, GIGAAM_E_WORKSPACE, GIGAAM_E_HIP.            */
+int gigaam_rnnt_decode(gigaam_rnnt* head, const float* enc_dev, int32_t enc_stride,
+                       const int32_t* frames_host, int32_t batch, void* workspace,
+                       size_t workspace_bytes, int32_t* tokens_dev, int32_t* token_frames_dev,
+                       int32_t* n_tokens_dev, int32_t max_tokens, void* hip_stream);
+
 /* Diagnostics: per-kernel timing. Between gigaam_profile_start and _stop every launch
  * of gigaam_encode is bracketed by HIP events recorded on the caller's stream (the
  * events add a little stream overhead). gigaam_profile_report waits for those events

@@ -200,5 +200,52 @@ def quantize_int8_g64(w: np.ndarray, group: int = 64) -> tuple[np.ndarray, np.nd
     return quantize_g64(w, 8, group)
 
 
+def rnnt_config(d_model: int, n_classes: int, dtype: str, pred_hidden: int = 320,
+                joint_hidden: int = 320, max_symbols: int = 10) -> dict:
+    """RNNT head shape: a 320-wide single-layer LSTM and joint ("GigaAM on MLX ...",
+    section "What we're porting"); the symbol cap per frame is a decoding setting."""
+    return dict(d_model=d_model, n_classes=n_classes, pred_hidden=pred_hidden,
+                joint_hidden=joint_hidden, max_symbols=max_symbols, dtype=dtype)
+
+
+def rnnt_entries(cfg: dict) -> list[tuple[str, tuple[int, ...]]]:
+    P, J, C, d = cfg["pred_hidden"], cfg["joint_hidden"], cfg["n_classes"], cfg["d_model"]
+    return [("rnnt.embed.weight", (C, P)), ("rnnt.lstm.weight_ih_l0", (4 * P, P)),
+            ("rnnt.lstm.weight_hh_l0", (4 * P, P)), ("rnnt.lstm.bias_ih_l0", (4 * P,)),
+            ("rnnt.lstm.bias_hh_l0", (4 * P,)), ("rnnt.joint.enc.weight", (J, d)),
+            ("rnnt.joint.enc.bias", (J,)), ("rnnt.joint.pred.weight", (J, P)),
+            ("rnnt.joint.pred.bias", (J,)), ("rnnt.joint.out.weight", (C, J)),
+            ("rnnt.joint.out.bias", (C,))]
+
+
+def make_rnnt_weights(cfg: dict, seed: int, blank_bias: float = 2.0) -> dict[str, np.ndarray]:
+    """Random-init RNNT head: matrices N(0, 1/fan_in) (unit-scale activations, so the
+    decisions depend on both the frame and the predictor state), embedding N(0, 1),
+    biases N(0, 0.1^2), plus ``blank_bias`` on the blank output so that a fair share of
+    the decisions are blanks, as in speech. Rounded to the storage type of the dtype."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    for name, shape in rnnt_entries(cfg):
+        if name.endswith("embed.weight"):
+            a = rng.standard_normal(shape)
+        elif len(shape) == 2:
+            a = rng.standard_normal(shape) / np.sqrt(shape[1])
+        else:
+            a = 0.1 * rng.standard_normal(shape)
+        out[name] = a
+    out["rnnt.joint.out.bias"][-1] += blank_bias
+    return {k: round_storage(v, cfg["dtype"]) for k, v in out.items()}
+
+
+def make_encoder_like(rng: np.random.Generator, frames: list[int], d: int) -> np.ndarray:
+    """Stand-in encoder output for the head alone: per clip, rows of N(0, 1) (the scale
+    of a LayerNorm output), zero-padded to the longest clip: float32 [B, U_max, d]."""
+    U = max(frames)
+    e = np.zeros((len(frames), U, d), dtype=np.float32)
+    for b, u in enumerate(frames):
+        e[b, :u] = rng.standard_normal((u, d)).astype(np.float32)
+    return e
+
+
 from .workloads import (WORKLOADS, workload, workload_config,  # noqa: E402,F401
                         workload_signals, workload_weights)

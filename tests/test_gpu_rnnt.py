@@ -1,0 +1,98 @@
+"""GPU: RNNT greedy decoding (gigaam_rnnt_decode) against the oracle.
+
+The head alone runs on stand-in encoder outputs (seeded N(0, 1) rows, clips of 1 to
+500 frames); the full path runs the tiny fp32 encoder and the head. A decoder's path
+is checked decision by decision: the oracle re-scores the GPU's symbols (and the frame
+of each) through its own prediction and joint networks, and every chosen symbol must
+be the oracle's argmax, or within the path's logit tolerance of it (a near-tie both
+precisions resolve correctly); >= 99.5% must be the exact argmax, and the fp32 path must
+reproduce the oracle's symbols exactly."""
+import numpy as np
+import pytest
+
+import synth
+from gpu_common import say
+from oracle import rnnt
+
+pytestmark = pytest.mark.gpu
+
+FRAMES = [1, 9, 64, 150, 333, 500]
+TOL = {"f32": 1e-3, "f16": 2e-2, "bf16": 5e-2}
+
+
+def _check_clip(P, enc_b, toks, frs, n, max_symbols, dtype, tag):
+    toks, frs = [int(x) for x in toks[:n]], [int(x) for x in frs[:n]]
+    steps = rnnt.rescore_path(enc_b, toks, frs, P, max_symbols=max_symbols)
+    exact, worst = 0, 0.0
+    for t, chosen, lg in steps:
+        lg32 = np.asarray(lg, np.float32).astype(np.float64)
+        gap = lg32.max() - lg32[chosen]
+        worst = max(worst, gap)
+        exact += int(chosen == rnnt.argmax32(lg))
+    want = rnnt.greedy_decode(enc_b, P, max_symbols=max_symbols)
+    blanks = sum(1 for _, ch, _ in steps if ch == P["rnnt.joint.out.bias"].shape[0] - 1)
+    say(f"[rnnt] {tag} U={enc_b.shape[0]}: {n} symbols ({len(steps)} decisions, {blanks} blank), "
+        f"exact {exact}/{len(steps)}, worst gap {worst:.2e}, oracle {len(want)} symbols, "
+        f"same {toks == want}")
+    assert worst <= TOL[dtype]
+    if dtype == "f32":
+        assert toks == want
+    return exact, len(steps)
+
+
+def _structure(out, frames, max_symbols):
+    tok = out["tokens"].cpu().numpy()
+    fr = out["token_frames"].cpu().numpy()
+    n = out["n_tokens"].cpu().numpy()
+    for b, u in enumerate(frames):
+        assert 0 <= n[b] <= u * max_symbols
+        assert np.all(tok[b, n[b]:] == -1) and np.all(fr[b, n[b]:] == -1)
+        f = fr[b, : n[b]]
+        assert np.all(np.diff(f) >= 0) and (n[b] == 0 or (f.min() >= 0 and f.max() < u))
+        if n[b]:
+            assert np.bincount(f).max() <= max_symbols
+    return tok, fr, n
+
+
+@pytest.mark.parametrize("dtype,C", [("f32", 34), ("f16", 34), ("bf16", 34), ("f16", 1025)])
+def test_rnnt_head_matches_oracle(dtype, C):
+    import torch
+    import conformer_speech_recognition_amd as gg
+    cfg = synth.rnnt_config(768, C, dtype)
+    w = synth.make_rnnt_weights(cfg, 21)
+    P = {k: np.asarray(v, np.float64) for k, v in w.items()}
+    enc = synth.make_encoder_like(np.random.default_rng(22), FRAMES, 768)
+    say(f"[rnnt] head {dtype} C={C}: decode {len(FRAMES)} clips")
+    head = gg.RnntHead(cfg, w)
+    out = head.decode(torch.from_numpy(enc).cuda(), FRAMES)
+    torch.cuda.synchronize()
+    tok, fr, n = _structure(out, FRAMES, cfg["max_symbols"])
+    ex = tot = 0
+    for b, u in enumerate(FRAMES):
+        e, t = _check_clip(P, enc[b, :u].astype(np.float64), tok[b], fr[b], n[b],
+                           cfg["max_symbols"], dtype, f"{dtype} C={C} clip {b}")
+        ex += e
+        tot += t
+    assert ex / tot >= 0.995
+    # the same call again gives the same bits
+    out2 = head.decode(torch.from_numpy(enc).cuda(), FRAMES)
+    assert torch.equal(out2["tokens"], out["tokens"]) and torch.equal(out2["n_tokens"], out["n_tokens"])
+
+
+def test_rnnt_after_the_tiny_encoder():
+    """Full path: the tiny fp32 encoder's output decoded on the GPU, re-scored against
+    the oracle's own encoder output and head."""
+    import torch
+    import conformer_speech_recognition_amd as gg
+    from gpu_common import model, oracle_clip, workload
+    cfg, pcm, lens, _ = workload("tiny")
+    out = model("tiny").encode(torch.from_numpy(pcm).cuda(), lens, want_enc=True)
+    rcfg = synth.rnnt_config(cfg["d_model"], 34, "f32")
+    w = synth.make_rnnt_weights(rcfg, 23)
+    P = {k: np.asarray(v, np.float64) for k, v in w.items()}
+    U = [int(u) for u in out["n_frames"]]
+    dec = gg.RnntHead(rcfg, w).decode(out["enc_out"], U)
+    torch.cuda.synchronize()
+    tok, fr, n = _structure(dec, U, rcfg["max_symbols"])
+    ref = oracle_clip("tiny", 0)
+    _check_clip(P, ref["enc_out"], tok[0], fr[0], n[0], rcfg["max_symbols"], "f32", "tiny e2e")
