@@ -115,6 +115,49 @@ def cpu_baseline(name, budget_s):
                       f"({audio:.2f} s of audio in {dt:.1f} s)"}
 
 
+def rnnt_leg(model, pcm_d, lens, cfg, steps, warmup):
+    """Greedy RNNT decoding of the batch's encoder output (synthetic character head of
+    the pages' RNNT model: 33 letters + blank, LSTM 320, joint 320), timed with events
+    on the stream alone and together with the encode."""
+    import torch
+    import conformer_speech_recognition_amd as gg
+    import synth
+    rcfg = synth.rnnt_config(cfg["d_model"], 34, "bf16" if cfg["dtype"] == "bf16" else
+                             ("f32" if cfg["dtype"] == "f32" else "f16"))
+    # blank bias 3.4: on this encoder output the random head then emits about two symbols
+    # per frame (more than speech, so the decode time is on the slow side)
+    head = gg.RnntHead(rcfg, synth.make_rnnt_weights(rcfg, 31, blank_bias=3.4))
+    enc = model.encode(pcm_d, lens, want_enc=True, want_frame_ids=False)
+    U = [int(u) for u in enc["n_frames"]]
+    for _ in range(warmup):
+        out = head.decode(enc["enc_out"], U)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    dec_ms, both_ms = [], []
+    for _ in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        out = head.decode(enc["enc_out"], U)
+        e1.record(st)
+        e1.synchronize()
+        dec_ms.append(e0.elapsed_time(e1))
+    for _ in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        enc2 = model.encode(pcm_d, lens, want_enc=True, want_frame_ids=False)
+        out = head.decode(enc2["enc_out"], U)
+        e1.record(st)
+        e1.synchronize()
+        both_ms.append(e0.elapsed_time(e1))
+    n = out["n_tokens"].cpu().numpy()
+    audio_s = float(np.sum(lens)) / 16000.0
+    return {"classes": 34, "dtype": rcfg["dtype"], "max_symbols": rcfg["max_symbols"],
+            "decode_ms_p50": round(float(np.median(dec_ms)), 4),
+            "encode_plus_decode_ms_p50": round(float(np.median(both_ms)), 4),
+            "encode_plus_decode_audio_s_per_s": round(audio_s / (float(np.median(both_ms)) * 1e-3), 1),
+            "symbols_per_frame": round(float(n.sum()) / float(sum(U)), 3)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -125,6 +168,9 @@ def main():
     ap.add_argument("--graph", action="store_true", help="replay the encode as a captured graph")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rnnt", action="store_true",
+                    help="also time greedy RNNT decoding (character head, 34 classes) of every "
+                         "encoded batch and report it beside the encoder line")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {a.gpus}); the "
@@ -223,6 +269,8 @@ def main():
                             "total_ms": round(r["total_ms"] / a.profile_steps, 4)} for r in prof),
                           key=lambda r: -r["total_ms"]),
     }
+    if a.rnnt:
+        line["rnnt"] = rnnt_leg(model, pcm_d, lens, cfg, a.steps, a.warmup)
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(a.workload, a.cpu_budget)
     print(json.dumps(line), flush=True)

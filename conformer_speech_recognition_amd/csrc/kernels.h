@@ -108,10 +108,11 @@ struct RnntParams {
   const void* woT;                 // T [J][Cp]   (W_out transposed, columns padded)
   const float* bo;                 // [C]
   int P, J, C, Cp, max_symbols, stride, max_tokens;
+  int wo_lds;                      // W_out^T is copied to LDS (rnnt_lds_bytes counts it)
   int* tokens; int* tframes; int* ntok;
   int frames[kMaxBatch];
 };
-size_t rnnt_lds_bytes(DType dt, int P, int J, int Cp);
+size_t rnnt_lds_bytes(DType dt, int P, int J, int Cp, bool wo_lds);
 hipError_t launch_rnnt_decode(DType dt, const RnntParams& p, int batch, hipStream_t s);
 
 }  // namespace gg

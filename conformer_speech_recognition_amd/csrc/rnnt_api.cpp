@@ -167,7 +167,7 @@ extern "C" int gigaam_rnnt_create(const gigaam_rnnt_config* cfg, const void* pac
   if (!packed_dev || !out) return fail(GIGAAM_E_INVAL, "NULL pointer");
   if ((uintptr_t)packed_dev & 255) return fail(GIGAAM_E_INVAL, "packed weights not 256-B aligned");
   const RnntLayout L = rnnt_layout(*cfg);
-  if (rnnt_lds_bytes((DType)cfg->dtype, cfg->pred_hidden, cfg->joint_hidden, L.Cp) > 160 * 1024)
+  if (rnnt_lds_bytes((DType)cfg->dtype, cfg->pred_hidden, cfg->joint_hidden, L.Cp, false) > 160 * 1024)
     return fail(GIGAAM_E_UNSUPPORTED, "RNNT state does not fit the 160 KiB of LDS");
   gigaam_rnnt* h = new gigaam_rnnt;
   h->cfg = *cfg;
@@ -251,6 +251,8 @@ extern "C" int gigaam_rnnt_decode(gigaam_rnnt* head, const float* enc_dev, int32
   rp.woT = Wp + L.woT; rp.bo = (const float*)(Wp + L.bo);
   rp.P = P; rp.J = J; rp.C = C; rp.Cp = L.Cp; rp.max_symbols = c.max_symbols;
   rp.stride = enc_stride; rp.max_tokens = max_tokens;
+  // W_out^T stays in LDS when that keeps the workgroup within 96 KiB
+  rp.wo_lds = rnnt_lds_bytes(dt, P, J, L.Cp, true) <= 96 * 1024;
   rp.tokens = tokens_dev; rp.tframes = token_frames_dev; rp.ntok = n_tokens_dev;
   for (int b = 0; b < batch; ++b) rp.frames[b] = frames_host[b];
   HIP_TRY(launch_rnnt_decode(dt, rp, batch, s));
