@@ -61,6 +61,19 @@ __device__ __forceinline__ float max3_(float a, float b, float c) {
   asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
   return r;
 }
+// Work order. Workgroups are dispatched round-robin over the 8 XCDs (workgroup i runs on
+// XCD i % 8), each with its own L2. Item w = head * n_tiles + q-tile keeps the q-tiles of
+// one clip and head next to each other; giving every XCD a contiguous range of items
+// means the K and V blocks of a clip and head are fetched into one L2, not into all.
+__device__ __forceinline__ void attn_item(int bid, int n_tiles, int n_heads, int& tile, int& h) {
+  const int total = n_tiles * n_heads;
+  const int q = total / 8, r = total % 8;
+  const int x = bid % 8, j = bid / 8;
+  const int w = x * q + (x < r ? x : r) + j;
+  h = w / n_tiles;
+  tile = w - h * n_tiles;
+}
+
 __device__ __forceinline__ float max_xor16(float v) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
                                                   false, false);
@@ -88,7 +101,8 @@ __global__ void __launch_bounds__(256) k_attn(AttnParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
-  const int tile = blockIdx.x, h = blockIdx.y;
+  int tile, h;
+  attn_item(blockIdx.x, p.n_tiles, p.n_heads, tile, h);
   const int b = p.tileQ[tile];
   const int base = p.cuU[b], U = p.cuU[b + 1] - base;
   const int qi = (tile - p.cuQ[b]) * 64 + wave * 16 + c16;
@@ -266,7 +280,8 @@ __global__ void __launch_bounds__(256) k_attn_f32(AttnParams p) {
   __shared__ float sVt[DK][VP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
-  const int tile = blockIdx.x, h = blockIdx.y;
+  int tile, h;
+  attn_item(blockIdx.x, p.n_tiles, p.n_heads, tile, h);
   const int b = p.tileQ[tile];
   const int base = p.cuU[b], U = p.cuU[b + 1] - base;
   const int qi = (tile - p.cuQ[b]) * 64 + wave * 16 + c16;
@@ -350,7 +365,7 @@ __global__ void __launch_bounds__(256) k_attn_f32(AttnParams p) {
 
 hipError_t launch_attention(DType dt, int dk, const AttnParams& p, hipStream_t s) {
   if (p.n_tiles <= 0) return hipSuccess;
-  dim3 grid(p.n_tiles, p.n_heads), blk(256);
+  dim3 grid(p.n_tiles * p.n_heads), blk(256);
 #define GG_A(T, D) hipLaunchKernelGGL((k_attn<T, D>), grid, blk, 0, s, p)
   if (dt == DT_F32) {
     if (dk == 48) hipLaunchKernelGGL(k_attn_f32<48>, grid, blk, 0, s, p);
