@@ -48,8 +48,12 @@ template <> __device__ __forceinline__ float from_f32<float>(float x) { return x
 template <> __device__ __forceinline__ f16 from_f32<f16>(float x) { return (f16)x; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
 
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
-__device__ __forceinline__ float siluf_(float x) { return x / (1.0f + __expf(-x)); }
+// Logistic sigmoid and SiLU from the hardware exp2 and reciprocal (about 1 ulp each);
+// an IEEE division costs ten dependent instructions per element in the epilogues.
+__device__ __forceinline__ float sigmoidf_(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.44269504088896341f * x));
+}
+__device__ __forceinline__ float siluf_(float x) { return x * sigmoidf_(x); }
 
 // Wave-wide (64 lanes) butterfly sums.
 __device__ __forceinline__ float wave_sum(float v) {
