@@ -177,6 +177,81 @@ def rnnt_leg(model, pcm_d, lens, cfg, steps, warmup):
             "symbols_per_frame": round(float(n.sum()) / float(sum(U)), 3)}
 
 
+def stream_leg(model, cfg, seconds=60, push_s=1.0, window_s=30.0):
+    """Pseudo-streaming: a synthetic signal pushed in push_s pieces, every push followed
+    by a re-encode of the last min(total, window_s) seconds (one gigaam_stream_step).
+    Per-step times are HIP events on the stream around push + step; the session is run
+    once untimed first."""
+    import torch
+    import conformer_speech_recognition_amd as gg
+    import synth
+    audio = torch.from_numpy(synth.make_signal(np.random.default_rng(60), int(seconds * 16000))).cuda()
+    n = int(push_s * 16000)
+    st = torch.cuda.current_stream()
+
+    def session(timed):
+        s = gg.Stream(model, window=int(window_s * 16000))
+        ms = []
+        for i in range(0, audio.numel(), n):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            s.push(audio[i: i + n])
+            s.step(want_frame_ids=False)
+            e1.record(st)
+            if timed:
+                e1.synchronize()
+                ms.append(e0.elapsed_time(e1))
+        torch.cuda.synchronize()
+        return ms
+    session(False)
+    ms = session(True)
+    buf = [min((i + 1) * push_s, window_s) for i in range(len(ms))]
+    at = {f"{int(b)}s": round(float(np.median([m for m, x in zip(ms, buf) if x == b])), 4)
+          for b in (1, 5, 10, 20, 30) if b in buf}
+    total = sum(ms) * 1e-3
+    return {"audio_s": seconds, "push_s": push_s, "window_s": window_s, "steps": len(ms),
+            "step_ms_at_buffer": at, "session_ms": round(sum(ms), 3),
+            "stream_audio_s_per_s": round(seconds / total, 1),
+            "reencoded_audio_s_per_s": round(sum(buf) / total, 1)}
+
+
+def sweep_leg(model, reps=5):
+    """Throughput of one encode call versus chunk length (a 300 s signal cut into equal
+    chunks encoded as one batch) and versus batch size (clips of 20 s)."""
+    import torch
+    import synth
+    x = synth.make_signal(np.random.default_rng(61), 300 * 16000)
+    st = torch.cuda.current_stream()
+
+    def rate(clips):
+        L = max(len(c) for c in clips)
+        pcm = np.zeros((len(clips), L), np.float32)
+        for i, c in enumerate(clips):
+            pcm[i, : len(c)] = c
+        lens = np.array([len(c) for c in clips], np.int32)
+        d = torch.from_numpy(pcm).cuda()
+        for _ in range(2):
+            model.encode(d, lens, want_frame_ids=False)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(st)
+        for _ in range(reps):
+            model.encode(d, lens, want_frame_ids=False)
+        e1.record(st)
+        e1.synchronize()
+        return round(float(lens.sum()) / 16000.0 * reps / (e0.elapsed_time(e1) * 1e-3), 1)
+
+    chunk = {}
+    for sec in (5, 10, 20, 30, 40):
+        n = sec * 16000
+        chunk[f"{sec}s"] = rate([x[i: i + n] for i in range(0, len(x), n)])
+    batch = {}
+    for b in (1, 2, 4, 8, 16, 32, 64):
+        clips = [synth.make_signal(np.random.default_rng(100 + i), 320000) for i in range(b)]
+        batch[str(b)] = rate(clips)
+    return {"unit": "audio-s/s", "chunk_len_300s_signal": chunk, "batch_of_20s_clips": batch}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -190,6 +265,11 @@ def main():
     ap.add_argument("--rnnt", action="store_true",
                     help="also time greedy RNNT decoding (character head, 34 classes) of every "
                          "encoded batch and report it beside the encoder line")
+    ap.add_argument("--stream", action="store_true",
+                    help="also time pseudo-streaming: 60 s pushed in 1 s pieces, each push followed "
+                         "by a re-encode of the last <= 30 s")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also report throughput versus chunk length and batch size")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {a.gpus}); the "
@@ -290,6 +370,10 @@ def main():
     }
     if a.rnnt:
         line["rnnt"] = rnnt_leg(model, pcm_d, lens, cfg, a.steps, a.warmup)
+    if a.stream:
+        line["stream"] = stream_leg(model, cfg)
+    if a.sweep:
+        line["sweep"] = sweep_leg(model)
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(a.workload, a.cpu_budget)
     print(json.dumps(line), flush=True)

@@ -69,6 +69,18 @@ def make_config(cfg: dict) -> Config:
     return c
 
 
+class StreamState(ctypes.Structure):
+    _fields_ = [("total", ctypes.c_int64), ("window", ctypes.c_int32), ("capacity", ctypes.c_int32),
+                ("start", ctypes.c_int32), ("length", ctypes.c_int32)]
+
+
+class StreamPlan(ctypes.Structure):
+    _fields_ = [("move_src", ctypes.c_int32), ("move_len", ctypes.c_int32),
+                ("append_at", ctypes.c_int32), ("append_len", ctypes.c_int32),
+                ("skip", ctypes.c_int32), ("start", ctypes.c_int32), ("length", ctypes.c_int32),
+                ("total", ctypes.c_int64)]
+
+
 _lib = None
 _P = ctypes.c_void_p
 _I = ctypes.c_int32
@@ -103,6 +115,11 @@ _SIGNATURES = {
     "gigaam_rnnt_destroy": (None, [_P]),
     "gigaam_rnnt_workspace_bytes": (ctypes.c_int, [_P, _I, _I, ctypes.POINTER(_SZ)]),
     "gigaam_rnnt_decode": (ctypes.c_int, [_P, _P, _I, _IP, _I, _P, _SZ, _P, _P, _P, _I, _P]),
+    "gigaam_stream_init": (ctypes.c_int, [ctypes.POINTER(StreamState), _I, _I]),
+    "gigaam_stream_plan_push": (ctypes.c_int, [ctypes.POINTER(StreamState), _I, ctypes.POINTER(StreamPlan)]),
+    "gigaam_stream_push": (ctypes.c_int, [ctypes.POINTER(StreamState), _P, _P, _I, _P]),
+    "gigaam_stream_step": (ctypes.c_int, [_P, ctypes.POINTER(StreamState), _P, _P, _SZ, _P, _P, _P, _P,
+                                          _P, _IP, _P]),
     "gigaam_profile_start": (ctypes.c_int, []),
     "gigaam_profile_stop": (ctypes.c_int, []),
     "gigaam_profile_report": (ctypes.c_int, [ctypes.c_char_p, _SZ]),
@@ -285,6 +302,62 @@ class Model:
         s = (stream or torch.cuda.current_stream(self.device)).cuda_stream
         _check(lib().gigaam_encode_stage(self._h, pcm.data_ptr(), lp, B, stride, ws.data_ptr(),
                                          ws.numel(), stage, out.data_ptr(), out.numel(), s))
+        return out
+
+
+class Stream:
+    """Pseudo-streaming over a Model: a device ring of ``capacity`` samples (default twice
+    the window) and one workspace sized for the window, reused by every step. ``push``
+    appends device samples; ``step`` re-encodes the last min(total, window) samples and
+    returns what ``Model.encode`` returns for one clip."""
+
+    def __init__(self, model: Model, window: int = 480000, capacity: int | None = None):
+        import torch
+        self.model = model
+        capacity = 2 * window if capacity is None else capacity
+        self.state = StreamState()
+        _check(lib().gigaam_stream_init(ctypes.byref(self.state), window, capacity))
+        self.ring = torch.empty(capacity, dtype=torch.float32, device=model.device)
+        self.ws = torch.empty(model.workspace_bytes(1, window), dtype=torch.uint8, device=model.device)
+
+    def plan(self, n: int) -> StreamPlan:
+        p = StreamPlan()
+        _check(lib().gigaam_stream_plan_push(ctypes.byref(self.state), n, ctypes.byref(p)))
+        return p
+
+    def push(self, pcm, stream=None):
+        import torch
+        if not (pcm.is_cuda and pcm.dtype == torch.float32 and pcm.dim() == 1 and pcm.is_contiguous()):
+            raise ValueError("pcm must be a contiguous 1-D float32 CUDA tensor")
+        s = (stream or torch.cuda.current_stream(self.model.device)).cuda_stream
+        _check(lib().gigaam_stream_push(ctypes.byref(self.state), self.ring.data_ptr(),
+                                        pcm.data_ptr() if pcm.numel() else None, pcm.numel(), s))
+
+    def window_view(self):
+        """The ring's current window (a view, valid until the next push)."""
+        return self.ring[self.state.start: self.state.start + self.state.length]
+
+    def step(self, want_enc: bool = False, want_frame_ids: bool = True, stream=None) -> dict:
+        import torch
+        n = int(self.state.length)
+        U = frames(n)[2] if n >= 320 else 0
+        C, d = self.model.cfg["n_classes"], self.model.cfg["d_model"]
+        dev = self.model.device
+        out = dict(log_probs=torch.empty(1, max(U, 1), C, dtype=torch.float32, device=dev),
+                   token_ids=torch.empty(1, max(U, 1), dtype=torch.int32, device=dev),
+                   n_tokens=torch.empty(1, dtype=torch.int32, device=dev))
+        if want_frame_ids:
+            out["frame_ids"] = torch.empty(1, max(U, 1), dtype=torch.int32, device=dev)
+        if want_enc:
+            out["enc_out"] = torch.empty(1, max(U, 1), d, dtype=torch.float32, device=dev)
+        nfr = np.zeros(1, dtype=np.int32)
+        s = (stream or torch.cuda.current_stream(dev)).cuda_stream
+        _check(lib().gigaam_stream_step(self.model._h, ctypes.byref(self.state), self.ring.data_ptr(),
+                                        self.ws.data_ptr(), self.ws.numel(), out["log_probs"].data_ptr(),
+                                        out["token_ids"].data_ptr(), out["n_tokens"].data_ptr(),
+                                        _ptr(out.get("frame_ids")), _ptr(out.get("enc_out")),
+                                        nfr.ctypes.data_as(_IP), s))
+        out["n_frames"] = nfr
         return out
 
 

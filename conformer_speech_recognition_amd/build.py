@@ -17,7 +17,7 @@ LIB = os.path.join(HERE, "libgigaam.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["gigaam.cpp", "rnnt_api.cpp", "meta.hip", "frontend.hip", "gemm.hip", "norm.hip",
+SOURCES = ["gigaam.cpp", "rnnt_api.cpp", "stream.cpp", "meta.hip", "frontend.hip", "gemm.hip", "norm.hip",
            "attention.hip", "dwconv.hip", "ctc.hip", "rnnt.hip"]
 
 CFLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-x", "hip",

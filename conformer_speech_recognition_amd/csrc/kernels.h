@@ -45,6 +45,8 @@ hipError_t launch_gemm(DType dt, int qbits, AMode am, Epi ep, const GemmParams& 
 // ---- meta -------------------------------------------------------------------------
 hipError_t launch_meta(const MetaArgs& a, const MetaDev& m, int T_tot, int S_tot, int U_tot,
                        hipStream_t s);
+// n floats from src to dst (non-overlapping device ranges)
+hipError_t launch_copy_f32(float* dst, const float* src, long n, hipStream_t s);
 
 // ---- frontend -----------------------------------------------------------------------
 hipError_t launch_frontend(const float* pcm, int stride, const float* window, const float* fb,

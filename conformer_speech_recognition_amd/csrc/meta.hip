@@ -51,3 +51,22 @@ hipError_t launch_meta(const MetaArgs& a, const MetaDev& m, int T_tot, int S_tot
 }
 
 }  // namespace gg
+
+namespace gg {
+
+// Plain device copy of n floats (the streaming ring's moves and appends); the ranges
+// never overlap.
+__global__ void __launch_bounds__(256) k_copy_f32(float* __restrict__ dst,
+                                                  const float* __restrict__ src, long n) {
+  const long stride = (long)gridDim.x * blockDim.x;
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += stride) dst[i] = src[i];
+}
+
+hipError_t launch_copy_f32(float* dst, const float* src, long n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const long blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(k_copy_f32, dim3(blocks < 1024 ? blocks : 1024), dim3(256), 0, s, dst, src, n);
+  return hipGetLastError();
+}
+
+}  // namespace gg

@@ -294,6 +294,63 @@ int gigaam_rnnt_decode(gigaam_rnnt* head, const float* enc_dev, int32_t enc_stri
                        size_t workspace_bytes, int32_t* tokens_dev, int32_t* token_frames_dev,
                        int32_t* n_tokens_dev, int32_t max_tokens, void* hip_stream);
 
+/* ---------------------------------------------------------------------------------
+ * Pseudo-streaming ("GigaAM on MLX ...", section "Streaming: honestly, it's
+ * pseudo-streaming"): the model is not a streaming model, so a stream keeps a growing
+ * buffer of the audio received so far and every step re-encodes all of it, but never
+ * more than the last `window` samples (30 s = 480000 in the port); a step costs more as
+ * the buffer grows.
+ *
+ * The caller owns a device ring of `capacity` float samples (capacity >= 2 * window) and
+ * a gigaam_stream_state, a plain host struct. gigaam_stream_push appends samples; when the
+ * ring has no room after the window, the retained samples are first moved to its start
+ * (a device copy of at most `window` samples, once per capacity - window samples pushed).
+ * gigaam_stream_step encodes the current window with gigaam_encode (batch 1); its
+ * workspace is gigaam_workspace_bytes(model, 1, window) and serves every step.       */
+typedef struct gigaam_stream_state {
+  int64_t total;      /* samples pushed since gigaam_stream_init                      */
+  int32_t window;     /* most samples one step encodes (>= 320)                         */
+  int32_t capacity;   /* samples the device ring holds (>= 2 * window)                  */
+  int32_t start;      /* ring offset of the window's first sample                       */
+  int32_t length;     /* samples in the window: min(total, window)                      */
+} gigaam_stream_state;
+
+/* What a push of n samples does to the ring, computed on the host only:
+ *   move_len samples at ring offset move_src go to offset 0 (move_len may be 0), then
+ *   the last append_len = min(n, window) samples of the pushed chunk go to offset
+ *   append_at; the new window is [start, start + length) of the updated state.       */
+typedef struct gigaam_stream_plan {
+  int32_t move_src, move_len;
+  int32_t append_at, append_len, skip;   /* skip = n - append_len leading samples dropped */
+  int32_t start, length;                 /* window after the push                          */
+  int64_t total;
+} gigaam_stream_plan;
+
+/* Initialise a state: window in [320, 2^30 / 2], capacity >= 2 * window.
+ * Errors: GIGAAM_E_INVAL.                                                             */
+int gigaam_stream_init(gigaam_stream_state* state, int32_t window, int32_t capacity);
+
+/* Plan a push of n >= 0 samples (no device work, state unchanged). Errors: GIGAAM_E_INVAL. */
+int gigaam_stream_plan_push(const gigaam_stream_state* state, int32_t n,
+                            gigaam_stream_plan* plan);
+
+/* Append n samples from pcm_dev (device, float) to the ring ring_dev (device, float
+ * [capacity]) with the library's copy kernel on hip_stream, then update the state (only
+ * when every launch succeeded). pcm_dev may be NULL when n == 0.
+ * Errors: GIGAAM_E_INVAL, GIGAAM_E_HIP.                                              */
+int gigaam_stream_push(gigaam_stream_state* state, float* ring_dev, const float* pcm_dev,
+                       int32_t n, void* hip_stream);
+
+/* Encode the current window: gigaam_encode of ring_dev + start with one clip of
+ * `length` samples; the outputs are those of gigaam_encode for batch 1 (U = frames of
+ * the window). Errors: GIGAAM_E_INVAL (fewer than 320 samples buffered, null pointer),
+ * GIGAAM_E_WORKSPACE, GIGAAM_E_HIP.                                                   */
+int gigaam_stream_step(gigaam_model* model, const gigaam_stream_state* state,
+                       const float* ring_dev, void* workspace, size_t workspace_bytes,
+                       float* log_probs_dev, int32_t* token_ids_dev, int32_t* n_tokens_dev,
+                       int32_t* frame_ids_dev, float* enc_out_dev, int32_t* n_frames_host,
+                       void* hip_stream);
+
 /* Diagnostics: per-kernel timing. Between gigaam_profile_start and _stop every launch
  * of gigaam_encode is bracketed by HIP events recorded on the caller's stream (the
  * events add a little stream overhead). gigaam_profile_report waits for those events
