@@ -103,7 +103,7 @@ _SIGNATURES = {
     "gigaam_workspace_bytes": (ctypes.c_int, [_P, _I, _I, ctypes.POINTER(_SZ)]),
     "gigaam_encode": (ctypes.c_int, [_P, _P, _IP, _I, _I, _P, _SZ, _P, _P, _P, _P, _P, _IP, _P]),
     "gigaam_encode_stage": (ctypes.c_int, [_P, _P, _IP, _I, _I, _P, _SZ, _I, _P, _SZ, _P]),
-    "gigaam_debug_gemm": (ctypes.c_int, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
+    "gigaam_debug_gemm": (ctypes.c_int, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _SZ, _IP, _P]),
     "gigaam_debug_attention": (ctypes.c_int, [_I, _I, _I, _I, _IP, _P, _P, _P, _SZ, _P]),
     "gigaam_rnnt_check_config": (ctypes.c_int, [ctypes.POINTER(RnntConfig)]),
     "gigaam_rnnt_canonical_count": (ctypes.c_int, [ctypes.POINTER(RnntConfig), _IP, ctypes.POINTER(_SZ)]),
@@ -368,18 +368,23 @@ def tokens_list(out: dict) -> list[list[int]]:
     return [ids[b, : n[b]].tolist() for b in range(len(n))]
 
 
-def debug_gemm(dtype: str, A, W, bias=None, scale=None, stream=None):
+def debug_gemm(dtype: str, A, W, bias=None, scale=None, split: bool = False, stream=None):
     """C = A @ W.T + bias with the encoder's GEMM kernel (A, W device tensors in the
     storage type of ``dtype``; for 'w8f16' / 'w6f16' / 'w4f16' W is the packed uint8
-    rows [N][K * bits / 8] of the header's layout, with fp16 ``scale`` [N][K / 64])."""
+    rows [N][K * bits / 8] of the header's layout, with fp16 ``scale`` [N][K / 64]).
+    With ``split`` the kernel may split the K sum as the encoder does for small batches;
+    returns (C, slices used)."""
     import torch
     M, K = A.shape
     N = W.shape[0]
     C = torch.empty(M, N, dtype=torch.float32, device=A.device)
+    part = torch.empty(256 * 256 * 128, dtype=torch.float32, device=A.device) if split else None
+    ks = np.zeros(1, dtype=np.int32)
     s = (stream or torch.cuda.current_stream(A.device)).cuda_stream
     _check(lib().gigaam_debug_gemm(DTYPES[dtype], M, N, K, A.data_ptr(), W.data_ptr(), _ptr(scale),
-                                   _ptr(bias), C.data_ptr(), s))
-    return C
+                                   _ptr(bias), C.data_ptr(), _ptr(part), part.numel() if split else 0,
+                                   ks.ctypes.data_as(_IP), s))
+    return (C, int(ks[0])) if split else C
 
 
 def profile_start():

@@ -500,6 +500,10 @@ __global__ void __launch_bounds__(64 * WGM * WGN, OCC) k_gemm_dl(GemmParams p) {
   const int m0 = tm * BM, n0 = tn * BN;
   const int KT = p.K / KB;
   const char* Ab = (const char*)((AM == A_DUAL && n0 >= p.nsplit) ? p.A2 : p.A);
+  // split-K: slice blockIdx.y multiplies k in [y K, (y + 1) K) and writes its own
+  // [M][ldc] block of partial sums
+  const long koff = (long)blockIdx.y * p.K;
+  if (gridDim.y > 1) p.C = (float*)p.C + blockIdx.y * (long)p.M * p.ldc;
 
   // load plan: instruction i of this wave fills stage rows RPI * (wave * LPW + i) + ...;
   // lane -> row R = base + lane / CPR, physical chunk lane % CPR = logical chunk ^ key(R)
@@ -510,10 +514,10 @@ __global__ void __launch_bounds__(64 * WGM * WGN, OCC) k_gemm_dl(GemmParams p) {
     const int lc = (lane % CPR) ^ ((R >> SWS) & (CPR - 1));
     if (R < BM) {
       const int gm = m0 + R < p.M ? m0 + R : p.M - 1;
-      src[i] = Ab + ((long)gm * p.lda + lc * 8) * sizeof(T);
+      src[i] = Ab + ((long)gm * p.lda + koff + lc * 8) * sizeof(T);
     } else {
       const int gn = n0 + R - BM < p.N ? n0 + R - BM : p.N - 1;
-      src[i] = (const char*)p.W + ((long)gn * p.ldw + lc * 8) * sizeof(T);
+      src[i] = (const char*)p.W + ((long)gn * p.ldw + koff + lc * 8) * sizeof(T);
     }
   }
   const uint32_t sbase = lds_u32(smem) + wave * LPW * 1024;
@@ -621,8 +625,107 @@ static hipError_t run_tiles(AMode am, Epi ep, const GemmParams& p, hipStream_t s
 //   N > 1024          : 256 x 128 tile, 64x64 per wave, 3 stages of 32 k (72 KiB LDS)
 //   N <= 1024, K <= 1024: 128 x 128 tile, 32x64 per wave, 3 stages of 32 k (48 KiB LDS)
 //   else              : 128 x 256 tile, 64x64 per wave, 2 stages of 64 k (96 KiB LDS)
+// 4 floats -> 4 elements of T in 8 bytes (round to nearest even)
+template <typename T> __device__ __forceinline__ u32x2 pack4(f32x4 v);
+template <> __device__ __forceinline__ u32x2 pack4<f16>(f32x4 v) {
+  f16x4 h = {(f16)v[0], (f16)v[1], (f16)v[2], (f16)v[3]};
+  return __builtin_bit_cast(u32x2, h);
+}
+template <> __device__ __forceinline__ u32x2 pack4<bf16>(f32x4 v) {
+  bf16x4 h = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+  return __builtin_bit_cast(u32x2, h);
+}
+
+// Split-K: out = epilogue(sum over slices of the fp32 partials + bias), the slices summed
+// in order 0, 1, ... (deterministic). Thread = 4 consecutive output columns of one row;
+// GLU reads the value columns and their gates 32 columns later (64-column groups).
+template <typename T, int EP>
+__global__ void __launch_bounds__(256) k_splitk_reduce(const float* __restrict__ part, int slices,
+                                                       GemmParams p) {
+  const int No = (EP == E_GLU) ? p.N / 2 : p.N;
+  const long q = (long)blockIdx.x * 256 + threadIdx.x;
+  const int qpr = No / 4;
+  if (q >= (long)p.M * qpr) return;
+  const int row = (int)(q / qpr), co = (int)(q % qpr) * 4;
+  const long slice = (long)p.M * p.N;
+  auto sum4 = [&](int col) {
+    f32x4 v = p.bias ? *(const f32x4*)(p.bias + col) : f32x4{0.f, 0.f, 0.f, 0.f};
+    const float* src = part + (long)row * p.N + col;
+    f32x4 a = *(const f32x4*)src;
+    for (int k = 1; k < slices; ++k) a += *(const f32x4*)(src + k * slice);
+    return a + v;
+  };
+  if constexpr (EP == E_GLU) {
+    const int c = (co / 32) * 64 + co % 32;              // value column; its gate is c + 32
+    const f32x4 v = sum4(c), g = sum4(c + 32);
+    f32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = v[j] * sigmoidf_(g[j]);
+    *(u32x2*)((T*)p.C + (long)row * p.ldc + co) = pack4<T>(o);
+  } else {
+    f32x4 v = sum4(co);
+    if constexpr (EP == E_SILU) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = siluf_(v[j]);
+    }
+    if constexpr (EP == E_STORE || EP == E_SILU) {
+      *(u32x2*)((T*)p.C + (long)row * p.ldc + co) = pack4<T>(v);
+    } else if constexpr (EP == E_RESID) {
+      f32x4* d = (f32x4*)((float*)p.C + (long)row * p.ldc + co);
+      *d = *d + p.alpha * v;
+    } else {
+      *(f32x4*)((float*)p.C + (long)row * p.ldc + co) = v;
+    }
+  }
+}
+
+// Slices for a launch of `tiles` workgroups over K (k-tile KB): only when the tiles fill
+// less than half the chip, at most 8 slices of at least two k-tiles, tiles * slices <= 256.
+static int splitk_slices(const GemmParams& p, long tiles, int KB, Epi ep) {
+  if (!p.part || tiles >= 128 || p.N % 4 != 0 || (ep == E_GLU && p.N % 64 != 0) || p.ldc % 4 != 0)
+    return 1;
+  int ks = 1;
+  while (ks < 8 && tiles * ks * 2 <= 256 && p.K % (ks * 2 * KB) == 0 && p.K / (ks * 2) >= 2 * KB &&
+         (long)p.M * p.N * ks * 2 <= p.part_cap)
+    ks *= 2;
+  return ks;
+}
+
+template <typename T>
+static hipError_t run_splitk_reduce(Epi ep, int ks, const GemmParams& p, hipStream_t s) {
+  const int No = (ep == E_GLU) ? p.N / 2 : p.N;
+  const long n = (long)p.M * (No / 4);
+  dim3 grid((unsigned)((n + 255) / 256));
+#define GG_R(EPv)                                                                      \
+  if (ep == EPv) {                                                                     \
+    hipLaunchKernelGGL((k_splitk_reduce<T, EPv>), grid, dim3(256), 0, s, p.part, ks, p); \
+    return hipGetLastError();                                                          \
+  }
+  GG_R(E_STORE) GG_R(E_SILU) GG_R(E_RESID) GG_R(E_GLU) GG_R(E_F32)
+#undef GG_R
+  return hipErrorInvalidValue;
+}
+
 template <typename T, int BM, int BN, int WGM, int WGN, int S, int KB>
 static hipError_t run_dl(AMode am, Epi ep, const GemmParams& p, hipStream_t s) {
+  const long tiles = (long)((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+  const int ks = splitk_slices(p, tiles, KB, ep);
+  if (ks > 1) {
+    // each slice's raw sums into part, then the epilogue over their ordered sum
+    GemmParams q = p;
+    q.K = p.K / ks;
+    q.C = p.part;
+    q.ldc = p.N;
+    q.bias = nullptr;
+    dim3 grid((unsigned)tiles, ks), blk(64 * WGM * WGN);
+    if (am == A_DUAL)
+      hipLaunchKernelGGL((k_gemm_dl<T, BM, BN, WGM, WGN, S, KB, A_DUAL, E_F32>), grid, blk, 0, s, q);
+    else
+      hipLaunchKernelGGL((k_gemm_dl<T, BM, BN, WGM, WGN, S, KB, A_PLAIN, E_F32>), grid, blk, 0, s, q);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return run_splitk_reduce<T>(ep, ks, p, s);
+  }
   dim3 grid(((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN)), blk(64 * WGM * WGN);
 #define GG_DL(AMv, EPv)                                                                          \
   if (am == AMv && ep == EPv) {                                                                  \
@@ -635,12 +738,33 @@ static hipError_t run_dl(AMode am, Epi ep, const GemmParams& p, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+// tile geometry of the direct-load shapes below: {BM, BN, KB}
+static void dl_geometry(const GemmParams& p, int& BM, int& BN, int& KB) {
+  if (p.N > 1024) { BM = 256; BN = 128; KB = 32; }
+  else if (p.K <= 1024) { BM = 128; BN = 128; KB = 32; }
+  else { BM = 128; BN = 256; KB = 64; }
+}
+
 template <typename T>
 static hipError_t run_dl_shape(AMode am, Epi ep, const GemmParams& p, hipStream_t s) {
   if (p.N > 1024) return run_dl<T, 256, 128, 4, 2, 3, 32>(am, ep, p, s);
   // narrow and short (the d x d projections): smaller tiles, twice as many blocks
   if (p.K <= 1024) return run_dl<T, 128, 128, 4, 2, 3, 32>(am, ep, p, s);
   return run_dl<T, 128, 256, 2, 4, 2, 64>(am, ep, p, s);
+}
+
+static bool direct_path(DType dt, int qbits, AMode am, Epi ep, const GemmParams& p) {
+  return dt != DT_F32 && qbits == 0 && (am == A_PLAIN || am == A_DUAL) && p.K % 64 == 0 &&
+         (ep == E_STORE || ep == E_SILU || ep == E_RESID || ep == E_GLU || ep == E_F32) &&
+         (am == A_PLAIN || ep == E_STORE);
+}
+
+int gemm_split_slices(DType dt, int qbits, AMode am, Epi ep, const GemmParams& p) {
+  if (!direct_path(dt, qbits, am, ep, p)) return 1;
+  int BM, BN, KB;
+  dl_geometry(p, BM, BN, KB);
+  const long tiles = (long)((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+  return splitk_slices(p, tiles, KB, ep);
 }
 
 hipError_t launch_gemm(DType dt, int qbits, AMode am, Epi ep, const GemmParams& p,
@@ -651,9 +775,7 @@ hipError_t launch_gemm(DType dt, int qbits, AMode am, Epi ep, const GemmParams& 
     if (am == A_F32) am = A_PLAIN;
     if (am == A_CONV_F32) am = A_CONV;
   }
-  const bool direct = qbits == 0 && (am == A_PLAIN || am == A_DUAL) && p.K % 64 == 0 &&
-                      (ep == E_STORE || ep == E_SILU || ep == E_RESID || ep == E_GLU || ep == E_F32) &&
-                      (am == A_PLAIN || ep == E_STORE);
+  const bool direct = direct_path(dt, qbits, am, ep, p);
   switch (dt) {
     case DT_F32: return run_tiles<float, 0>(am, ep, p, s);
     case DT_F16: return direct ? run_dl_shape<f16>(am, ep, p, s) : run_tiles<f16, 0>(am, ep, p, s);

@@ -535,7 +535,7 @@ namespace {
 
 struct Ws {
   size_t cuT, cuS, cuU, cuQ, rowT, rowS, rowU, tileQ;
-  size_t mel, h1, x, y, r, qkv, ao, hid, cos_t, sin_t, logits, fids;
+  size_t mel, h1, x, y, r, qkv, ao, hid, cos_t, sin_t, logits, fids, part;
   size_t total;
 };
 
@@ -560,6 +560,8 @@ Ws plan(const gigaam_config& c, int B, int T_tot, int S_tot, int U_tot, int nQ, 
   w.sin_t = take((size_t)U_max * (d / c.n_heads / 2) * 4);
   w.logits = take((size_t)U_tot * c.n_classes * 4);
   w.fids = take((size_t)B * U_max * 4);
+  // split-K partial sums of the 16-bit GEMMs (small batches)
+  w.part = take(c.dtype == GIGAAM_F32 ? 0 : (size_t)kSplitPartFloats * 4);
   w.total = off;
   return w;
 }
@@ -672,7 +674,12 @@ int run(gigaam_model* m, const float* pcm, const int32_t* lengths, int32_t B, in
     return GIGAAM_OK;
   };
   auto G = [&](const char* name, AMode am, Epi ep, int wq, const GemmParams& gp) -> int {
-    LAUNCH(name, launch_gemm(dt, wq, am, ep, gp, s));
+    GemmParams q = gp;
+    if (c.dtype != GIGAAM_F32) {
+      q.part = (float*)(W + w.part);
+      q.part_cap = kSplitPartFloats;
+    }
+    LAUNCH(name, launch_gemm(dt, wq, am, ep, q, s));
     return GIGAAM_OK;
   };
   auto lin = [&](const Lin& l, int M, int N, int K, const void* A, int lda, void* Cp, int ldc,
@@ -791,14 +798,20 @@ extern "C" int gigaam_encode_stage(gigaam_model* model, const float* pcm_dev, co
 
 extern "C" int gigaam_debug_gemm(int32_t dtype, int32_t M, int32_t N, int32_t K, const void* A_dev,
                                  const void* W_dev, const void* scale_dev, const float* bias_dev,
-                                 float* C_dev, void* hip_stream) {
+                                 float* C_dev, float* part_dev, size_t part_floats,
+                                 int32_t* slices_host, void* hip_stream) {
   if (dtype < GIGAAM_F32 || dtype > GIGAAM_W4F16) return fail(GIGAAM_E_INVAL, "dtype %d", dtype);
   if (M < 1 || N < 1 || K < 1) return fail(GIGAAM_E_INVAL, "bad shape %d x %d x %d", M, N, K);
   if (K % (dtype == GIGAAM_F32 ? 32 : 64)) return fail(GIGAAM_E_INVAL, "K %d not a multiple of the k-tile", K);
   const int qb = qbits_of(dtype);
   if (!A_dev || !W_dev || !C_dev || (qb && !scale_dev))
     return fail(GIGAAM_E_INVAL, "NULL pointer");
+  if (part_dev && ((uintptr_t)part_dev & 15))
+    return fail(GIGAAM_E_INVAL, "partial-sum buffer not 16-byte aligned");
   GemmParams p = gemm(M, N, K, A_dev, K, W_dev, scale_dev, bias_dev, C_dev, N);
+  p.part = part_dev;
+  p.part_cap = part_dev ? (long)part_floats : 0;
+  if (slices_host) *slices_host = gemm_split_slices((DType)dtype, qb, A_PLAIN, E_F32, p);
   HIP_TRY(launch_gemm((DType)dtype, qb, A_PLAIN, E_F32, p, (hipStream_t)hip_stream));
   return GIGAAM_OK;
 }

@@ -35,12 +35,20 @@ struct GemmParams {
   const int* cu_in;                // conv modes: input row offsets per clip
   const int* cu_out;               // conv modes: output row offsets per clip
   int cin;                         // conv modes: input channels (row length of source)
+  float* part;                     // split-K partial sums (fp32), or nullptr: never split
+  long part_cap;                   // floats available at part
 };
+
+// Floats of split-K partials any launch_gemm call may use (the workspace reserves this
+// much for part): a split keeps tiles * slices <= 256, so M * N * slices <= 256 * 256 * 128.
+constexpr long kSplitPartFloats = 256L * 256 * 128;
 
 // qbits: 0 = weights stored in the operand type; 8 / 6 / 4 = packed quantised rows with
 // fp16 group scales (dequantised to fp16 in the kernel)
 hipError_t launch_gemm(DType dt, int qbits, AMode am, Epi ep, const GemmParams& p,
                        hipStream_t s);
+// K slices launch_gemm uses for these arguments (1: no split)
+int gemm_split_slices(DType dt, int qbits, AMode am, Epi ep, const GemmParams& p);
 
 // ---- meta -------------------------------------------------------------------------
 hipError_t launch_meta(const MetaArgs& a, const MetaDev& m, int T_tot, int S_tot, int U_tot,

@@ -208,10 +208,16 @@ int gigaam_encode_stage(gigaam_model* model, const float* pcm_dev, const int32_t
  * GIGAAM_F16: fp16, GIGAAM_BF16: bf16; GIGAAM_W8F16 / W6F16 / W4F16: A fp16, W the
  * packed b-bit rows described above with scale_dev [N][K/64] fp16 scales); bias_dev
  * float[N] or NULL; C_dev float [M][N].
+ * part_dev: float [part_floats] scratch (16-byte aligned) for split-K partial sums, or
+ * NULL. With it the kernel splits the K sum across workgroups when the output tiles
+ * alone fill less than half the GPU, as the encoder does for small batches: each slice
+ * writes fp32 partials and a second kernel adds the slices in order and applies the
+ * epilogue. slices_host (may be NULL) receives the number of K slices used (1: none).
  * K must be a multiple of 64 (32 for GIGAAM_F32). Errors: GIGAAM_E_INVAL, GIGAAM_E_HIP. */
 int gigaam_debug_gemm(int32_t dtype, int32_t M, int32_t N, int32_t K, const void* A_dev,
                       const void* W_dev, const void* scale_dev, const float* bias_dev,
-                      float* C_dev, void* hip_stream);
+                      float* C_dev, float* part_dev, size_t part_floats, int32_t* slices_host,
+                      void* hip_stream);
 
 /* Diagnostics: the encoder's attention kernel on its own, over packed clips.
  * frames_host int32 [batch]: frames U_b of each clip (>= 1); qkv_dev [sum U_b][3 d_model]

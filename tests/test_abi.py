@@ -201,7 +201,9 @@ def test_encode_argument_errors_before_any_launch(gg):
     assert L.gigaam_encode_stage(h, fake, lens, 2, 32000, fake, nb.value, 0, out, 10, None) == gg.E_INVAL
     L.gigaam_destroy(h)
     assert L.gigaam_create(ctypes.byref(c), fake + 4, fake, fake, ctypes.byref(h)) == gg.E_INVAL
-    assert L.gigaam_debug_gemm(1, 4, 4, 100, fake, fake, None, None, fake, None) == gg.E_INVAL
+    assert L.gigaam_debug_gemm(1, 4, 4, 100, fake, fake, None, None, fake, None, 0, None, None) == gg.E_INVAL
+    assert L.gigaam_debug_gemm(1, 4, 4, 128, fake, fake, None, None, fake, fake + 4, 64, None,
+                               None) == gg.E_INVAL                  # misaligned partial buffer
 
 
 def test_workspace_bound_covers_every_length_mix(gg):

@@ -97,20 +97,35 @@ def test_workload_parity(name):
     assert raw_n / tot >= 0.98
 
 
-def test_batch_invariance_bit_exact():
-    """A clip's outputs do not depend on the other clips of the batch: the clip run alone
-    gives identical bits (row-independent GEMMs, per-clip attention / conv tiles)."""
+def test_clip_alone_matches_its_batch():
+    """A clip's outputs do not depend on the other clips of the batch beyond rounding: run
+    alone (few encoder rows, so its GEMMs split the K sums across workgroups and add the
+    slices in a fixed order) it agrees with its row of the batched run within the 16-bit
+    tolerance, meets the oracle bar itself, and repeats bit for bit."""
     import torch
     name = "batch32"
     out = _run(name)
     m = model(name)
     _, pcm, lens, _ = workload(name)
-    for b in (0, 5):
+    for b in _sample(name):
         L = int(lens[b])
-        one = m.encode(torch.from_numpy(pcm[b:b + 1, :L].copy()).cuda(), [L], want_enc=True)
-        u = one["n_frames"][0]
-        np.testing.assert_array_equal(one["enc_out"].cpu().numpy()[0], out["enc_out"][b, :u])
-        np.testing.assert_array_equal(one["frame_ids"].cpu().numpy()[0], out["frame_ids"][b, :u])
+        d = torch.from_numpy(pcm[b:b + 1, :L].copy()).cuda()
+        one = m.encode(d, [L], want_enc=True)
+        again = m.encode(d, [L], want_enc=True)
+        u = int(one["n_frames"][0])
+        for k in ("enc_out", "log_probs", "frame_ids"):
+            assert torch.equal(one[k], again[k])
+        enc = one["enc_out"].cpu().numpy()[0]
+        lp = one["log_probs"].cpu().numpy()[0]
+        d_batch = np.abs(enc - out["enc_out"][b, :u]).max()
+        ref = oracle_clip(name, b)
+        err = np.abs(enc - ref["enc_out"]).max()
+        lp_err = np.abs(lp - ref["log_probs"]).max()
+        raw, tie, _, _ = argmax_agreement(one["frame_ids"].cpu().numpy()[0], ref["log_probs"], lp_err)
+        say(f"[{name}] clip {b} alone U={u}: vs batch max|d| {d_batch:.3e}, vs oracle {err:.3e}, "
+            f"agree {raw:.4f} (tie-aware {tie:.4f})")
+        assert d_batch <= TOL_LOW and err <= TOL_LOW and lp_err <= TOL_LOW
+        assert tie >= ARGMAX_AGREE and raw >= 0.98
 
 
 def test_deterministic_and_poisoned_workspace():
