@@ -381,114 +381,51 @@ template <int N> __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Epilogue through LDS: the finished accumulators (bias and activation applied) are
-// written to LDS in the output type, then every thread copies whole 16-byte row segments
-// to global memory, so the stores are fully coalesced. fp32 tiles that do not fit are
-// done in chunks of whole wave-rows. The residual form adds the staged alpha * (acc + b)
-// to 16-byte vectors of x.
-template <typename T, int BM, int BN, int WGM, int WGN, int EP, int LDSB>
-__device__ __forceinline__ void epilogue_lds(const GemmParams& p,
-                                             f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32],
-                                             char* smem, int m0, int n0, int wm, int wn, int lane,
-                                             int tid) {
-  constexpr int WTM = BM / WGM, WTN = BN / WGN, MI = WTM / 32, NI = WTN / 32;
-  constexpr bool F32OUT = (EP == E_RESID || EP == E_F32 || EP == E_RELU_F32);
-  constexpr int OES = F32OUT ? 4 : (int)sizeof(T);
-  constexpr int BNO = (EP == E_GLU) ? BN / 2 : BN;             // output columns of the tile
-  constexpr int PITCH = BNO * OES + 16;                         // LDS bytes per staged row
-  constexpr int CHM = LDSB / PITCH;
-  constexpr int CH = (CHM >= BM) ? BM : (CHM / WTM) * WTM;     // rows per chunk
-  constexpr int NT = 64 * WGM * WGN;
-  constexpr int EPS = 16 / OES;                                 // elements per 16-byte segment
-  constexpr int SEGS = BNO / EPS;                               // segments per staged row
-  static_assert(CH >= WTM && BM % CH == 0, "epilogue chunking");
-  const int n0o = (EP == E_GLU) ? n0 / 2 : n0;
-  const int Nout = (EP == E_GLU) ? p.N / 2 : p.N;
-  const bool vec = ((long)p.ldc * OES) % 16 == 0;
-  const int c = lane & 31, h4 = 4 * (lane >> 5);
-#pragma unroll
-  for (int c0 = 0; c0 < BM; c0 += CH) {
-    __syncthreads();
-    if (wm * WTM >= c0 && wm * WTM < c0 + CH) {
-      if constexpr (EP == E_GLU) {
-#pragma unroll
-        for (int q = 0; q < NI / 2; ++q) {
-          const int cv = n0 + wn * WTN + 2 * q * 32 + c, cg = cv + 32;
-          const float bv = (p.bias && cv < p.N) ? p.bias[cv] : 0.f;
-          const float bg = (p.bias && cg < p.N) ? p.bias[cg] : 0.f;
-          const int co = (wn * WTN) / 2 + q * 32 + c;
-#pragma unroll
-          for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int rl = wm * WTM - c0 + mi * 32 + 8 * (r >> 2) + h4 + (r & 3);
-              const float v = acc[mi][2 * q][r] + bv, g = acc[mi][2 * q + 1][r] + bg;
-              *(T*)(smem + rl * PITCH + co * OES) = from_f32<T>(v * sigmoidf_(g));
-            }
-        }
-      } else {
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) {
-          const int ct = wn * WTN + ni * 32 + c;
-          const float bb = (p.bias && n0 + ct < p.N) ? p.bias[n0 + ct] : 0.f;
-#pragma unroll
-          for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int rl = wm * WTM - c0 + mi * 32 + 8 * (r >> 2) + h4 + (r & 3);
-              const float v = acc[mi][ni][r] + bb;
-              char* d = smem + rl * PITCH + ct * OES;
-              if constexpr (EP == E_STORE) *(T*)d = from_f32<T>(v);
-              else if constexpr (EP == E_SILU) *(T*)d = from_f32<T>(siluf_(v));
-              else if constexpr (EP == E_RELU) *(T*)d = from_f32<T>(fmaxf(v, 0.f));
-              else if constexpr (EP == E_RELU_F32) *(float*)d = fmaxf(v, 0.f);
-              else if constexpr (EP == E_RESID) *(float*)d = p.alpha * v;
-              else *(float*)d = v;
-            }
-        }
-      }
-    }
-    __syncthreads();
-    for (int e = tid; e < CH * SEGS; e += NT) {
-      const int rl = e / SEGS, sg = e - rl * SEGS;
-      const int row = m0 + c0 + rl;
-      const int col = n0o + sg * EPS;
-      if (row >= p.M || col >= Nout) continue;
-      const char* ls = smem + rl * PITCH + sg * 16;
-      char* gd = (char*)p.C + ((long)row * p.ldc + col) * OES;
-      if (vec && col + EPS <= Nout) {
-        if constexpr (EP == E_RESID) *(f32x4*)gd = *(const f32x4*)gd + *(const f32x4*)ls;
-        else *(u32x4*)gd = *(const u32x4*)ls;
-      } else {
-        for (int j = 0; j < EPS && col + j < Nout; ++j) {
-          if constexpr (EP == E_RESID) ((float*)gd)[j] += ((const float*)ls)[j];
-          else if constexpr (F32OUT) ((float*)gd)[j] = ((const float*)ls)[j];
-          else ((T*)gd)[j] = ((const T*)ls)[j];
-        }
-      }
-    }
-  }
+// 4 floats -> 4 elements of T in 8 bytes (round to nearest even)
+template <typename T> __device__ __forceinline__ u32x2 pack4(f32x4 v);
+template <> __device__ __forceinline__ u32x2 pack4<f16>(f32x4 v) {
+  f16x4 h = {(f16)v[0], (f16)v[1], (f16)v[2], (f16)v[3]};
+  return __builtin_bit_cast(u32x2, h);
+}
+template <> __device__ __forceinline__ u32x2 pack4<bf16>(f32x4 v) {
+  bf16x4 h = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+  return __builtin_bit_cast(u32x2, h);
+}
+
+// ---------------------------------------------------------------------------------------
+// The direct-load GEMM, software-pipelined: each wave reads the fragments of the next
+// 16-k phase between the MFMAs of the current one, and the k-tile boundary (own loads
+// waited, then the barrier) sits before the last phase's MFMAs, whose slots also issue
+// the loads of k-tile kt + S into the stage just freed, spread evenly over the MFMAs. A
+// wave never waits for an LDS read it issued in the same phase; the second wave on each
+// SIMD fills the remaining gaps (and runs its epilogue math while the other computes).
+//
+// The MFMA operands are swapped (W rows feed the MFMA's rows): a lane's accumulators of
+// a 32 x 32 block are one output row and four runs of 4 consecutive output columns, so
+// the epilogue stages the tile in LDS with 8-byte (T) or 16-byte (fp32) writes before the
+// row-wise 16-byte copy-out (every thread's LDS reads issued before its stores).
+
+// rows per epilogue chunk: the largest power-of-two part of BM that fits the LDS
+constexpr int chunk_rows(int BM, int fit) {
+  int c = BM;
+  while (c > fit && c > 32) c /= 2;
+  return c;
 }
 
 template <typename T, int BM, int BN, int WGM, int WGN, int S, int KB, int AM, int EP, int OCC = 1>
-__global__ void __launch_bounds__(64 * WGM * WGN, OCC) k_gemm_dl(GemmParams p) {
-  constexpr int NW = WGM * WGN;                 // waves per block
-  constexpr int WTM = BM / WGM, WTN = BN / WGN;
-  constexpr int MI = WTM / 32, NI = WTN / 32;
-  constexpr int RB = KB * 2;                    // bytes of one LDS row (KB k-elements)
-  constexpr int CPR = RB / 16;                  // 16-byte chunks per row (4 or 8)
-  constexpr int RPI = 1024 / RB;                // rows filled by one 1-KiB load instruction
-  // LDS serves a ds_read_b128 16 lanes at a time over 64 four-byte banks (256 B): the 16
-  // rows a fragment read touches per cycle must land on 16 different 16-byte slots of a
-  // 256-byte window. Rows of RB bytes repeat that window every 256 / RB rows, so the
-  // chunk XOR key is (row / (256 / RB)) mod CPR.
-  constexpr int SWS = (RB == 128) ? 1 : 2;      // swizzle key: (row >> SWS) & (CPR - 1)
-  constexpr int ROWS = BM + BN;
-  constexpr int STAGE = ROWS * RB;
-  constexpr int LPW = ROWS / RPI / NW;          // load instructions per wave per k-tile
+__global__ void __launch_bounds__(64 * WGM * WGN, OCC) k_gemm_p(GemmParams p) {
+  constexpr int NW = WGM * WGN, NT = 64 * NW;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN, MI = WTM / 32, NI = WTN / 32;
+  constexpr int RB = KB * 2, CPR = RB / 16, RPI = 1024 / RB;
+  constexpr int SWS = (RB == 128) ? 1 : 2;
+  constexpr int ROWS = BM + BN, STAGE = ROWS * RB;
+  constexpr int LPW = ROWS / RPI / NW;                 // loads per wave per k-tile
+  constexpr int PH = KB / 16;                          // 16-k phases per k-tile
+  constexpr int NM = MI * NI, NR = MI + NI;
+  constexpr int R0 = NR >= NM ? 0 : NM - NR;           // first MFMA slot of the boundary reads
   static_assert(KB == 32 || KB == 64, "k-tile");
-  static_assert(MI >= 1 && NI >= 1 && LPW * RPI * NW == ROWS && S >= 2, "tile");
-  static_assert(LPW * (S - 2) <= 63, "vmcnt range");
+  static_assert(LPW * RPI * NW == ROWS, "load plan");
+  static_assert(LPW * (S - 2) <= 63 && S >= 2, "vmcnt range");
   static_assert(EP != E_GLU || NI % 2 == 0, "GLU needs value/gate block pairs");
   __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
 
@@ -500,13 +437,9 @@ __global__ void __launch_bounds__(64 * WGM * WGN, OCC) k_gemm_dl(GemmParams p) {
   const int m0 = tm * BM, n0 = tn * BN;
   const int KT = p.K / KB;
   const char* Ab = (const char*)((AM == A_DUAL && n0 >= p.nsplit) ? p.A2 : p.A);
-  // split-K: slice blockIdx.y multiplies k in [y K, (y + 1) K) and writes its own
-  // [M][ldc] block of partial sums
-  const long koff = (long)blockIdx.y * p.K;
+  const long koff = (long)blockIdx.y * p.K;            // split-K slice
   if (gridDim.y > 1) p.C = (float*)p.C + blockIdx.y * (long)p.M * p.ldc;
 
-  // load plan: instruction i of this wave fills stage rows RPI * (wave * LPW + i) + ...;
-  // lane -> row R = base + lane / CPR, physical chunk lane % CPR = logical chunk ^ key(R)
   const char* src[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
@@ -521,70 +454,186 @@ __global__ void __launch_bounds__(64 * WGM * WGN, OCC) k_gemm_dl(GemmParams p) {
     }
   }
   const uint32_t sbase = lds_u32(smem) + wave * LPW * 1024;
-  auto issue = [&](int kt, int st) {
-#pragma unroll
-    for (int i = 0; i < LPW; ++i) dma16(sbase + st * STAGE + i * 1024, src[i] + kt * RB);
-  };
 
-  f32x16 acc[MI][NI];
+  f32x16 acc[NI][MI];
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi)
+  for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
-    for (int ni = 0; ni < NI; ++ni)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
+      for (int r = 0; r < 16; ++r) acc[ni][mi][r] = 0.0f;
 
-#pragma unroll
-  for (int st = 0; st < S - 1; ++st)
-    if (st < KT) issue(st, st);
-
-  // fragment rows are (lane & 31) + multiples of 32, so the swizzle key depends on lane only
   const int frow = (lane & 31) * RB;
   const int fkey = ((lane & 31) >> SWS) & (CPR - 1);
-  // 32-row blocks of the wave that lie wholly past M (the last row tile of a ragged M)
-  // read and multiply nothing
-  const int live = (p.M - m0 - wm * WTM + 31) / 32;
+  const int arow = (wm * WTM) * RB + frow, brow = (BM + wn * WTN) * RB + frow;
+  u32x4 fa[2][MI], fb[2][NI];
+  auto rd = [&](int st, int kc, int b, int r) {
+    const int off = st * STAGE + ((((kc * 2) + (lane >> 5)) ^ fkey) << 4);
+    if (r < MI) fa[b][r] = *(const u32x4*)(smem + off + arow + r * 32 * RB);
+    else fb[b][r - MI] = *(const u32x4*)(smem + off + brow + (r - MI) * 32 * RB);
+  };
+
+  // prologue: k-tiles 0 .. S-1 in flight, then k-tile 0 complete
+#pragma unroll
+  for (int g = 0; g < S; ++g)
+    if (g < KT)
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) dma16(sbase + g * STAGE + i * 1024, src[i] + g * RB);
+  {
+    const int inflight = KT < S ? KT : S;
+    if constexpr (S >= 4) { if (inflight >= 4) wait_vmcnt<3 * LPW>(); else if (inflight == 3) wait_vmcnt<2 * LPW>(); else if (inflight == 2) wait_vmcnt<LPW>(); else wait_vmcnt<0>(); }
+    else if constexpr (S == 3) { if (inflight >= 3) wait_vmcnt<2 * LPW>(); else if (inflight == 2) wait_vmcnt<LPW>(); else wait_vmcnt<0>(); }
+    else { if (inflight >= 2) wait_vmcnt<LPW>(); else wait_vmcnt<0>(); }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < NR; ++r) rd(0, 0, 0, r);
+
   for (int kt = 0; kt < KT; ++kt) {
-    const int ahead = (KT - 1 - kt) < (S - 2) ? (KT - 1 - kt) : (S - 2);
-    if constexpr (S >= 4) { if (ahead >= 2) wait_vmcnt<2 * LPW>(); else if (ahead == 1) wait_vmcnt<LPW>(); else wait_vmcnt<0>(); }
-    else if constexpr (S == 3) { if (ahead >= 1) wait_vmcnt<LPW>(); else wait_vmcnt<0>(); }
-    else wait_vmcnt<0>();
-    __syncthreads();
-    if (kt + S - 1 < KT) issue(kt + S - 1, (kt + S - 1) % S);
-    const char* base = smem + (kt % S) * STAGE;
-    if (live >= MI) {
+    const int st = kt % S, sn = (kt + 1) % S;
 #pragma unroll
-      for (int kc = 0; kc < KB / 16; ++kc) {
-        const int off = frow + ((((kc * 2) + (lane >> 5)) ^ fkey) << 4);
-        u32x4 af[MI], bfr[NI];
+    for (int kc = 0; kc < PH; ++kc) {
+      const int b = kc & 1;
+      if (kc < PH - 1) {
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi) af[mi] = *(const u32x4*)(base + (wm * WTM + mi * 32) * RB + off);
+        for (int j = 0; j < NM; ++j) {
+          Mma<T>::run(acc[j % NI][j / NI], fb[b][j % NI], fa[b][j / NI]);
+          if (j < NR) rd(st, kc + 1, b ^ 1, j);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (NR > NM) {
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni) bfr[ni] = *(const u32x4*)(base + (BM + wn * WTN + ni * 32) * RB + off);
+          for (int r = NM; r < NR; ++r) rd(st, kc + 1, b ^ 1, r);
+        }
+      } else {
+        // boundary: k-tile kt + 1 landed (own loads, then everyone's), stage st free
+        if (kt + 1 < KT) {
+          const int ahead = (KT - 2 - kt) < (S - 2) ? (KT - 2 - kt) : (S - 2);
+          if constexpr (S >= 4) { if (ahead >= 2) wait_vmcnt<2 * LPW>(); else if (ahead == 1) wait_vmcnt<LPW>(); else wait_vmcnt<0>(); }
+          else if constexpr (S == 3) { if (ahead >= 1) wait_vmcnt<LPW>(); else wait_vmcnt<0>(); }
+          else wait_vmcnt<0>();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        const bool more = kt + S < KT, next = kt + 1 < KT;
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
+        for (int j = 0; j < NM; ++j) {
+          Mma<T>::run(acc[j % NI][j / NI], fb[b][j % NI], fa[b][j / NI]);
+          if (more) {
 #pragma unroll
-          for (int ni = 0; ni < NI; ++ni) Mma<T>::run(acc[mi][ni], af[mi], bfr[ni]);
-      }
-    } else if (live > 0) {
-#pragma unroll
-      for (int kc = 0; kc < KB / 16; ++kc) {
-        const int off = frow + ((((kc * 2) + (lane >> 5)) ^ fkey) << 4);
-        u32x4 bfr[NI];
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) bfr[ni] = *(const u32x4*)(base + (BM + wn * WTN + ni * 32) * RB + off);
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi) {
-          if (mi < live) {
-            const u32x4 af = *(const u32x4*)(base + (wm * WTM + mi * 32) * RB + off);
-#pragma unroll
-            for (int ni = 0; ni < NI; ++ni) Mma<T>::run(acc[mi][ni], af, bfr[ni]);
+            for (int i = 0; i < LPW; ++i)          // loads spread evenly over the slots
+              if (i * NM / LPW == j) dma16(sbase + st * STAGE + i * 1024, src[i] + (kt + S) * RB);
           }
+          // the next k-tile's first reads take the last slots (all slots when NR > NM)
+          if (next && j >= R0) rd(sn, 0, 0, j - R0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (NR > NM) {
+          if (next)
+#pragma unroll
+            for (int r = NM; r < NR; ++r) rd(sn, 0, 0, r);
         }
       }
     }
   }
-  epilogue_lds<T, BM, BN, WGM, WGN, EP, S * STAGE>(p, acc, smem, m0, n0, wm, wn, lane, tid);
+
+  // ---- epilogue: stage through LDS in chunks of whole 32-row blocks, copy out rows
+  constexpr bool F32OUT = (EP == E_RESID || EP == E_F32);
+  constexpr int OES = F32OUT ? 4 : (int)sizeof(T);
+  constexpr int BNO = (EP == E_GLU) ? BN / 2 : BN;
+  constexpr int PITCH = BNO * OES + 16;
+  constexpr int CH = chunk_rows(BM, (S * STAGE) / PITCH);
+  constexpr int NCH = BM / CH;
+  constexpr int SEGS = BNO * OES / 16;
+  constexpr int PER = (CH * SEGS + NT - 1) / NT;
+  constexpr int EPS = 16 / OES;
+  static_assert(CH >= 32 && BM % CH == 0 && CH * PITCH <= S * STAGE, "epilogue chunking");
+  const int lr = lane & 31, h4 = 4 * (lane >> 5);
+  const int n0o = (EP == E_GLU) ? n0 / 2 : n0;
+  const int Nout = (EP == E_GLU) ? p.N / 2 : p.N;
+  const bool vec = ((long)p.ldc * OES) % 16 == 0;
+  // this lane's bias: 4 consecutive columns per (block, g), loaded once
+  f32x4 bv[NI][4];
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int col = n0 + wn * WTN + ni * 32 + 8 * g + h4;
+      bv[ni][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (p.bias) {
+        if (col + 4 <= p.N && (p.N & 3) == 0) bv[ni][g] = *(const f32x4*)(p.bias + col);
+        else
+          for (int j = 0; j < 4; ++j) bv[ni][g][j] = col + j < p.N ? p.bias[col + j] : 0.f;
+      }
+    }
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    __syncthreads();
+    const int rb0 = wm * WTM - c * CH;                          // wave's first row in the chunk
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const int rb = rb0 + mi * 32;
+      if (rb >= 0 && rb < CH) {
+        char* srow = smem + (rb + lr) * PITCH;
+        if constexpr (EP == E_GLU) {
+#pragma unroll
+          for (int q = 0; q < NI / 2; ++q)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              f32x4 v;
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                v[j] = (acc[2 * q][mi][4 * g + j] + bv[2 * q][g][j]) *
+                       sigmoidf_(acc[2 * q + 1][mi][4 * g + j] + bv[2 * q + 1][g][j]);
+              *(u32x2*)(srow + (wn * WTN / 2 + q * 32 + 8 * g + h4) * OES) = pack4<T>(v);
+            }
+        } else {
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              f32x4 v;
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const float x = acc[ni][mi][4 * g + j] + bv[ni][g][j];
+                v[j] = (EP == E_SILU) ? siluf_(x) : (EP == E_RESID) ? p.alpha * x : x;
+              }
+              const int cs = wn * WTN + ni * 32 + 8 * g + h4;
+              if constexpr (F32OUT) *(f32x4*)(srow + cs * 4) = v;
+              else *(u32x2*)(srow + cs * OES) = pack4<T>(v);
+            }
+        }
+      }
+    }
+    __syncthreads();
+    u32x4 sv[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = tid + NT * i, rl = e / SEGS, sg = e % SEGS;
+      if (e < CH * SEGS) sv[i] = *(const u32x4*)(smem + rl * PITCH + sg * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = tid + NT * i, rl = e / SEGS, sg = e % SEGS;
+      const int row = m0 + c * CH + rl, col = n0o + sg * EPS;
+      if (e >= CH * SEGS || row >= p.M || col >= Nout) continue;
+      char* gd = (char*)p.C + ((long)row * p.ldc + col) * OES;
+      if (vec && col + EPS <= Nout) {
+        if constexpr (EP == E_RESID)
+          *(f32x4*)gd = *(const f32x4*)gd + __builtin_bit_cast(f32x4, sv[i]);
+        else
+          *(u32x4*)gd = sv[i];
+      } else {                                      // ragged last segment or unaligned rows
+        const char* ls = smem + rl * PITCH + sg * 16;
+        for (int j = 0; j < EPS && col + j < Nout; ++j) {
+          if constexpr (EP == E_RESID) ((float*)gd)[j] += ((const float*)ls)[j];
+          else if constexpr (F32OUT) ((float*)gd)[j] = ((const float*)ls)[j];
+          else ((T*)gd)[j] = ((const T*)ls)[j];
+        }
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -618,22 +667,6 @@ template <typename T, int QB>
 static hipError_t run_tiles(AMode am, Epi ep, const GemmParams& p, hipStream_t s) {
   if (p.N <= 512 && ep != E_GLU) return run_epi<T, 128, 64, 4, 1, QB>(am, ep, p, s);
   return run_epi<T, 128, 128, 2, 2, QB>(am, ep, p, s);
-}
-
-// Direct-load pipeline for fp16/bf16 operands already in T (plain or dual A). Three
-// shapes of 8 waves, picked by N and K (measured on the encoder's GEMMs):
-//   N > 1024          : 256 x 128 tile, 64x64 per wave, 3 stages of 32 k (72 KiB LDS)
-//   N <= 1024, K <= 1024: 128 x 128 tile, 32x64 per wave, 3 stages of 32 k (48 KiB LDS)
-//   else              : 128 x 256 tile, 64x64 per wave, 2 stages of 64 k (96 KiB LDS)
-// 4 floats -> 4 elements of T in 8 bytes (round to nearest even)
-template <typename T> __device__ __forceinline__ u32x2 pack4(f32x4 v);
-template <> __device__ __forceinline__ u32x2 pack4<f16>(f32x4 v) {
-  f16x4 h = {(f16)v[0], (f16)v[1], (f16)v[2], (f16)v[3]};
-  return __builtin_bit_cast(u32x2, h);
-}
-template <> __device__ __forceinline__ u32x2 pack4<bf16>(f32x4 v) {
-  bf16x4 h = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
-  return __builtin_bit_cast(u32x2, h);
 }
 
 // Split-K: out = epilogue(sum over slices of the fp32 partials + bias), the slices summed
@@ -706,10 +739,11 @@ static hipError_t run_splitk_reduce(Epi ep, int ks, const GemmParams& p, hipStre
   return hipErrorInvalidValue;
 }
 
-template <typename T, int BM, int BN, int WGM, int WGN, int S, int KB>
+template <typename T, int BM, int BN, int WGM, int WGN, int S, int KB, int OCC>
 static hipError_t run_dl(AMode am, Epi ep, const GemmParams& p, hipStream_t s) {
   const long tiles = (long)((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   const int ks = splitk_slices(p, tiles, KB, ep);
+  dim3 blk(64 * WGM * WGN);
   if (ks > 1) {
     // each slice's raw sums into part, then the epilogue over their ordered sum
     GemmParams q = p;
@@ -717,20 +751,20 @@ static hipError_t run_dl(AMode am, Epi ep, const GemmParams& p, hipStream_t s) {
     q.C = p.part;
     q.ldc = p.N;
     q.bias = nullptr;
-    dim3 grid((unsigned)tiles, ks), blk(64 * WGM * WGN);
+    dim3 grid((unsigned)tiles, ks);
     if (am == A_DUAL)
-      hipLaunchKernelGGL((k_gemm_dl<T, BM, BN, WGM, WGN, S, KB, A_DUAL, E_F32>), grid, blk, 0, s, q);
+      hipLaunchKernelGGL((k_gemm_p<T, BM, BN, WGM, WGN, S, KB, A_DUAL, E_F32, OCC>), grid, blk, 0, s, q);
     else
-      hipLaunchKernelGGL((k_gemm_dl<T, BM, BN, WGM, WGN, S, KB, A_PLAIN, E_F32>), grid, blk, 0, s, q);
+      hipLaunchKernelGGL((k_gemm_p<T, BM, BN, WGM, WGN, S, KB, A_PLAIN, E_F32, OCC>), grid, blk, 0, s, q);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return run_splitk_reduce<T>(ep, ks, p, s);
   }
-  dim3 grid(((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN)), blk(64 * WGM * WGN);
-#define GG_DL(AMv, EPv)                                                                          \
-  if (am == AMv && ep == EPv) {                                                                  \
-    hipLaunchKernelGGL((k_gemm_dl<T, BM, BN, WGM, WGN, S, KB, AMv, EPv>), grid, blk, 0, s, p);  \
-    return hipGetLastError();                                                                    \
+  dim3 grid((unsigned)tiles);
+#define GG_DL(AMv, EPv)                                                                            \
+  if (am == AMv && ep == EPv) {                                                                    \
+    hipLaunchKernelGGL((k_gemm_p<T, BM, BN, WGM, WGN, S, KB, AMv, EPv, OCC>), grid, blk, 0, s, p); \
+    return hipGetLastError();                                                                      \
   }
   GG_DL(A_PLAIN, E_STORE) GG_DL(A_PLAIN, E_SILU) GG_DL(A_PLAIN, E_RESID) GG_DL(A_PLAIN, E_GLU)
   GG_DL(A_PLAIN, E_F32) GG_DL(A_DUAL, E_STORE)
@@ -738,19 +772,27 @@ static hipError_t run_dl(AMode am, Epi ep, const GemmParams& p, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-// tile geometry of the direct-load shapes below: {BM, BN, KB}
-static void dl_geometry(const GemmParams& p, int& BM, int& BN, int& KB) {
-  if (p.N > 1024) { BM = 256; BN = 128; KB = 32; }
-  else if (p.K <= 1024) { BM = 128; BN = 128; KB = 32; }
-  else { BM = 128; BN = 256; KB = 64; }
+// Shapes of the direct-load pipeline, 8 waves each, chosen by timing inside the encode
+// (operands arriving cold from the previous kernel) at 8207 rows:
+//   single-source outputs wider than 1024 (FFN up, pointwise-1): 256 x 256 tiles, 64 x 128
+//     per wave, 2 stages of 64 k (128 KiB LDS, one workgroup per CU);
+//   the q/k/v projection (two A sources split at a 128-aligned column) and outputs of at
+//     most 1024 columns with long K (FFN down): 256 x 128 tiles, 3 stages of 32 k, two
+//     workgroups per CU;
+//   outputs of at most 1024 columns with K <= 1024 (out-proj, pointwise-2): 128 x 128
+//     tiles, 3 stages of 32 k, two workgroups per CU.
+// Geometry {BM, BN, KB} of each, for the split-K planning:
+static void dl_geometry(AMode am, const GemmParams& p, int& BM, int& BN, int& KB) {
+  if (p.N > 1024 && am != A_DUAL) { BM = 256; BN = 256; KB = 64; }
+  else if (p.N > 1024 || p.K > 1024) { BM = 256; BN = 128; KB = 32; }
+  else { BM = 128; BN = 128; KB = 32; }
 }
 
 template <typename T>
 static hipError_t run_dl_shape(AMode am, Epi ep, const GemmParams& p, hipStream_t s) {
-  if (p.N > 1024) return run_dl<T, 256, 128, 4, 2, 3, 32>(am, ep, p, s);
-  // narrow and short (the d x d projections): smaller tiles, twice as many blocks
-  if (p.K <= 1024) return run_dl<T, 128, 128, 4, 2, 3, 32>(am, ep, p, s);
-  return run_dl<T, 128, 256, 2, 4, 2, 64>(am, ep, p, s);
+  if (p.N > 1024 && am != A_DUAL) return run_dl<T, 256, 256, 4, 2, 2, 64, 1>(am, ep, p, s);
+  if (p.N > 1024 || p.K > 1024) return run_dl<T, 256, 128, 4, 2, 3, 32, 2>(am, ep, p, s);
+  return run_dl<T, 128, 128, 4, 2, 3, 32, 2>(am, ep, p, s);
 }
 
 static bool direct_path(DType dt, int qbits, AMode am, Epi ep, const GemmParams& p) {
@@ -762,7 +804,7 @@ static bool direct_path(DType dt, int qbits, AMode am, Epi ep, const GemmParams&
 int gemm_split_slices(DType dt, int qbits, AMode am, Epi ep, const GemmParams& p) {
   if (!direct_path(dt, qbits, am, ep, p)) return 1;
   int BM, BN, KB;
-  dl_geometry(p, BM, BN, KB);
+  dl_geometry(am, p, BM, BN, KB);
   const long tiles = (long)((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   return splitk_slices(p, tiles, KB, ep);
 }
@@ -776,6 +818,7 @@ hipError_t launch_gemm(DType dt, int qbits, AMode am, Epi ep, const GemmParams& 
     if (am == A_CONV_F32) am = A_CONV;
   }
   const bool direct = direct_path(dt, qbits, am, ep, p);
+  if (direct && am == A_DUAL && p.nsplit % 128 != 0) return hipErrorInvalidValue;
   switch (dt) {
     case DT_F32: return run_tiles<float, 0>(am, ep, p, s);
     case DT_F16: return direct ? run_dl_shape<f16>(am, ep, p, s) : run_tiles<f16, 0>(am, ep, p, s);
