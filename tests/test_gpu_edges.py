@@ -1,0 +1,94 @@
+"""GPU edge cases of the packed batch against the oracle: one-frame clips next to long
+ones, clips whose encoder length sits on either side of the 64-frame attention and
+depthwise tiles, lengths one sample past a frame boundary, and the largest batch one
+call accepts (256 clips). The fp32 path must match the oracle to 1e-4 with identical
+tokens; the 16-layer fp16 path meets the 16-bit bar on every clip."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_common import ARGMAX_AGREE, TOL_F32, TOL_LOW, argmax_agreement, model, say, workload
+
+pytestmark = pytest.mark.gpu
+
+# encoder frames 1, 1, 2, 3, 63, 64, 65, 127, 128, 129, 250 (320 samples is the shortest clip)
+EDGE_LENGTHS = [320, 479, 960, 1600, 40000, 40640, 41280, 80960, 81600, 82240, 159680]
+
+
+def _batch(lengths, seed):
+    rng = np.random.default_rng(seed)
+    sig = [synth.make_signal(rng, int(n)) for n in lengths]
+    return synth.pad_batch(sig)
+
+
+def _check_clip(out, b, ref, dtype):
+    u = ref["enc_out"].shape[0]
+    assert out["n_frames"][b] == u
+    enc = out["enc_out"][b, :u]
+    assert np.all(out["enc_out"][b, u:] == 0) and np.all(out["frame_ids"][b, u:] == -1)
+    err = np.abs(enc - ref["enc_out"]).max()
+    ids = out["frame_ids"][b, :u]
+    n = out["n_tokens"][b]
+    if dtype == "f32":
+        assert err <= TOL_F32, (b, u, err)
+        np.testing.assert_array_equal(ids, oracle.greedy_ids(ref["log_probs"]))
+        assert out["token_ids"][b, :n].tolist() == ref["tokens"]
+        return err, 1.0
+    lp_err = np.abs(out["log_probs"][b, :u] - ref["log_probs"]).max()
+    raw, tie, _, _ = argmax_agreement(ids, ref["log_probs"], lp_err)
+    assert err <= TOL_LOW and lp_err <= TOL_LOW, (b, u, err, lp_err)
+    return err, tie
+
+
+def _encode(name, pcm, lens):
+    import torch
+    out = model(name).encode(torch.from_numpy(pcm).cuda(), lens, want_enc=True)
+    torch.cuda.synchronize()
+    return {k: (v.cpu().numpy() if hasattr(v, "cpu") else v) for k, v in out.items()}
+
+
+@pytest.mark.parametrize("name", ["tiny", "v3_20s"])
+def test_ragged_extremes(name):
+    cfg, _, _, w = workload(name)
+    lengths = EDGE_LENGTHS if name == "tiny" else EDGE_LENGTHS[::2]
+    pcm, lens = _batch(lengths, 70)
+    say(f"[edges] {name}: {len(lens)} clips, encoder frames "
+        f"{[oracle.encoder_frames(int(n))[2] for n in lens]}")
+    out = _encode(name, pcm, lens)
+    dtype = "f32" if cfg["dtype"] == "f32" else "low"
+    agree, frames = 0.0, 0
+    for b, L in enumerate(lens):
+        ref = oracle.encode_clip(pcm[b, :L], w, cfg)
+        err, tie = _check_clip(out, b, ref, dtype)
+        u = ref["enc_out"].shape[0]
+        agree += tie * u
+        frames += u
+        say(f"[edges] {name} clip {b} U={u}: enc max|d| {err:.3e}")
+    assert agree / frames >= ARGMAX_AGREE
+
+
+def test_largest_batch():
+    import torch
+    import conformer_speech_recognition_amd as gg
+    cfg, _, _, w = workload("tiny")
+    rng = np.random.default_rng(71)
+    lengths = rng.integers(320, 9600, gg.MAX_BATCH)
+    pcm, lens = _batch(lengths, 72)
+    say(f"[edges] tiny: batch of {len(lens)} clips, {int(lens.sum())} samples")
+    out = _encode("tiny", pcm, lens)
+    C = cfg["n_classes"]
+    for b, L in enumerate(lens):                     # every clip: shape and collapse rules
+        u = oracle.encoder_frames(int(L))[2]
+        assert out["n_frames"][b] == u
+        ids = out["frame_ids"][b, :u]
+        assert ids.min() >= 0 and ids.max() < C and np.all(out["frame_ids"][b, u:] == -1)
+        n = out["n_tokens"][b]
+        assert out["token_ids"][b, :n].tolist() == oracle.ctc_collapse(ids, C - 1)
+    order = np.argsort(lens)
+    for b in sorted({int(order[0]), int(order[-1]), 0, 100, 255}):
+        _check_clip(out, b, oracle.encode_clip(pcm[b, :lens[b]], w, cfg), "f32")
+        one = model("tiny").encode(torch.from_numpy(pcm[b:b + 1, :lens[b]].copy()).cuda(),
+                                   [int(lens[b])], want_enc=True)
+        u = int(one["n_frames"][0])
+        np.testing.assert_array_equal(one["enc_out"].cpu().numpy()[0], out["enc_out"][b, :u])
