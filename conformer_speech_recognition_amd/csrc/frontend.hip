@@ -12,6 +12,10 @@
 //   X[k1 + 16 k2] = sum_{n2<20} Z[n2][k1] W20^(n2 k2)            (20-point DFTs)
 // evaluated in fp32 with twiddles rounded from fp64, for bins k <= 160 only; then
 // power, mel projection and log-clip. The small DFTs keep their twiddles in registers.
+// A one-block prologue kernel builds, once per launch, the twiddle table and each mel
+// filter's range of nonzero weights; the projection sums over that range only, in the
+// same ascending order as the full sum, so the result is the same (the skipped terms
+// are exact zeros).
 #include "kernels.h"
 
 namespace gg {
@@ -21,9 +25,34 @@ constexpr int FE_N = 320;     // FFT size = window length
 constexpr int FE_K = 161;     // power bins 0..160
 constexpr int FE_M = 64;      // mel bins
 
+// twiddles W320^j = tw[j] - i tw[320 + j] (rounded from fp64) and, per mel filter m, the
+// first and last bin with a nonzero weight (melr[2m], melr[2m + 1]; an all-zero filter
+// gets an empty range)
+__global__ void __launch_bounds__(FE_N) k_frontend_prep(const float* __restrict__ fb,
+                                                        float* __restrict__ tw,
+                                                        int* __restrict__ melr) {
+  const int i = threadIdx.x;
+  double sn, cs;
+  sincospi(2.0 * i / FE_N, &sn, &cs);
+  tw[i] = (float)cs;
+  tw[FE_N + i] = (float)sn;
+  if (i < FE_M) {
+    int lo = FE_K, hi = -1;
+    for (int k = 0; k < FE_K; ++k)
+      if (fb[k * FE_M + i] != 0.f) {
+        lo = k < lo ? k : lo;
+        hi = k;
+      }
+    melr[2 * i] = lo;
+    melr[2 * i + 1] = hi;
+  }
+}
+
 __global__ void __launch_bounds__(256) k_frontend(const float* __restrict__ pcm, int stride,
                                                   const float* __restrict__ window,
-                                                  const float* __restrict__ fb, MetaDev m,
+                                                  const float* __restrict__ fb,
+                                                  const float* __restrict__ tw,
+                                                  const int* __restrict__ melr, MetaDev m,
                                                   int T_tot, float* __restrict__ mel) {
   __shared__ float xw[FE_FT][FE_N];
   __shared__ float tc[FE_N], ts[FE_N];           // W320^j = tc[j] - i ts[j]
@@ -33,10 +62,8 @@ __global__ void __launch_bounds__(256) k_frontend(const float* __restrict__ pcm,
   const int f0 = blockIdx.x * FE_FT;
 
   for (int i = tid; i < FE_N; i += 256) {
-    double sn, cs;
-    sincospi(2.0 * i / FE_N, &sn, &cs);
-    tc[i] = (float)cs;
-    ts[i] = (float)sn;
+    tc[i] = tw[i];
+    ts[i] = tw[FE_N + i];
   }
   for (int e = tid; e < FE_FT * FE_N; e += 256) {
     const int f = e / FE_N, n = e - f * FE_N, g = f0 + f;
@@ -100,18 +127,22 @@ __global__ void __launch_bounds__(256) k_frontend(const float* __restrict__ pcm,
   // mel projection + log clip: thread (f, m)
   for (int e = tid; e < FE_FT * FE_M; e += 256) {
     const int f = e >> 6, mm = e & 63;
+    const int lo = melr[2 * mm], hi = melr[2 * mm + 1];
     float acc = 0.f;
-    for (int k = 0; k < FE_K; ++k) acc = fmaf(fb[k * FE_M + mm], P[f][k], acc);
+#pragma unroll 4
+    for (int k = lo; k <= hi; ++k) acc = fmaf(fb[k * FE_M + mm], P[f][k], acc);
     const int g = f0 + f;
     if (g < T_tot) mel[(long)g * FE_M + mm] = logf(fminf(fmaxf(acc, 1e-9f), 1e9f));
   }
 }
 
 hipError_t launch_frontend(const float* pcm, int stride, const float* window, const float* fb,
-                           const MetaDev& m, int T_tot, float* mel, hipStream_t s) {
+                           const MetaDev& m, int T_tot, float* mel, float* tw, int* melr,
+                           hipStream_t s) {
   if (T_tot <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_frontend_prep, dim3(1), dim3(FE_N), 0, s, fb, tw, melr);
   hipLaunchKernelGGL(k_frontend, dim3((T_tot + FE_FT - 1) / FE_FT), dim3(256), 0, s, pcm, stride,
-                     window, fb, m, T_tot, mel);
+                     window, fb, tw, melr, m, T_tot, mel);
   return hipGetLastError();
 }
 

@@ -535,7 +535,7 @@ namespace {
 
 struct Ws {
   size_t cuT, cuS, cuU, cuQ, rowT, rowS, rowU, tileQ;
-  size_t mel, h1, x, y, r, qkv, ao, hid, cos_t, sin_t, logits, fids, part;
+  size_t mel, h1, x, y, r, qkv, ao, hid, cos_t, sin_t, logits, fids, part, fe;
   size_t total;
 };
 
@@ -560,6 +560,7 @@ Ws plan(const gigaam_config& c, int B, int T_tot, int S_tot, int U_tot, int nQ, 
   w.sin_t = take((size_t)U_max * (d / c.n_heads / 2) * 4);
   w.logits = take((size_t)U_tot * c.n_classes * 4);
   w.fids = take((size_t)B * U_max * 4);
+  w.fe = take((640 + 128) * 4);               // frontend twiddles and mel filter ranges
   // split-K partial sums of the 16-bit GEMMs (small batches)
   w.part = take(c.dtype == GIGAAM_F32 ? 0 : (size_t)kSplitPartFloats * 4);
   w.total = off;
@@ -691,7 +692,8 @@ int run(gigaam_model* m, const float* pcm, const int32_t* lengths, int32_t B, in
   // ---- geometry to the device
   LAUNCH("meta", launch_meta(meta, md, T_tot, S_tot, U_tot, s));
   // ---- a1 frontend
-  LAUNCH("frontend", launch_frontend(pcm, stride, m->window, m->fb, md, T_tot, mel, s));
+  LAUNCH("frontend", launch_frontend(pcm, stride, m->window, m->fb, md, T_tot, mel,
+                                     (float*)(W + w.fe), (int*)(W + w.fe + 640 * 4), s));
   if (stage == GIGAAM_STAGE_MEL) return copy_out(mel, (size_t)T_tot * 64);
   // ---- a2, a3 subsampling (implicit-GEMM Conv1d k5 s2 p2 + ReLU)
   {
