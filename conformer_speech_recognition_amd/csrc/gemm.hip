@@ -425,7 +425,8 @@ __global__ void __launch_bounds__(64 * WGM * WGN, OCC) k_gemm_p(GemmParams p) {
   constexpr int R0 = NR >= NM ? 0 : NM - NR;           // first MFMA slot of the boundary reads
   static_assert(KB == 32 || KB == 64, "k-tile");
   static_assert(LPW * RPI * NW == ROWS, "load plan");
-  static_assert(LPW * (S - 2) <= 63 && S >= 2, "vmcnt range");
+  // the prologue leaves up to min(S, 4) - 1 load groups in flight (the vmcnt field is 6 bits)
+  static_assert(LPW * ((S < 4 ? S : 4) - 1) <= 63 && S >= 2, "vmcnt range");
   static_assert(EP != E_GLU || NI % 2 == 0, "GLU needs value/gate block pairs");
   __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
 
