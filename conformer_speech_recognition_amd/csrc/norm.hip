@@ -1,4 +1,4 @@
-// Row LayerNorm (one wave per row, fp32 statistics) with three fused variants:
+// Row LayerNorm (one wave per row or per two rows, fp32 statistics) with three fused variants:
 //   LN_PLAIN : y = LN(x) -> T                      (FFN and conv-module pre-norms)
 //   LN_ROPE  : y = LN(x) -> T and r = rope(y) -> T (attention pre-norm; the rotation is
 //              applied per head to the raw normed input BEFORE the q/k projections,
@@ -54,21 +54,13 @@ __device__ __forceinline__ void ln_row(float (&v)[4 * NI], const float* g, const
   }
 }
 
+// normalise one row held in v (the row's loads already issued) and write its outputs
 template <typename T, int NI, int MODE>
-__global__ void __launch_bounds__(256) k_ln(LnParams p) {
+__device__ __forceinline__ void ln_finish(const LnParams& p, float (&v)[4 * NI], int row, int lane,
+                                          float* sr, float cv, float sv) {
   constexpr int D = NI * 256;
-  __shared__ float srow[MODE == LN_ROPE ? 4 : 1][MODE == LN_ROPE ? D + D / 16 : 1];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int row = blockIdx.x * 4 + wv;
-  if (row >= p.rows) return;
-  float v[4 * NI];
+  constexpr int DK = D / 16, HALF = DK / 2;      // 16 heads
   float* xr = p.x + (long)row * D + 4 * lane;
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const f32x4 q = *(const f32x4*)(xr + 256 * i);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) v[4 * i + j] = q[j];
-  }
   ln_row<NI>(v, p.g1, p.b1, lane, p.eps);
   T* yr = (T*)p.y + (long)row * D + 4 * lane;
   if constexpr (MODE == LN_TWO) {
@@ -87,18 +79,14 @@ __global__ void __launch_bounds__(256) k_ln(LnParams p) {
 #pragma unroll
   for (int i = 0; i < NI; ++i) store4<T>(yr + 256 * i, v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
   if constexpr (MODE == LN_ROPE) {
-    constexpr int DK = D / 16, HALF = DK / 2;      // 16 heads
-    float* sr = srow[wv];
 #pragma unroll
     for (int i = 0; i < NI; ++i)
       *(f32x4*)(sr + 256 * i + 4 * lane) = f32x4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
-    // this frame's cos / sin rows next to the normed row (one coalesced load each)
-    const int b = p.rowclip[row];
-    const int t = row - p.cu[b];
+    // this frame's cos / sin rows next to the normed row
     float* cs = sr + D;
     if (lane < HALF) {
-      cs[lane] = p.cos_t[(long)t * HALF + lane];
-      cs[HALF + lane] = p.sin_t[(long)t * HALF + lane];
+      cs[lane] = cv;
+      cs[HALF + lane] = sv;
     }
     float r[4 * NI];
 #pragma unroll
@@ -116,13 +104,62 @@ __global__ void __launch_bounds__(256) k_ln(LnParams p) {
   }
 }
 
+// One wave per RPW consecutive rows: every row's loads (and, for RoPE, its cos / sin
+// entries, a chain of three dependent loads) are issued before the first row's statistics,
+// so a wave keeps RPW rows of reads in flight and the grid fits the chip in one round.
+template <typename T, int NI, int MODE, int RPW>
+__global__ void __launch_bounds__(256) k_ln(LnParams p) {
+  constexpr int D = NI * 256;
+  constexpr int DK = D / 16, HALF = DK / 2;
+  __shared__ float srow[MODE == LN_ROPE ? 4 : 1][MODE == LN_ROPE ? D + D / 16 : 1];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int row0 = (blockIdx.x * 4 + wv) * RPW;
+  if (row0 >= p.rows) return;
+  float v[RPW][4 * NI];
+  float cv[RPW], sv[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int row = row0 + r < p.rows ? row0 + r : p.rows - 1;   // past the end: reload the last
+    const float* xr = p.x + (long)row * D + 4 * lane;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const f32x4 q = *(const f32x4*)(xr + 256 * i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[r][4 * i + j] = q[j];
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    cv[r] = 0.f;
+    sv[r] = 0.f;
+    if constexpr (MODE == LN_ROPE) {
+      const int row = row0 + r < p.rows ? row0 + r : p.rows - 1;
+      const int t = row - p.cu[p.rowclip[row]];
+      if (lane < HALF) {
+        cv[r] = p.cos_t[(long)t * HALF + lane];
+        sv[r] = p.sin_t[(long)t * HALF + lane];
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < RPW; ++r)
+    if (row0 + r < p.rows) ln_finish<T, NI, MODE>(p, v[r], row0 + r, lane, srow[wv], cv[r], sv[r]);
+}
+
+// rows per wave, by timing inside the encode: two for the two-norm variant (14.8 vs 16.7 us
+// at 8207 rows of 768), one for the others (two made the RoPE variant slower, 13.6 -> 14.9)
+template <typename T, int NI, int MODE, int RPW>
+static void ln_launch(const LnParams& p, hipStream_t s) {
+  dim3 grid((p.rows + 4 * RPW - 1) / (4 * RPW));
+  hipLaunchKernelGGL((k_ln<T, NI, MODE, RPW>), grid, dim3(256), 0, s, p);
+}
+
 template <typename T, int NI>
 static hipError_t ln_modes(LnMode mode, const LnParams& p, hipStream_t s) {
-  dim3 grid((p.rows + 3) / 4);
   switch (mode) {
-    case LN_PLAIN: hipLaunchKernelGGL((k_ln<T, NI, LN_PLAIN>), grid, dim3(256), 0, s, p); break;
-    case LN_ROPE: hipLaunchKernelGGL((k_ln<T, NI, LN_ROPE>), grid, dim3(256), 0, s, p); break;
-    case LN_TWO: hipLaunchKernelGGL((k_ln<T, NI, LN_TWO>), grid, dim3(256), 0, s, p); break;
+    case LN_PLAIN: ln_launch<T, NI, LN_PLAIN, 1>(p, s); break;
+    case LN_ROPE: ln_launch<T, NI, LN_ROPE, 1>(p, s); break;
+    case LN_TWO: ln_launch<T, NI, LN_TWO, 2>(p, s); break;
   }
   return hipGetLastError();
 }
