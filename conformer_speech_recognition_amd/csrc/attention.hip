@@ -45,6 +45,15 @@ template <typename T> __device__ __forceinline__ u32x4 pack8f(const float* v) {
   return __builtin_bit_cast(u32x4, h);
 }
 
+// Column of key k (a multiple of 4) in a V^T row. The P operand of a lane in group g holds
+// keys 4g .. 4g + 3 and 16 + 4g .. 16 + 4g + 3 of each 32-key half; V^T rows store every
+// half as [4g .. 4g + 3 | 16 + 4g .. 16 + 4g + 3] for g = 0..3, so the lane's 8 keys are
+// one 16-byte LDS read (two 8-byte reads 32 bytes apart conflicted on half the banks).
+__device__ __forceinline__ int vcol(int k) {
+  const int w = k & 31;
+  return (k & ~31) + ((w & 15) >> 2) * 8 + (w >> 4) * 4;
+}
+
 // ---------------------------------------------------------------- fp16 / bf16 kernel
 // K and V^T tiles are double-buffered in LDS: the next 64-key tile is loaded into
 // registers while the current one is consumed, and stored after it (one barrier per
@@ -163,9 +172,11 @@ __global__ void __launch_bounds__(256) k_attn(AttnParams p) {
       typedef uint16_t h4 __attribute__((ext_vector_type(4)));
       const h8 v0 = __builtin_bit_cast(h8, rv[0]), v1 = __builtin_bit_cast(h8, rv[1]);
       const h8 v2 = __builtin_bit_cast(h8, rv[2]), v3 = __builtin_bit_cast(h8, rv[3]);
+      // keys 4vq .. 4vq + 3 go to their permuted column (see vcol)
+      const int col = vcol(4 * vq);
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        *(h4*)&sVt[buf][vch * 8 + i][4 * vq] = h4{v0[i], v1[i], v2[i], v3[i]};
+        *(h4*)&sVt[buf][vch * 8 + i][col] = h4{v0[i], v1[i], v2[i], v3[i]};
     }
   };
   // d_k = 48: the score MFMA's upper 16 k slots read the zero pad columns [48, 56) of the
@@ -244,10 +255,7 @@ __global__ void __launch_bounds__(256) k_attn(AttnParams p) {
       const u32x4 pb = pack8f<T>(pp);
 #pragma unroll
       for (int db = 0; db < NDBX; ++db) {
-        const T* vr = &sVt[buf][db * 16 + c16][32 * hk + 4 * g];
-        const u32x2 lo = *(const u32x2*)vr;
-        const u32x2 hi = *(const u32x2*)(vr + 16);
-        o[db] = AttnMma<T>::k32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb, o[db]);
+        o[db] = AttnMma<T>::k32(*(const u32x4*)&sVt[buf][db * 16 + c16][32 * hk + 8 * g], pb, o[db]);
       }
     }
     if (more) store(buf ^ 1);
