@@ -55,16 +55,70 @@ __device__ __forceinline__ float sigmoidf_(float x) {
 }
 __device__ __forceinline__ float siluf_(float x) { return x * sigmoidf_(x); }
 
-// Wave-wide (64 lanes) butterfly sums.
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+// Lane exchanges for butterfly reductions, without the LDS crossbar that a shuffle
+// (ds_bpermute) goes through.
+//  * lanes 32 / 16 apart: v_permlane32_swap / v_permlane16_swap on two copies of a value
+//    return {own, partner} in an order that depends on the lane's half, so the x32 / x16
+//    steps combine both results with a symmetric operation (a + b, max, argmax with the
+//    lower index on ties): each lane gets exactly combine(v, v[lane ^ o]).
+//  * lanes 8 apart: DPP row rotation by 8 inside a 16-lane row is exactly lane ^ 8.
+//  * lanes 4 apart: a row rotation by 4 equals lane ^ 4 once the values repeat every 8
+//    lanes of a row, which a butterfly run from 8 (or wider) downwards guarantees.
+//  * lanes 2 / 1 apart: DPP quad permutations [2,3,0,1] / [1,0,3,2] are exact.
+// So a butterfly over o = 32, 16, .., 1 (or 16, .., 1 or 8, .., 1 inside aligned groups)
+// computes the same values, in the same order, as one built on __shfl_xor.
+__device__ __forceinline__ uint32_t fbits(float v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ float ffrom(uint32_t v) { return __builtin_bit_cast(float, v); }
+template <int CTRL> __device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+}
+template <int CTRL> __device__ __forceinline__ float dpp_f(float v) { return ffrom(dpp_u<CTRL>(fbits(v))); }
+constexpr int kDppRor8 = 0x128, kDppRor4 = 0x124, kDppXor2 = 0x4E, kDppXor1 = 0xB1;
+
+// {own, partner} pairs (order unspecified) for lanes 32 / 16 apart
+__device__ __forceinline__ void pair_x32(uint32_t v, uint32_t& a, uint32_t& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  a = r[0];
+  b = r[1];
+}
+__device__ __forceinline__ void pair_x16(uint32_t v, uint32_t& a, uint32_t& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  a = r[0];
+  b = r[1];
+}
+
+// butterfly sum over aligned groups of G lanes (G = 64, 32, 16, 8, 4, 2 or 1)
+template <int G> __device__ __forceinline__ float group_sum(float v) {
+  uint32_t a, b;
+  if constexpr (G >= 64) { pair_x32(fbits(v), a, b); v = ffrom(a) + ffrom(b); }
+  if constexpr (G >= 32) { pair_x16(fbits(v), a, b); v = ffrom(a) + ffrom(b); }
+  if constexpr (G >= 16) { v += dpp_f<kDppRor8>(v); v += dpp_f<kDppRor4>(v); }
+  else if constexpr (G == 8) { v += __shfl_xor(v, 4, 64); }   // values not 8-periodic yet
+  if constexpr (G >= 4) v += dpp_f<kDppXor2>(v);
+  if constexpr (G >= 2) v += dpp_f<kDppXor1>(v);
   return v;
 }
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+__device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
+
+// wave-wide argmax: the larger value wins, the lower index on equal values (the values
+// must not be NaN)
+__device__ __forceinline__ void argmax_take(float& best, int& bi, float ov, int oi) {
+  if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
+}
+__device__ __forceinline__ void wave_argmax(float& best, int& bi) {
+  uint32_t a, b, ia, ib;
+  pair_x32(fbits(best), a, b);
+  pair_x32((uint32_t)bi, ia, ib);
+  best = ffrom(a); bi = (int)ia;
+  argmax_take(best, bi, ffrom(b), (int)ib);
+  pair_x16(fbits(best), a, b);
+  pair_x16((uint32_t)bi, ia, ib);
+  best = ffrom(a); bi = (int)ia;
+  argmax_take(best, bi, ffrom(b), (int)ib);
+  argmax_take(best, bi, dpp_f<kDppRor8>(best), (int)dpp_u<kDppRor8>((uint32_t)bi));
+  argmax_take(best, bi, dpp_f<kDppRor4>(best), (int)dpp_u<kDppRor4>((uint32_t)bi));
+  argmax_take(best, bi, dpp_f<kDppXor2>(best), (int)dpp_u<kDppXor2>((uint32_t)bi));
+  argmax_take(best, bi, dpp_f<kDppXor1>(best), (int)dpp_u<kDppXor1>((uint32_t)bi));
 }
 
 }  // namespace gg

@@ -30,12 +30,7 @@ __global__ void __launch_bounds__(256) k_logsoftmax_argmax(const float* __restri
     const float v = z[c];
     if (v > best) { best = v; bi = c; }        // ascending c: first max wins per lane
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const float ov = __shfl_xor(best, o, 64);
-    const int oi = __shfl_xor(bi, o, 64);
-    if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
-  }
+  wave_argmax(best, bi);
   float s = 0.f;
   for (int c = lane; c < C; c += 64) s += expf(z[c] - best);
   s = wave_sum(s);

@@ -88,15 +88,19 @@ __device__ __forceinline__ void ln_finish(const LnParams& p, float (&v)[4 * NI],
       cs[lane] = cv;
       cs[HALF + lane] = sv;
     }
+    // a lane's 4 consecutive features sit in one half of one head (4 divides d_k / 2), so
+    // their partners, cosines and sines are 16-byte LDS reads
     float r[4 * NI];
 #pragma unroll
-    for (int e = 0; e < 4 * NI; ++e) {
-      const int j = 256 * (e >> 2) + 4 * lane + (e & 3);     // feature index
+    for (int i = 0; i < NI; ++i) {
+      const int j = 256 * i + 4 * lane;                      // first feature of the group
       const int pos = j % DK;                                // position inside the head
       const bool lo = pos < HALF;
       const int i2 = lo ? pos : pos - HALF;
-      const float partner = sr[lo ? j + HALF : j - HALF];
-      r[e] = v[e] * cs[i2] + (lo ? -partner : partner) * cs[HALF + i2];
+      const f32x4 pt = *(const f32x4*)(sr + (lo ? j + HALF : j - HALF));
+      const f32x4 cc = *(const f32x4*)(cs + i2), sn = *(const f32x4*)(cs + HALF + i2);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) r[4 * i + q] = v[4 * i + q] * cc[q] + (lo ? -pt[q] : pt[q]) * sn[q];
     }
     T* rr = (T*)p.r + (long)row * D + 4 * lane;
 #pragma unroll
@@ -111,7 +115,7 @@ template <typename T, int NI, int MODE, int RPW>
 __global__ void __launch_bounds__(256) k_ln(LnParams p) {
   constexpr int D = NI * 256;
   constexpr int DK = D / 16, HALF = DK / 2;
-  __shared__ float srow[MODE == LN_ROPE ? 4 : 1][MODE == LN_ROPE ? D + D / 16 : 1];
+  __shared__ __attribute__((aligned(16))) float srow[MODE == LN_ROPE ? 4 : 1][MODE == LN_ROPE ? D + D / 16 : 1];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int row0 = (blockIdx.x * 4 + wv) * RPW;
   if (row0 >= p.rows) return;

@@ -81,9 +81,19 @@ __device__ void matvec_lanes(const T* __restrict__ M, int ldm, int rows, int col
 #pragma unroll
       for (int i = 0; i < V; ++i) acc[i] = fmaf(w[i], xr, acc[i]);
     }
-    for (int o = S >> 1; o >= 1; o >>= 1)
+    // butterfly over the S lanes of the group (same order as lane-xor shuffles)
 #pragma unroll
-      for (int i = 0; i < V; ++i) acc[i] += __shfl_xor(acc[i], o, 64);
+    for (int i = 0; i < V; ++i) {
+      switch (S) {
+        case 64: acc[i] = group_sum<64>(acc[i]); break;
+        case 32: acc[i] = group_sum<32>(acc[i]); break;
+        case 16: acc[i] = group_sum<16>(acc[i]); break;
+        case 8: acc[i] = group_sum<8>(acc[i]); break;
+        case 4: acc[i] = group_sum<4>(acc[i]); break;
+        case 2: acc[i] = group_sum<2>(acc[i]); break;
+        default: break;
+      }
+    }
     if (sl == 0)
 #pragma unroll
       for (int i = 0; i < V; ++i)
@@ -199,12 +209,7 @@ __global__ void __launch_bounds__(RN_T) k_rnnt(RnntParams p) {
         const float a = logit[v];
         if (a > best) { best = a; bi = v; }
       }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const float ov = __shfl_xor(best, o, 64);
-        const int oi = __shfl_xor(bi, o, 64);
-        if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
-      }
+      wave_argmax(best, bi);
       const int k = bi >= C ? blank : bi;             // all logits NaN: treat as blank
       if (k == blank) break;
       if (tid == 0) {
