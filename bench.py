@@ -38,15 +38,15 @@ PEAK_HBM_GBS = 8000.0
 # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch) on this
 # bench, scaled by what the counters read for a plain copy of known size; valid only while the
 # kernel's source is the one the counters were taken on (sha256 prefix)
-GEMM_SRC = ("conformer_speech_recognition_amd/csrc/gemm.hip", "69ae26207e7cdf73")
-ATTN_SRC = ("conformer_speech_recognition_amd/csrc/attention.hip", "c540d65501571cfc")
-TRAFFIC_KIB = {("batch32", "gemm.ffn_up"): (GEMM_SRC, 41517, 49242),
-               ("batch32", "gemm.ffn_down"): (GEMM_SRC, 83878, 24621),
-               ("batch32", "gemm.qkv"): (GEMM_SRC, 43010, 36932),
+GEMM_SRC = ("conformer_speech_recognition_amd/csrc/gemm.hip", "fb2f0c092ff68645")
+ATTN_SRC = ("conformer_speech_recognition_amd/csrc/attention.hip", "58980960d82127a7")
+TRAFFIC_KIB = {("batch32", "gemm.ffn_up"): (GEMM_SRC, 41514, 49242),
+               ("batch32", "gemm.ffn_down"): (GEMM_SRC, 83884, 24621),
+               ("batch32", "gemm.qkv"): (GEMM_SRC, 42919, 36932),
                ("batch32", "gemm.pw1_glu"): (GEMM_SRC, 21270, 12310),
-               ("batch32", "gemm.out_proj"): (GEMM_SRC, 25739, 24621),
-               ("batch32", "gemm.pw2"): (GEMM_SRC, 25739, 24621),
-               ("batch32", "attention"): (ATTN_SRC, 34518, 12965)}
+               ("batch32", "gemm.out_proj"): (GEMM_SRC, 25743, 24621),
+               ("batch32", "gemm.pw2"): (GEMM_SRC, 25743, 24621),
+               ("batch32", "attention"): (ATTN_SRC, 34602, 12906)}
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 
 
