@@ -372,8 +372,9 @@ def debug_gemm(dtype: str, A, W, bias=None, scale=None, split: bool = False, str
     """C = A @ W.T + bias with the encoder's GEMM kernel (A, W device tensors in the
     storage type of ``dtype``; for 'w8f16' / 'w6f16' / 'w4f16' W is the packed uint8
     rows [N][K * bits / 8] of the header's layout, with fp16 ``scale`` [N][K / 64]).
-    With ``split`` the kernel may split the K sum as the encoder does for small batches;
-    returns (C, slices used)."""
+    With ``split`` a scratch buffer is passed: the kernel may split the K sum as the
+    encoder does for small batches, or (quantised weights, >= 2048 rows) expand the
+    weights to fp16 in it first; returns (C, slices used)."""
     import torch
     M, K = A.shape
     N = W.shape[0]

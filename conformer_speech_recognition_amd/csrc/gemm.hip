@@ -815,9 +815,61 @@ int gemm_split_slices(DType dt, int qbits, AMode am, Epi ep, const GemmParams& p
   return splitk_slices(p, tiles, KB, ep);
 }
 
+// Quantised weights with many rows of A: the weights are expanded once per call to fp16
+// rows [N][K] in the workspace (the fp16(q * s) values the register-staged kernel forms
+// while staging, one rounding each), and the LDS-DMA pipeline runs on them. One thread
+// per 16 weights of a row.
+template <int QB>
+__global__ void __launch_bounds__(256) k_dequant(GemmParams p, f16* __restrict__ out) {
+  const int cpr = p.K / 16;
+  const long e = (long)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (long)p.N * cpr) return;
+  const int n = (int)(e / cpr), k = (int)(e - (long)n * cpr) * 16;
+  const uint8_t* q = (const uint8_t*)p.W + ((long)n * p.ldw + k) * QB / 8;
+  u32x4 c;
+  if constexpr (QB == 8) c = *(const u32x4*)q;
+  else if constexpr (QB == 4) { const u32x2 v = *(const u32x2*)q; c = u32x4{v[0], v[1], 0, 0}; }
+  else c = u32x4{((const uint32_t*)q)[0], ((const uint32_t*)q)[1], ((const uint32_t*)q)[2], 0};
+  const float sc = (float)p.Wscale[(long)n * (p.K / 64) + k / 64];
+  u32x4 lo, hi;
+  dequant16<QB>(c, sc, lo, hi);
+  u32x4* o = (u32x4*)(out + (long)n * p.K + k);
+  o[0] = lo;
+  o[1] = hi;
+}
+
+// rows of A from which expanding the weights first pays (the pipelined tiles then fill the
+// chip; below it the register-staged kernel reads the packed weights directly)
+constexpr int kDequantMinRows = 2048;
+
+static bool dequant_first(int qbits, AMode am, Epi ep, const GemmParams& p) {
+  if (qbits == 0 || !p.part || p.M < kDequantMinRows || p.K % 64 != 0) return false;
+  if ((long)p.N * p.K * 2 > p.part_cap * 4) return false;
+  return direct_path(DT_F16, 0, am, ep, p);
+}
+
 hipError_t launch_gemm(DType dt, int qbits, AMode am, Epi ep, const GemmParams& p,
                        hipStream_t s) {
   if (p.M <= 0) return hipSuccess;
+  if ((dt == DT_W8F16 || dt == DT_W6F16 || dt == DT_W4F16) && dequant_first(qbits, am, ep, p)) {
+    if (am == A_DUAL && p.nsplit % 128 != 0) return hipErrorInvalidValue;
+    f16* wd = (f16*)p.part;
+    const long n = (long)p.N * (p.K / 16);
+    dim3 grid((unsigned)((n + 255) / 256));
+    if (qbits == 8) hipLaunchKernelGGL(k_dequant<8>, grid, dim3(256), 0, s, p, wd);
+    else if (qbits == 6) hipLaunchKernelGGL(k_dequant<6>, grid, dim3(256), 0, s, p, wd);
+    else if (qbits == 4) hipLaunchKernelGGL(k_dequant<4>, grid, dim3(256), 0, s, p, wd);
+    else return hipErrorInvalidValue;
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    GemmParams q = p;
+    q.W = wd;
+    q.ldw = p.K;
+    q.Wscale = nullptr;
+    q.part = nullptr;                 // the workspace now holds the weights: no split
+    q.part_cap = 0;
+    return run_dl_shape<f16>(am, ep, q, s);
+  }
   // fp32 A sources are native for the fp32 GEMM
   if (dt == DT_F32) {
     if (am == A_F32) am = A_PLAIN;

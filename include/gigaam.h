@@ -212,7 +212,10 @@ int gigaam_encode_stage(gigaam_model* model, const float* pcm_dev, const int32_t
  * NULL. With it the kernel splits the K sum across workgroups when the output tiles
  * alone fill less than half the GPU, as the encoder does for small batches: each slice
  * writes fp32 partials and a second kernel adds the slices in order and applies the
- * epilogue. slices_host (may be NULL) receives the number of K slices used (1: none).
+ * epilogue. For the quantised dtypes with at least 2048 rows of A, the scratch instead
+ * receives the weights expanded to fp16 (N * K * 2 bytes must fit), and the fp16 kernel
+ * runs on them, as the encoder does for large batches. slices_host (may be NULL)
+ * receives the number of K slices used (1: none).
  * K must be a multiple of 64 (32 for GIGAAM_F32). Errors: GIGAAM_E_INVAL, GIGAAM_E_HIP. */
 int gigaam_debug_gemm(int32_t dtype, int32_t M, int32_t N, int32_t K, const void* A_dev,
                       const void* W_dev, const void* scale_dev, const float* bias_dev,

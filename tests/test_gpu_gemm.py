@@ -90,3 +90,27 @@ def test_split_k_matches_float64(dtype, M, N, K):
           f"vs unsplit {np.abs(C - C1).max():.3e}", flush=True)
     assert ks > 1
     assert err <= bound and np.abs(C1 - ref).max() <= bound
+
+
+DEQUANT_SHAPES = [(2048, 768, 768), (2100, 3072, 768), (4096, 768, 3072)]
+
+
+@pytest.mark.parametrize("dtype", ["w8f16", "w6f16", "w4f16"])
+@pytest.mark.parametrize("M,N,K", DEQUANT_SHAPES)
+def test_dequantised_pipeline_matches_float64(dtype, M, N, K):
+    """Many rows of A with quantised weights and a workspace: the weights are expanded to
+    fp16 first and the pipelined fp16 kernel runs on them; same bound, and it agrees with
+    the register-staged kernel that reads the packed weights directly."""
+    import conformer_speech_recognition_amd as gg
+    print(f"[gemm dequant] {dtype} M={M} N={N} K={K}", flush=True)
+    A, W, S, bias, a, w, b = _operands(dtype, M, N, K, seed=M * 3 + N + K)
+    C, ks = gg.debug_gemm(dtype, A, W, bias=bias, scale=S, split=True)
+    C = C.cpu().numpy().astype(np.float64)
+    C1 = gg.debug_gemm(dtype, A, W, bias=bias, scale=S).cpu().numpy().astype(np.float64)
+    ref = a @ w.T + b
+    bound = 1e-6 * K * np.abs(a).max() * np.abs(w).max() + 1e-5
+    err = np.abs(C - ref).max()
+    print(f"[gemm dequant] {dtype} {M}x{N}x{K}: max|d| = {err:.3e} (bound {bound:.2e}), "
+          f"vs register-staged {np.abs(C - C1).max():.3e}", flush=True)
+    assert ks == 1
+    assert err <= bound and np.abs(C1 - ref).max() <= bound
