@@ -31,20 +31,38 @@ constexpr int FE_M = 64;      // mel bins
 __global__ void __launch_bounds__(FE_N) k_frontend_prep(const float* __restrict__ fb,
                                                         float* __restrict__ tw,
                                                         int* __restrict__ melr) {
+  __shared__ int lo_s[FE_M], hi_s[FE_M];
   const int i = threadIdx.x;
+  if (i < FE_M) {
+    lo_s[i] = FE_K;
+    hi_s[i] = -1;
+  }
   double sn, cs;
   sincospi(2.0 * i / FE_N, &sn, &cs);
   tw[i] = (float)cs;
   tw[FE_N + i] = (float)sn;
+  __syncthreads();
+  // every filterbank entry once (coalesced, all loads issued before any test); the first
+  // and last nonzero bin of each filter by LDS min / max (order-independent)
+  constexpr int PER = (FE_K * FE_M + FE_N - 1) / FE_N;
+  float v[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int e = i + j * FE_N;
+    v[j] = e < FE_K * FE_M ? fb[e] : 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int e = i + j * FE_N;
+    if (v[j] != 0.f) {
+      atomicMin(&lo_s[e % FE_M], e / FE_M);
+      atomicMax(&hi_s[e % FE_M], e / FE_M);
+    }
+  }
+  __syncthreads();
   if (i < FE_M) {
-    int lo = FE_K, hi = -1;
-    for (int k = 0; k < FE_K; ++k)
-      if (fb[k * FE_M + i] != 0.f) {
-        lo = k < lo ? k : lo;
-        hi = k;
-      }
-    melr[2 * i] = lo;
-    melr[2 * i + 1] = hi;
+    melr[2 * i] = lo_s[i];
+    melr[2 * i + 1] = hi_s[i];
   }
 }
 
@@ -54,10 +72,18 @@ __global__ void __launch_bounds__(256) k_frontend(const float* __restrict__ pcm,
                                                   const float* __restrict__ tw,
                                                   const int* __restrict__ melr, MetaDev m,
                                                   int T_tot, float* __restrict__ mel) {
-  __shared__ float xw[FE_FT][FE_N];
+  // one LDS region holds, in turn, the windowed frames, the stage-1 outputs and the power
+  // spectra (each stage reads its input into registers before the next is written), so
+  // four blocks fit on a CU
+  constexpr int ZP = 17;                          // row pitch of the stage-1 outputs
+  constexpr int ZSZ = FE_FT * 20 * ZP;
+  static_assert(FE_FT * FE_N <= 2 * ZSZ && FE_FT * (FE_K + 3) <= 2 * ZSZ, "LDS reuse");
+  __shared__ float region[2 * ZSZ];
   __shared__ float tc[FE_N], ts[FE_N];           // W320^j = tc[j] - i ts[j]
-  __shared__ float zr[FE_FT][20][17], zi[FE_FT][20][17];
-  __shared__ float P[FE_FT][FE_K + 3];
+  float (*xw)[FE_N] = (float (*)[FE_N])region;
+  float (*zr)[20][ZP] = (float (*)[20][ZP])region;
+  float (*zi)[20][ZP] = (float (*)[20][ZP])(region + ZSZ);
+  float (*P)[FE_K + 3] = (float (*)[FE_K + 3])region;
   const int tid = threadIdx.x;
   const int f0 = blockIdx.x * FE_FT;
 
@@ -78,11 +104,15 @@ __global__ void __launch_bounds__(256) k_frontend(const float* __restrict__ pcm,
   __syncthreads();
 
   // stage 1: thread (f, n2) -> 16-point DFT over n1, then the W320^(n2 k1) twiddle
+  const int f1 = tid / 20, n21 = tid - f1 * 20;
+  float x[16];
   if (tid < FE_FT * 20) {
-    const int f = tid / 20, n2 = tid - f * 20;
-    float x[16];
 #pragma unroll
-    for (int n1 = 0; n1 < 16; ++n1) x[n1] = xw[f][20 * n1 + n2];
+    for (int n1 = 0; n1 < 16; ++n1) x[n1] = xw[f1][20 * n1 + n21];
+  }
+  __syncthreads();                               // the frames are in registers: reuse
+  if (tid < FE_FT * 20) {
+    const int f = f1, n2 = n21;
 #pragma unroll
     for (int k1 = 0; k1 < 16; ++k1) {
       float yr = 0.f, yi = 0.f;
@@ -101,11 +131,15 @@ __global__ void __launch_bounds__(256) k_frontend(const float* __restrict__ pcm,
   __syncthreads();
 
   // stage 2: thread (f, k1) -> 20-point DFT over n2 for k2 = 0..10, power of bins <= 160
+  const int f2 = tid >> 4, k12 = tid & 15;
+  float ar[20], ai[20];
   if (tid < FE_FT * 16) {
-    const int f = tid >> 4, k1 = tid & 15;
-    float ar[20], ai[20];
 #pragma unroll
-    for (int n2 = 0; n2 < 20; ++n2) { ar[n2] = zr[f][n2][k1]; ai[n2] = zi[f][n2][k1]; }
+    for (int n2 = 0; n2 < 20; ++n2) { ar[n2] = zr[f2][n2][k12]; ai[n2] = zi[f2][n2][k12]; }
+  }
+  __syncthreads();                               // stage-1 outputs in registers: reuse
+  if (tid < FE_FT * 16) {
+    const int f = f2, k1 = k12;
 #pragma unroll
     for (int k2 = 0; k2 <= 10; ++k2) {
       const int k = k1 + 16 * k2;
