@@ -45,20 +45,23 @@ template <typename T> __device__ __forceinline__ u32x4 pack8f(const float* v) {
   return __builtin_bit_cast(u32x4, h);
 }
 
-// Column of key k (a multiple of 4) in a V^T row. The P operand of a lane in group g holds
-// keys 4g .. 4g + 3 and 16 + 4g .. 16 + 4g + 3 of each 32-key half; V^T rows store every
-// half as [4g .. 4g + 3 | 16 + 4g .. 16 + 4g + 3] for g = 0..3, so the lane's 8 keys are
-// one 16-byte LDS read (two 8-byte reads 32 bytes apart conflicted on half the banks).
-__device__ __forceinline__ int vcol(int k) {
-  const int w = k & 31;
-  return (k & ~31) + ((w & 15) >> 2) * 8 + (w >> 4) * 4;
+// gfx950 transposing LDS read (ds_read_b64_tr_b16). Inside each group of 16 lanes, lane
+// i = 4 s + q names 4 consecutive 16-bit elements (8 bytes); lane j of the group receives
+// element (j & 3) of the rows named by lanes j / 4, 4 + j / 4, 8 + j / 4 and 12 + j / 4, in
+// that order (measured on the device: lane j, slot s <- lane 4 s + j / 4, element j & 3).
+// So if lane 4 s + q points at V[key_s][d0 + 4 q .. d0 + 4 q + 3] of a row-major V tile,
+// lane j gets V[key_0..key_3][d0 + j]: four keys of one dimension, an MFMA A-operand half.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+template <typename T> __device__ __forceinline__ u32x2 lds_read_tr(const T* p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p)));
 }
 
 // ---------------------------------------------------------------- fp16 / bf16 kernel
-// K and V^T tiles are double-buffered in LDS: the next 64-key tile is loaded into
-// registers while the current one is consumed, and stored after it (one barrier per
-// tile). V is transposed in 4-key x 8-dim register blocks, written as 8-byte LDS stores
-// (16 consecutive lanes take 16 consecutive key blocks of one dim block: 32 distinct banks).
+// K and V tiles are double-buffered in LDS, both row-major (key, dim) copies of the global
+// rows: the next 64-key tile is loaded into registers while the current one is consumed,
+// and stored after it (one barrier per tile). The P.V product reads its V^T operand with
+// the transposing LDS read, so V is never transposed in registers.
 //
 // The softmax is kept in base 2 with the scale folded into one FMA per score:
 // p = 2^(s*c - m*c), c = log2(e)/sqrt(d_k), m the running max of the raw scores.  The
@@ -97,16 +100,17 @@ __device__ __forceinline__ float max_xor32(float v) {
 template <typename T, int DK>
 __global__ void __launch_bounds__(256) k_attn(AttnParams p) {
   constexpr int KP = DK + 8;         // LDS row pitch (elements) of K: 16 rows -> 16 bank groups
-  constexpr int VP = AT_KV + 8;      // LDS row pitch of V^T
+  // LDS row pitch of V: dims, then a column of ones and zeros up to DK + 16; 80 elements
+  // put the 8 rows one transposing read pass touches on disjoint banks
+  constexpr int VP = 80;
   constexpr int NDB = DK / 16;       // 16-wide dim blocks of the output
-  constexpr int NDBX = NDB + 1;      // + one block whose first V^T row is all ones: row sums
+  constexpr int NDBX = NDB + 1;      // + one block whose first column is all ones: row sums
   constexpr int CPR = DK / 8;        // 16-byte chunks per K / V row
-  constexpr int KCH = AT_KV * CPR;   // 16-byte K chunks per tile
-  constexpr int VBL = (AT_KV / 4) * CPR;       // 4-key x 8-dim V blocks per tile
-  constexpr int KPT = (KCH + 255) / 256;       // K chunks per thread
-  static_assert(VBL <= 256, "one V block per thread");
+  constexpr int KCH = AT_KV * CPR;   // 16-byte chunks per tile (each of K and V)
+  constexpr int KPT = (KCH + 255) / 256;       // chunks per thread
+  static_assert(DK + 16 <= VP, "V row pitch");
   __shared__ T sK[2][AT_KV][KP];
-  __shared__ T sVt[2][DK + 16][VP];
+  __shared__ __attribute__((aligned(16))) T sV[2][AT_KV][VP];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
@@ -130,21 +134,18 @@ __global__ void __launch_bounds__(256) k_attn(AttnParams p) {
   const u32x4 qa = *(const u32x4*)(qp + 8 * g);
   const u32x4 qb = hi_ok ? *(const u32x4*)(qp + 32 + 8 * g) : u32x4{0, 0, 0, 0};
 
-  // this thread's tile loads: 16-byte K chunks (e = tid + 256 i: key e / CPR, chunk e % CPR)
-  // and one V block (keys 4vq.. 4vq+3, dims 8vch.. 8vch+7), as raw buffer loads against a
-  // per-tile resource that ends at the clip's last row: rows past the clip read as zero
-  int koff[KPT], kls[KPT];            // global byte offset in the tile, LDS element offset
+  // this thread's tile loads: 16-byte K and V chunks (e = tid + 256 i: key e / CPR, chunk
+  // e % CPR), as raw buffer loads against a per-tile resource that ends at the clip's last
+  // row: rows past the clip read as zero
+  int koff[KPT], kls[KPT], vls[KPT];  // global byte offset in the tile, LDS element offsets
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
     const int e = tid + 256 * i, key = e / CPR, ch = e - key * CPR;
     koff[i] = (key * ld + ch * 8) * (int)sizeof(T);
     kls[i] = key * KP + ch * 8;
+    vls[i] = key * VP + ch * 8;
   }
-  const int vq = tid & 15, vch = tid >> 4;
-  const int voff = ((4 * vq) * ld + vch * 8) * (int)sizeof(T);
-  const int vstep = ld * (int)sizeof(T);
-  u32x4 rk[KPT];
-  u32x4 rv[4];
+  u32x4 rk[KPT], rv[KPT];
   auto load = [&](int kv0) {
     const int bytes = (U - kv0) * ld * (int)sizeof(T);
     const __amdgpu_buffer_rsrc_t rK =
@@ -153,31 +154,18 @@ __global__ void __launch_bounds__(256) k_attn(AttnParams p) {
         __builtin_amdgcn_make_buffer_rsrc((void*)(Vg + (long)kv0 * ld), 0, bytes, 0x00020000);
 #pragma unroll
     for (int i = 0; i < KPT; ++i)
-      if (KCH % 256 == 0 || tid + 256 * i < KCH)
+      if (KCH % 256 == 0 || tid + 256 * i < KCH) {
         rk[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rK, koff[i], 0, 0));
-    if (tid < VBL) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        rv[j] = __builtin_bit_cast(u32x4,
-                                   __builtin_amdgcn_raw_buffer_load_b128(rV, voff + j * vstep, 0, 0));
-    }
+        rv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rV, koff[i], 0, 0));
+      }
   };
   auto store = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i)
-      if (KCH % 256 == 0 || tid + 256 * i < KCH)
+      if (KCH % 256 == 0 || tid + 256 * i < KCH) {
         *(u32x4*)(&sK[buf][0][0] + kls[i]) = rk[i];
-    if (tid < VBL) {
-      typedef uint16_t h8 __attribute__((ext_vector_type(8)));
-      typedef uint16_t h4 __attribute__((ext_vector_type(4)));
-      const h8 v0 = __builtin_bit_cast(h8, rv[0]), v1 = __builtin_bit_cast(h8, rv[1]);
-      const h8 v2 = __builtin_bit_cast(h8, rv[2]), v3 = __builtin_bit_cast(h8, rv[3]);
-      // keys 4vq .. 4vq + 3 go to their permuted column (see vcol)
-      const int col = vcol(4 * vq);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        *(h4*)&sVt[buf][vch * 8 + i][col] = h4{v0[i], v1[i], v2[i], v3[i]};
-    }
+        *(u32x4*)(&sV[buf][0][0] + vls[i]) = rv[i];
+      }
   };
   // d_k = 48: the score MFMA's upper 16 k slots read the zero pad columns [48, 56) of the
   // K rows (set once here, never overwritten by the tile stores)
@@ -185,13 +173,16 @@ __global__ void __launch_bounds__(256) k_attn(AttnParams p) {
     *(u32x4*)&sK[tid / AT_KV][tid % AT_KV][DK] = u32x4{0, 0, 0, 0};
   const int khi = hi_ok ? 32 + 8 * g : DK;
 
-  // rows DK.. DK+15 of both V^T buffers: a row of ones then zeros, so that the P.V
+  // columns DK.. DK+15 of both V buffers: a column of ones then zeros, so that the P.V
   // product also accumulates each query's probability sum (in the rounded P the MFMA uses)
   {
-    const int vb = tid >> 7, row = (tid >> 3) & 15, col = (tid & 7) * 8;
-    const uint32_t one2 = row == 0 ? (uint32_t)__builtin_bit_cast(uint16_t, (T)1.0f) * 0x10001u : 0u;
-    *(u32x4*)&sVt[vb][DK + row][col] = u32x4{one2, one2, one2, one2};
+    const int vb = tid >> 7, key = (tid >> 1) & 63, half = tid & 1;
+    const uint32_t one = half == 0 ? (uint32_t)__builtin_bit_cast(uint16_t, (T)1.0f) : 0u;
+    *(u32x4*)&sV[vb][key][DK + 8 * half] = u32x4{one, 0u, 0u, 0u};
   }
+  // this lane's rows for the transposing V reads: lane 4 s + q of its 16-lane group names
+  // key 4 g + s (and 16 + 4 g + s) of a 32-key half, dims 4 q .. 4 q + 3 of a dim block
+  const int tr_key = 4 * g + (c16 >> 2), tr_dim = 4 * (c16 & 3);
   float m_run = -INFINITY;
   f32x4 o[NDBX];
 #pragma unroll
@@ -255,7 +246,10 @@ __global__ void __launch_bounds__(256) k_attn(AttnParams p) {
       const u32x4 pb = pack8f<T>(pp);
 #pragma unroll
       for (int db = 0; db < NDBX; ++db) {
-        o[db] = AttnMma<T>::k32(*(const u32x4*)&sVt[buf][db * 16 + c16][32 * hk + 8 * g], pb, o[db]);
+        // V^T rows db*16 + c16, keys 32 hk + 4 g + 0..3 and 32 hk + 16 + 4 g + 0..3
+        const u32x2 lo = lds_read_tr(&sV[buf][32 * hk + tr_key][db * 16 + tr_dim]);
+        const u32x2 hi = lds_read_tr(&sV[buf][32 * hk + 16 + tr_key][db * 16 + tr_dim]);
+        o[db] = AttnMma<T>::k32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb, o[db]);
       }
     }
     if (more) store(buf ^ 1);
