@@ -217,7 +217,9 @@ __global__ void __launch_bounds__(256) k_gemm(GemmParams p) {
   int tm, tn;
   tile_coords(blockIdx.x, (p.M + BM - 1) / BM, (p.N + BN - 1) / BN, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
-  const int KT = p.K / BKE;
+  // split-K: slice blockIdx.y takes k-tiles [kt0, kt0 + KT) and writes its own fp32 slice
+  const int KT = p.K / BKE / (int)gridDim.y, kt0 = (int)blockIdx.y * KT;
+  if (gridDim.y > 1) p.C = (float*)p.C + blockIdx.y * (long)p.M * p.ldc;
 
   const char* Abase = (const char*)((AM == A_DUAL && n0 >= p.nsplit) ? p.A2 : p.A);
 
@@ -332,14 +334,14 @@ __global__ void __launch_bounds__(256) k_gemm(GemmParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
 
-  load_tile(0);
+  load_tile(kt0);
   store_tile(0);
   __syncthreads();
 
   const int fr = lane & 31, fk = lane >> 5;
   for (int kt = 0; kt < KT; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < KT) load_tile(kt + 1);
+    if (kt + 1 < KT) load_tile(kt0 + kt + 1);
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
       u32x4 af[MI], bfr[NI];
@@ -643,8 +645,8 @@ __global__ void __launch_bounds__(64 * WGM * WGN, OCC) k_gemm_p(GemmParams p) {
 // dispatch
 
 template <typename T, int BM, int BN, int WGM, int WGN, int QB>
-static hipError_t run_epi(AMode am, Epi ep, const GemmParams& p, hipStream_t s) {
-  dim3 grid(((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN));
+static hipError_t run_epi(AMode am, Epi ep, const GemmParams& p, hipStream_t s, int ks = 1) {
+  dim3 grid(((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN), ks);
 #define GG_L(AMv, EPv)                                                                   \
   if (am == AMv && ep == EPv) {                                                          \
     hipLaunchKernelGGL((k_gemm<T, BM, BN, WGM, WGN, AMv, QB, EPv>), grid, dim3(256), 0, s, p); \
@@ -652,24 +654,19 @@ static hipError_t run_epi(AMode am, Epi ep, const GemmParams& p, hipStream_t s) 
   }
   if constexpr (QB != 0) {
     GG_L(A_PLAIN, E_SILU) GG_L(A_PLAIN, E_RESID) GG_L(A_DUAL, E_STORE) GG_L(A_PLAIN, E_GLU)
-    GG_L(A_PLAIN, E_F32)
+    GG_L(A_PLAIN, E_F32) GG_L(A_DUAL, E_F32)
   } else {
     GG_L(A_PLAIN, E_STORE) GG_L(A_PLAIN, E_SILU) GG_L(A_PLAIN, E_RESID) GG_L(A_DUAL, E_STORE)
     GG_L(A_PLAIN, E_GLU) GG_L(A_PLAIN, E_F32) GG_L(A_CONV, E_RELU_F32)
     if constexpr (sizeof(T) == 2) {
-      GG_L(A_F32, E_F32) GG_L(A_CONV_F32, E_RELU)
+      GG_L(A_F32, E_F32) GG_L(A_CONV_F32, E_RELU) GG_L(A_DUAL, E_F32) GG_L(A_CONV, E_F32)
+      GG_L(A_CONV_F32, E_F32)
     } else {
       GG_L(A_CONV, E_RELU)
     }
   }
 #undef GG_L
   return hipErrorInvalidValue;
-}
-
-template <typename T, int QB>
-static hipError_t run_tiles(AMode am, Epi ep, const GemmParams& p, hipStream_t s) {
-  if (p.N <= 512 && ep != E_GLU) return run_epi<T, 128, 64, 4, 1, QB>(am, ep, p, s);
-  return run_epi<T, 128, 128, 2, 2, QB>(am, ep, p, s);
 }
 
 // Split-K: out = epilogue(sum over slices of the fp32 partials + bias), the slices summed
@@ -704,7 +701,11 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(const float* __restrict__
 #pragma unroll
       for (int j = 0; j < 4; ++j) v[j] = siluf_(v[j]);
     }
-    if constexpr (EP == E_STORE || EP == E_SILU) {
+    if constexpr (EP == E_RELU || EP == E_RELU_F32) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = fmaxf(v[j], 0.f);
+    }
+    if constexpr (EP == E_STORE || EP == E_SILU || EP == E_RELU) {
       *(u32x2*)((T*)p.C + (long)row * p.ldc + co) = pack4<T>(v);
     } else if constexpr (EP == E_RESID) {
       f32x4* d = (f32x4*)((float*)p.C + (long)row * p.ldc + co);
@@ -737,9 +738,40 @@ static hipError_t run_splitk_reduce(Epi ep, int ks, const GemmParams& p, hipStre
     hipLaunchKernelGGL((k_splitk_reduce<T, EPv>), grid, dim3(256), 0, s, p.part, ks, p); \
     return hipGetLastError();                                                          \
   }
-  GG_R(E_STORE) GG_R(E_SILU) GG_R(E_RESID) GG_R(E_GLU) GG_R(E_F32)
+  GG_R(E_STORE) GG_R(E_SILU) GG_R(E_RESID) GG_R(E_GLU) GG_R(E_F32) GG_R(E_RELU) GG_R(E_RELU_F32)
 #undef GG_R
   return hipErrorInvalidValue;
+}
+
+// The register-staged kernel (fp32, quantised weights, the implicit convs): with few output
+// tiles the K sum is split as in the direct path (16-bit models, which bring a workspace).
+static void tiles_geometry(Epi ep, const GemmParams& p, int& BM, int& BN) {
+  if (p.N <= 512 && ep != E_GLU) { BM = 128; BN = 64; }
+  else { BM = 128; BN = 128; }
+}
+
+template <typename T, int QB>
+static hipError_t run_tiles(AMode am, Epi ep, const GemmParams& p, hipStream_t s) {
+  int BM, BN;
+  tiles_geometry(ep, p, BM, BN);
+  const long tiles = (long)((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+  auto go = [&](Epi e, const GemmParams& q, int k) {
+    if (BN == 64) return run_epi<T, 128, 64, 4, 1, QB>(am, e, q, s, k);
+    return run_epi<T, 128, 128, 2, 2, QB>(am, e, q, s, k);
+  };
+  if constexpr (sizeof(T) == 2) {
+    const int ks = splitk_slices(p, tiles, 64, ep);
+    if (ks > 1) {
+      GemmParams q = p;
+      q.C = p.part;
+      q.ldc = p.N;
+      q.bias = nullptr;
+      const hipError_t e = go(E_F32, q, ks);
+      if (e != hipSuccess) return e;
+      return run_splitk_reduce<T>(ep, ks, p, s);
+    }
+  }
+  return go(ep, p, 1);
 }
 
 template <typename T, int BM, int BN, int WGM, int WGN, int S, int KB, int OCC>
@@ -785,20 +817,45 @@ static hipError_t run_dl(AMode am, Epi ep, const GemmParams& p, hipStream_t s) {
 //     64 k (144 KiB, one workgroup per CU: half the barriers of 32-k tiles, 59.9 -> 54.5 us);
 //   outputs of at most 1024 columns with K <= 1024 (out-proj, pointwise-2): 128 x 128
 //     tiles, 2 stages of 64 k, two workgroups per CU.
+// With few rows (a clip or two, a streaming window) the large tiles leave most of the chip
+// idle: when one of them would give fewer than 128 tiles, the 128 x 128 shape is used
+// (then split-K on top when even those are few).
+static long tile_count(const GemmParams& p, int BM, int BN) {
+  return (long)((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+}
+constexpr long kNarrowBelow = 160;
+enum DlShape { DL_WIDE, DL_DUAL, DL_LONGK, DL_NARROW };
+static DlShape dl_shape(AMode am, const GemmParams& p) {
+  DlShape sh = DL_NARROW;
+  if (p.N > 1024 && am != A_DUAL) sh = DL_WIDE;
+  else if (p.N > 1024) sh = DL_DUAL;
+  else if (p.K > 1024) sh = DL_LONGK;
+  if (sh == DL_WIDE && tile_count(p, 256, 256) * splitk_slices(p, tile_count(p, 256, 256), 64, E_STORE) < kNarrowBelow)
+    sh = DL_NARROW;
+  if (sh == DL_DUAL && tile_count(p, 256, 128) * splitk_slices(p, tile_count(p, 256, 128), 32, E_STORE) < kNarrowBelow)
+    sh = DL_NARROW;
+  if (sh == DL_LONGK && tile_count(p, 256, 128) * splitk_slices(p, tile_count(p, 256, 128), 64, E_STORE) < kNarrowBelow)
+    sh = DL_NARROW;
+  return sh;
+}
 // Geometry {BM, BN, KB} of each, for the split-K planning:
 static void dl_geometry(AMode am, const GemmParams& p, int& BM, int& BN, int& KB) {
-  if (p.N > 1024 && am != A_DUAL) { BM = 256; BN = 256; KB = 64; }
-  else if (p.N > 1024) { BM = 256; BN = 128; KB = 32; }
-  else if (p.K > 1024) { BM = 256; BN = 128; KB = 64; }
-  else { BM = 128; BN = 128; KB = 64; }
+  switch (dl_shape(am, p)) {
+    case DL_WIDE: BM = 256; BN = 256; KB = 64; break;
+    case DL_DUAL: BM = 256; BN = 128; KB = 32; break;
+    case DL_LONGK: BM = 256; BN = 128; KB = 64; break;
+    default: BM = 128; BN = 128; KB = 64; break;
+  }
 }
 
 template <typename T>
 static hipError_t run_dl_shape(AMode am, Epi ep, const GemmParams& p, hipStream_t s) {
-  if (p.N > 1024 && am != A_DUAL) return run_dl<T, 256, 256, 4, 2, 2, 64, 1>(am, ep, p, s);
-  if (p.N > 1024) return run_dl<T, 256, 128, 4, 2, 3, 32, 2>(am, ep, p, s);
-  if (p.K > 1024) return run_dl<T, 256, 128, 4, 2, 3, 64, 1>(am, ep, p, s);
-  return run_dl<T, 128, 128, 4, 2, 2, 64, 2>(am, ep, p, s);
+  switch (dl_shape(am, p)) {
+    case DL_WIDE: return run_dl<T, 256, 256, 4, 2, 2, 64, 1>(am, ep, p, s);
+    case DL_DUAL: return run_dl<T, 256, 128, 4, 2, 3, 32, 2>(am, ep, p, s);
+    case DL_LONGK: return run_dl<T, 256, 128, 4, 2, 3, 64, 1>(am, ep, p, s);
+    default: return run_dl<T, 128, 128, 4, 2, 2, 64, 2>(am, ep, p, s);
+  }
 }
 
 static bool direct_path(DType dt, int qbits, AMode am, Epi ep, const GemmParams& p) {
@@ -807,13 +864,6 @@ static bool direct_path(DType dt, int qbits, AMode am, Epi ep, const GemmParams&
          (am == A_PLAIN || ep == E_STORE);
 }
 
-int gemm_split_slices(DType dt, int qbits, AMode am, Epi ep, const GemmParams& p) {
-  if (!direct_path(dt, qbits, am, ep, p)) return 1;
-  int BM, BN, KB;
-  dl_geometry(am, p, BM, BN, KB);
-  const long tiles = (long)((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-  return splitk_slices(p, tiles, KB, ep);
-}
 
 // Quantised weights with many rows of A: the weights are expanded once per call to fp16
 // rows [N][K] in the workspace (the fp16(q * s) values the register-staged kernel forms
@@ -846,6 +896,19 @@ static bool dequant_first(int qbits, AMode am, Epi ep, const GemmParams& p) {
   if (qbits == 0 || !p.part || p.M < kDequantMinRows || p.K % 64 != 0) return false;
   if ((long)p.N * p.K * 2 > p.part_cap * 4) return false;
   return direct_path(DT_F16, 0, am, ep, p);
+}
+
+int gemm_split_slices(DType dt, int qbits, AMode am, Epi ep, const GemmParams& p) {
+  if (dt == DT_F32) return 1;
+  if (qbits != 0 && dequant_first(qbits, am, ep, p)) return 1;
+  if (!direct_path(dt, qbits, am, ep, p)) {           // the register-staged kernel
+    int BM, BN;
+    tiles_geometry(ep, p, BM, BN);
+    return splitk_slices(p, tile_count(p, BM, BN), 64, ep);
+  }
+  int BM, BN, KB;
+  dl_geometry(am, p, BM, BN, KB);
+  return splitk_slices(p, tile_count(p, BM, BN), KB, ep);
 }
 
 hipError_t launch_gemm(DType dt, int qbits, AMode am, Epi ep, const GemmParams& p,

@@ -52,14 +52,15 @@ Profiler g_prof;
 }  // namespace
 
 // Launch `expr` (a hipError_t expression), timing it when the profiler is on.
+// (profiling is best effort: a launch whose events fail to record is simply not timed)
 #define LAUNCH(name, expr)                                                              \
   do {                                                                                  \
-    hipEvent_t a_ = nullptr;                                                            \
-    if (g_prof.on && (a_ = g_prof.next())) hipEventRecord(a_, s);                       \
+    hipEvent_t a_ = g_prof.on ? g_prof.next() : nullptr;                                \
+    if (a_ && hipEventRecord(a_, s) != hipSuccess) a_ = nullptr;                        \
     HIP_TRY(expr);                                                                      \
     if (a_) {                                                                           \
       hipEvent_t b_ = g_prof.next();                                                    \
-      if (b_) { hipEventRecord(b_, s); g_prof.recs.push_back({name, a_, b_}); }         \
+      if (b_ && hipEventRecord(b_, s) == hipSuccess) g_prof.recs.push_back({name, a_, b_}); \
     }                                                                                   \
   } while (0)
 
