@@ -72,11 +72,12 @@ SPLIT_SHAPES = [(25, 768, 3072), (500, 768, 3072), (77, 2304, 768), (300, 768, 7
                 (130, 3072, 768)]
 
 
-@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "w8f16", "w6f16", "w4f16"])
 @pytest.mark.parametrize("M,N,K", SPLIT_SHAPES)
 def test_split_k_matches_float64(dtype, M, N, K):
     """Small M: the K sum split across workgroups (fp32 partials added in slice order by a
-    second kernel) meets the same bound, and the unsplit kernel agrees with it."""
+    second kernel) meets the same bound, and the unsplit kernel agrees with it (for the
+    quantised weights the split runs in the register-staged kernel)."""
     import conformer_speech_recognition_amd as gg
     print(f"[gemm split] {dtype} M={M} N={N} K={K}", flush=True)
     A, W, S, bias, a, w, b = _operands(dtype, M, N, K, seed=M * 5 + N + K)
