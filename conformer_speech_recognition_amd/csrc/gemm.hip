@@ -716,6 +716,13 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(const float* __restrict__
   }
 }
 
+// Residual GEMMs whose split-K sum the next kernel adds (the LayerNorm that reads x):
+// launch_gemm's caller passes where to report the slices; the reduce launch is skipped. Only
+// up to kDeferMaxSlices: the LayerNorm has one wave per row, and adding 8 slices there was
+// slower than the reduce kernel's wider grid (a 20 s clip's FFN-down splits 8 ways).
+static thread_local int* g_defer_ks = nullptr;
+constexpr int kDeferMaxSlices = 4;
+
 // Slices for a launch of `tiles` workgroups over K (k-tile KB): only when the tiles fill
 // less than half the chip, at most 8 slices of at least two k-tiles, tiles * slices <= 256.
 static int splitk_slices(const GemmParams& p, long tiles, int KB, Epi ep) {
@@ -768,6 +775,7 @@ static hipError_t run_tiles(AMode am, Epi ep, const GemmParams& p, hipStream_t s
       q.bias = nullptr;
       const hipError_t e = go(E_F32, q, ks);
       if (e != hipSuccess) return e;
+      if (g_defer_ks && ep == E_RESID && ks <= kDeferMaxSlices) { *g_defer_ks = ks; return hipSuccess; }
       return run_splitk_reduce<T>(ep, ks, p, s);
     }
   }
@@ -793,6 +801,7 @@ static hipError_t run_dl(AMode am, Epi ep, const GemmParams& p, hipStream_t s) {
       hipLaunchKernelGGL((k_gemm_p<T, BM, BN, WGM, WGN, S, KB, A_PLAIN, E_F32, OCC>), grid, blk, 0, s, q);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (g_defer_ks && ep == E_RESID && ks <= kDeferMaxSlices) { *g_defer_ks = ks; return hipSuccess; }
     return run_splitk_reduce<T>(ep, ks, p, s);
   }
   dim3 grid((unsigned)tiles);
@@ -911,8 +920,20 @@ int gemm_split_slices(DType dt, int qbits, AMode am, Epi ep, const GemmParams& p
   return splitk_slices(p, tile_count(p, BM, BN), KB, ep);
 }
 
-hipError_t launch_gemm(DType dt, int qbits, AMode am, Epi ep, const GemmParams& p,
-                       hipStream_t s) {
+static hipError_t launch_gemm_impl(DType dt, int qbits, AMode am, Epi ep, const GemmParams& p,
+                                   hipStream_t s);
+
+hipError_t launch_gemm(DType dt, int qbits, AMode am, Epi ep, const GemmParams& p, hipStream_t s,
+                       int* deferred_ks) {
+  if (deferred_ks) *deferred_ks = 0;
+  g_defer_ks = ep == E_RESID ? deferred_ks : nullptr;
+  const hipError_t e = launch_gemm_impl(dt, qbits, am, ep, p, s);
+  g_defer_ks = nullptr;
+  return e;
+}
+
+static hipError_t launch_gemm_impl(DType dt, int qbits, AMode am, Epi ep, const GemmParams& p,
+                                   hipStream_t s) {
   if (p.M <= 0) return hipSuccess;
   if ((dt == DT_W8F16 || dt == DT_W6F16 || dt == DT_W4F16) && dequant_first(qbits, am, ep, p)) {
     if (am == A_DUAL && p.nsplit % 128 != 0) return hipErrorInvalidValue;

@@ -675,13 +675,15 @@ int run(gigaam_model* m, const float* pcm, const int32_t* lengths, int32_t B, in
     HIP_TRY(hipMemcpyAsync(stage_out, src, n * 4, hipMemcpyDeviceToDevice, s));
     return GIGAAM_OK;
   };
-  auto G = [&](const char* name, AMode am, Epi ep, int wq, const GemmParams& gp) -> int {
+  // defer: a residual GEMM whose split-K slices (if it splits) the next LayerNorm adds
+  auto G = [&](const char* name, AMode am, Epi ep, int wq, const GemmParams& gp,
+               int* defer = nullptr) -> int {
     GemmParams q = gp;
     if (c.dtype != GIGAAM_F32) {
       q.part = (float*)(W + w.part);
       q.part_cap = kSplitPartFloats;
     }
-    LAUNCH(name, launch_gemm(dt, wq, am, ep, q, s));
+    LAUNCH(name, launch_gemm(dt, wq, am, ep, q, s, stage == STAGE_NONE ? defer : nullptr));
     return GIGAAM_OK;
   };
   auto lin = [&](const Lin& l, int M, int N, int K, const void* A, int lda, void* Cp, int ldc,
@@ -713,11 +715,13 @@ int run(gigaam_model* m, const float* pcm, const int32_t* lengths, int32_t B, in
   std::memset(&ln, 0, sizeof ln);
   ln.rows = U_tot; ln.d = d; ln.x = x; ln.eps = c.ln_eps;
   ln.cos_t = cos_t; ln.sin_t = sin_t; ln.rowclip = md.rowU; ln.cu = md.cuU;
+  // ks / rb / ra: a preceding residual GEMM's deferred split-K slices, its bias and scale
   auto LN = [&](LnMode mode, size_t g1, size_t b1, const float* g2, const float* b2, void* yo,
-                void* ro) -> int {
+                void* ro, int ks = 0, const float* rb = nullptr, float ra = 1.f) -> int {
     LnParams q = ln;
     q.g1 = (const float*)(P + g1); q.b1 = (const float*)(P + b1);
     q.g2 = g2; q.b2 = b2; q.y = yo; q.r = ro;
+    if (ks > 0) { q.rpart = (const float*)(W + w.part); q.rks = ks; q.rbias = rb; q.ralpha = ra; }
     LAUNCH(mode == LN_ROPE ? "layernorm_rope" : mode == LN_TWO ? "layernorm_two" : "layernorm",
            launch_layernorm(dt, mode, q, s));
     return GIGAAM_OK;
@@ -733,37 +737,39 @@ int run(gigaam_model* m, const float* pcm, const int32_t* lengths, int32_t B, in
     const int tap = 1000 + 10 * li;
     // a5 FFN1 (half step)
     if ((rc = G("gemm.ffn_up", A_PLAIN, E_SILU, o.ff1_1.qb, lin(o.ff1_1, U_tot, f, d, y, d, hid, f)))) return rc;
-    if ((rc = G("gemm.ffn_down", A_PLAIN, E_RESID, o.ff1_2.qb, lin(o.ff1_2, U_tot, d, f, hid, f, x, d, 0.5f)))) return rc;
+    int dks = 0;      // split-K slices of the last residual GEMM left for the next LayerNorm
+    if ((rc = G("gemm.ffn_down", A_PLAIN, E_RESID, o.ff1_2.qb, lin(o.ff1_2, U_tot, d, f, hid, f, x, d, 0.5f), &dks))) return rc;
     if (stage == tap + 0) return copy_out(x, (size_t)U_tot * d);
     // a6-a9 attention: LN + rope(y) -> [Q|K] from r, V from y -> flash attention -> out proj
-    if ((rc = LN(LN_ROPE, o.att_g, o.att_b, nullptr, nullptr, y, r))) return rc;
+    if ((rc = LN(LN_ROPE, o.att_g, o.att_b, nullptr, nullptr, y, r, dks, (const float*)(P + o.ff1_2.b), 0.5f))) return rc;
     {
       GemmParams gq = lin(o.qkv, U_tot, 3 * d, d, r, d, qkv, 3 * d);
       gq.A2 = y; gq.nsplit = 2 * d;
       if ((rc = G("gemm.qkv", A_DUAL, E_STORE, o.qkv.qb, gq))) return rc;
     }
     LAUNCH("attention", launch_attention(dt, dk, ap, s));
-    if ((rc = G("gemm.out_proj", A_PLAIN, E_RESID, o.out.qb, lin(o.out, U_tot, d, d, ao, d, x, d)))) return rc;
+    if ((rc = G("gemm.out_proj", A_PLAIN, E_RESID, o.out.qb, lin(o.out, U_tot, d, d, ao, d, x, d), &dks))) return rc;
     if (stage == tap + 1) return copy_out(x, (size_t)U_tot * d);
     // a10-a12 conv module
-    if ((rc = LN(LN_PLAIN, o.cv_g, o.cv_b, nullptr, nullptr, y, nullptr))) return rc;
+    if ((rc = LN(LN_PLAIN, o.cv_g, o.cv_b, nullptr, nullptr, y, nullptr, dks, (const float*)(P + o.out.b)))) return rc;
     if ((rc = G("gemm.pw1_glu", A_PLAIN, E_GLU, o.pw1.qb, lin(o.pw1, U_tot, 2 * d, d, y, d, hid, d)))) return rc;
     dp.w = (const float*)(P + o.dw_w); dp.b = (const float*)(P + o.dw_b);
     dp.bn_g = (const float*)(P + o.bn_g); dp.bn_b = (const float*)(P + o.bn_b);
     dp.bn_m = (const float*)(P + o.bn_m); dp.bn_v = (const float*)(P + o.bn_v);
     LAUNCH("dwconv_bn_silu", launch_dwconv(dt, c.conv_kernel, dp, s));
-    if ((rc = G("gemm.pw2", A_PLAIN, E_RESID, o.pw2.qb, lin(o.pw2, U_tot, d, d, hid2, d, x, d)))) return rc;
+    if ((rc = G("gemm.pw2", A_PLAIN, E_RESID, o.pw2.qb, lin(o.pw2, U_tot, d, d, hid2, d, x, d), &dks))) return rc;
     if (stage == tap + 2) return copy_out(x, (size_t)U_tot * d);
     // a13 FFN2 (half step) + final norm fused with the next block's first pre-norm
-    if ((rc = LN(LN_PLAIN, o.ff2_g, o.ff2_b, nullptr, nullptr, y, nullptr))) return rc;
+    if ((rc = LN(LN_PLAIN, o.ff2_g, o.ff2_b, nullptr, nullptr, y, nullptr, dks, (const float*)(P + o.pw2.b)))) return rc;
     if ((rc = G("gemm.ffn_up", A_PLAIN, E_SILU, o.ff2_1.qb, lin(o.ff2_1, U_tot, f, d, y, d, hid, f)))) return rc;
-    if ((rc = G("gemm.ffn_down", A_PLAIN, E_RESID, o.ff2_2.qb, lin(o.ff2_2, U_tot, d, f, hid, f, x, d, 0.5f)))) return rc;
+    if ((rc = G("gemm.ffn_down", A_PLAIN, E_RESID, o.ff2_2.qb, lin(o.ff2_2, U_tot, d, f, hid, f, x, d, 0.5f), &dks))) return rc;
     if (stage == tap + 3) return copy_out(x, (size_t)U_tot * d);
+    const float* rb2 = (const float*)(P + o.ff2_2.b);
     if (li + 1 < c.n_layers) {
       const LayerOff& nx = L.layers[li + 1];
-      if ((rc = LN(LN_TWO, o.no_g, o.no_b, (const float*)(P + nx.ff1_g), (const float*)(P + nx.ff1_b), y, nullptr))) return rc;
+      if ((rc = LN(LN_TWO, o.no_g, o.no_b, (const float*)(P + nx.ff1_g), (const float*)(P + nx.ff1_b), y, nullptr, dks, rb2, 0.5f))) return rc;
     } else {
-      if ((rc = LN(LN_TWO, o.no_g, o.no_b, nullptr, nullptr, nullptr, nullptr))) return rc;
+      if ((rc = LN(LN_TWO, o.no_g, o.no_b, nullptr, nullptr, nullptr, nullptr, dks, rb2, 0.5f))) return rc;
     }
     if (stage == GIGAAM_STAGE_LAYER + li) return copy_out(x, (size_t)U_tot * d);
   }

@@ -44,9 +44,11 @@ struct GemmParams {
 constexpr long kSplitPartFloats = 256L * 256 * 128;
 
 // qbits: 0 = weights stored in the operand type; 8 / 6 / 4 = packed quantised rows with
-// fp16 group scales (dequantised to fp16 in the kernel)
+// fp16 group scales (dequantised to fp16 in the kernel). deferred_ks (E_RESID only, may be
+// nullptr): when the K sum is split, the slices are left in p.part, their number is written
+// here and the caller's next kernel must add them (LnParams.rks); 0 when nothing is deferred.
 hipError_t launch_gemm(DType dt, int qbits, AMode am, Epi ep, const GemmParams& p,
-                       hipStream_t s);
+                       hipStream_t s, int* deferred_ks = nullptr);
 // K slices launch_gemm uses for these arguments (1: no split)
 int gemm_split_slices(DType dt, int qbits, AMode am, Epi ep, const GemmParams& p);
 
@@ -75,6 +77,9 @@ struct LnParams {
   const float* cos_t; const float* sin_t;  // [U_max][d_k/2]
   const int* rowclip; const int* cu;       // encoder-space clip map (for positions)
   float eps;
+  // a residual GEMM's deferred split-K sum, added to x first: x += ralpha * (sum of the rks
+  // slices of rpart [rks][rows][d] in slice order + rbias); rks = 0: none
+  const float* rpart; const float* rbias; int rks; float ralpha;
 };
 hipError_t launch_layernorm(DType dt, LnMode mode, const LnParams& p, hipStream_t s);
 hipError_t launch_rope_table(float* cos_t, float* sin_t, int n_pos, int dk, float base,

@@ -132,6 +132,28 @@ __global__ void __launch_bounds__(256) k_ln(LnParams p) {
       for (int j = 0; j < 4; ++j) v[r][4 * i + j] = q[j];
     }
   }
+  if (p.rks > 0) {
+    // the preceding residual GEMM's split K sum: x += ralpha * (slices in order + bias), the
+    // reduce step of that GEMM done here, and x written back unless the LayerNorm overwrites it
+    const long slice = (long)p.rows * D;
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      if (row0 + r >= p.rows) continue;
+      const long off = (long)(row0 + r) * D + 4 * lane;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        f32x4 a = *(const f32x4*)(p.rpart + off + 256 * i);
+        for (int k = 1; k < p.rks; ++k) a += *(const f32x4*)(p.rpart + off + 256 * i + k * slice);
+        const f32x4 b = p.rbias ? *(const f32x4*)(p.rbias + 256 * i + 4 * lane) : f32x4{0.f, 0.f, 0.f, 0.f};
+        const f32x4 sum = a + b;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[r][4 * i + j] = v[r][4 * i + j] + p.ralpha * sum[j];
+        if constexpr (MODE != LN_TWO)
+          *(f32x4*)(p.x + off + 256 * i) =
+              f32x4{v[r][4 * i], v[r][4 * i + 1], v[r][4 * i + 2], v[r][4 * i + 3]};
+      }
+    }
+  }
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
     cv[r] = 0.f;
