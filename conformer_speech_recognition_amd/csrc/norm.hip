@@ -111,7 +111,7 @@ __device__ __forceinline__ void ln_finish(const LnParams& p, float (&v)[4 * NI],
 // One wave per RPW consecutive rows: every row's loads (and, for RoPE, its cos / sin
 // entries, a chain of three dependent loads) are issued before the first row's statistics,
 // so a wave keeps RPW rows of reads in flight and the grid fits the chip in one round.
-template <typename T, int NI, int MODE, int RPW>
+template <typename T, int NI, int MODE, int RPW, bool RES>
 __global__ void __launch_bounds__(256) k_ln(LnParams p) {
   constexpr int D = NI * 256;
   constexpr int DK = D / 16, HALF = DK / 2;
@@ -132,7 +132,7 @@ __global__ void __launch_bounds__(256) k_ln(LnParams p) {
       for (int j = 0; j < 4; ++j) v[r][4 * i + j] = q[j];
     }
   }
-  if (p.rks > 0) {
+  if constexpr (RES) {
     // the preceding residual GEMM's split K sum: x += ralpha * (slices in order + bias), the
     // reduce step of that GEMM done here, and x written back unless the LayerNorm overwrites it
     const long slice = (long)p.rows * D;
@@ -177,7 +177,10 @@ __global__ void __launch_bounds__(256) k_ln(LnParams p) {
 template <typename T, int NI, int MODE, int RPW>
 static void ln_launch(const LnParams& p, hipStream_t s) {
   dim3 grid((p.rows + 4 * RPW - 1) / (4 * RPW));
-  hipLaunchKernelGGL((k_ln<T, NI, MODE, RPW>), grid, dim3(256), 0, s, p);
+  // the deferred-residual variant is its own instantiation: its stores to x would otherwise
+  // keep the plain kernel's parameter loads from being hoisted
+  if (p.rks > 0) hipLaunchKernelGGL((k_ln<T, NI, MODE, RPW, true>), grid, dim3(256), 0, s, p);
+  else hipLaunchKernelGGL((k_ln<T, NI, MODE, RPW, false>), grid, dim3(256), 0, s, p);
 }
 
 template <typename T, int NI>
