@@ -38,7 +38,7 @@ PEAK_HBM_GBS = 8000.0
 # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch) on this
 # bench, scaled by what the counters read for a plain copy of known size; valid only while the
 # kernel's source is the one the counters were taken on (sha256 prefix)
-GEMM_SRC = ("conformer_speech_recognition_amd/csrc/gemm.hip", "980d5cedfaccccd1")
+GEMM_SRC = ("conformer_speech_recognition_amd/csrc/gemm.hip", "179c7de6692995ef")
 ATTN_SRC = ("conformer_speech_recognition_amd/csrc/attention.hip", "95db4798160df9cc")
 TRAFFIC_KIB = {("batch32", "gemm.ffn_up"): (GEMM_SRC, 41514, 49242),
                ("batch32", "gemm.ffn_down"): (GEMM_SRC, 83884, 24621),
@@ -81,6 +81,7 @@ def role_flops(cfg, lens):
         "gemm.conv2": 2 * U * 5 * d * d,
         "gemm.ffn_up": 2 * U * d * f,
         "gemm.ffn_down": 2 * U * f * d,
+        "mlp_fused": 4 * U * d * f,            # both FFN GEMMs in one kernel (few rows)
         "gemm.qkv": 2 * U * d * 3 * d,
         "gemm.out_proj": 2 * U * d * d,
         "gemm.pw1_glu": 2 * U * d * 2 * d,
@@ -258,7 +259,49 @@ def sweep_leg(model, reps=5):
     for b in (1, 2, 4, 8, 16, 32, 64):
         clips = [synth.make_signal(np.random.default_rng(100 + i), 320000) for i in range(b)]
         batch[str(b)] = rate(clips)
-    return {"unit": "audio-s/s", "chunk_len_300s_signal": chunk, "batch_of_20s_clips": batch}
+    return {"unit": "audio-s/s", "chunk_len_300s_signal": chunk, "batch_of_20s_clips": batch,
+            "fused_mlp": mlp_variant()}
+
+
+def mlp_variant(reps=64, sets=32):
+    """The fused few-row FFN (d 768, f 3072, hidden activations kept on chip) against the same
+    two products as separate split-K GEMMs through HBM, per FFN call, at 25 / 64 / 500 / 896 rows
+    (25: one second of audio, 500: one 20 s clip). Calls rotate over `sets` weight sets (302 MB,
+    more than the 256 MB last-level cache), so the weights come from HBM as in an encode; each
+    call is issued from Python, so the few-row figures include the binding's per-call cost."""
+    import torch
+    import conformer_speech_recognition_amd as gg
+    st = torch.cuda.current_stream()
+    g = torch.Generator(device="cuda").manual_seed(71)
+    w1 = [(0.05 * torch.randn(3072, 768, device="cuda", generator=g)).half() for _ in range(sets)]
+    w2 = [(0.05 * torch.randn(768, 3072, device="cuda", generator=g)).half() for _ in range(sets)]
+    b1 = torch.randn(3072, device="cuda", generator=g)
+    b2 = torch.randn(768, device="cuda", generator=g)
+    out = {}
+    for M in (25, 64, 500, 896):
+        y = torch.randn(M, 768, device="cuda", generator=g).half()
+        x = torch.zeros(M, 768, device="cuda")
+        h = gg.debug_gemm("f16", y, w1[0], b1, split=True)[0].half()
+
+        def timed(fn):
+            for i in range(3):
+                fn(i % sets)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(st)
+            for i in range(reps):
+                fn(i % sets)
+            e1.record(st)
+            e1.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / reps
+
+        fused = timed(lambda i: gg.debug_mlp("f16", y, w1[i], b1, w2[i], b2, x))
+        two = timed(lambda i: (gg.debug_gemm("f16", y, w1[i], b1, split=True),
+                               gg.debug_gemm("f16", h, w2[i], b2, split=True)))
+        out[str(M)] = {"fused_us": round(fused, 1), "two_gemms_us": round(two, 1),
+                       "fused_tflops": round(4 * M * 768 * 3072 / (fused * 1e-6) / 1e12, 1)}
+    del w1, w2
+    return out
 
 
 def main():
@@ -338,7 +381,7 @@ def main():
     rb = role_bytes(cfg, lens)
     dom = max(prof, key=lambda r: r["total_ms"])
     name = dom["name"]
-    if name in rf and (name.startswith("gemm") or name == "attention"):
+    if name in rf and (name.startswith("gemm") or name in ("attention", "mlp_fused")):
         achieved = rf[name] / (dom["avg_us"] * 1e-6) / 1e12
         peak = PEAK_TFLOPS[cfg["dtype"]]
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",

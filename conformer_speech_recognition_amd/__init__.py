@@ -105,6 +105,8 @@ _SIGNATURES = {
     "gigaam_encode_stage": (ctypes.c_int, [_P, _P, _IP, _I, _I, _P, _SZ, _I, _P, _SZ, _P]),
     "gigaam_debug_gemm": (ctypes.c_int, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _SZ, _IP, _P]),
     "gigaam_debug_attention": (ctypes.c_int, [_I, _I, _I, _I, _IP, _P, _P, _P, _SZ, _P]),
+    "gigaam_debug_mlp": (ctypes.c_int, [_I, _I, _I, _I, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P,
+                                        _SZ, _P]),
     "gigaam_rnnt_check_config": (ctypes.c_int, [ctypes.POINTER(RnntConfig)]),
     "gigaam_rnnt_canonical_count": (ctypes.c_int, [ctypes.POINTER(RnntConfig), _IP, ctypes.POINTER(_SZ)]),
     "gigaam_rnnt_canonical_entry": (ctypes.c_int, [ctypes.POINTER(RnntConfig), _I, ctypes.c_char_p, _I,
@@ -386,6 +388,21 @@ def debug_gemm(dtype: str, A, W, bias=None, scale=None, split: bool = False, str
                                    _ptr(bias), C.data_ptr(), _ptr(part), part.numel() if split else 0,
                                    ks.ctypes.data_as(_IP), s))
     return (C, int(ks[0])) if split else C
+
+
+def debug_mlp(dtype: str, y, W1, b1, W2, b2, x, alpha: float = 0.5, stream=None):
+    """x += alpha * (W2 SiLU(W1 y + b1) + b2) with the encoder's fused few-row FFN kernel
+    ('f16' / 'bf16'; y [M][d], W1 [f][d], W2 [d][f] device tensors of that type; b1, b2, x
+    float32 device tensors; x is updated in place)."""
+    import torch
+    M, d = y.shape
+    f = W1.shape[0]
+    part = torch.empty((f // 256) * M * d, dtype=torch.float32, device=y.device)
+    s = (stream or torch.cuda.current_stream(y.device)).cuda_stream
+    _check(lib().gigaam_debug_mlp(DTYPES[dtype], M, d, f, y.data_ptr(), W1.data_ptr(), _ptr(b1),
+                                  W2.data_ptr(), _ptr(b2), alpha, x.data_ptr(), part.data_ptr(),
+                                  part.numel(), s))
+    return x
 
 
 def profile_start():

@@ -13,6 +13,8 @@
 // v_mfma_f32_32x32x2_f32 for fp32. A 16-byte LDS fragment per lane feeds either.
 // Because the A and B fragments of a lane always carry the same k indices, the sum over
 // k is exact whatever order the hardware assigns to the k slots.
+#include <cstring>
+
 #include "kernels.h"
 
 namespace gg {
@@ -975,6 +977,178 @@ static hipError_t launch_gemm_impl(DType dt, int qbits, AMode am, Epi ep, const 
       return direct ? run_dl_shape<f16>(am, ep, p, s) : run_tiles<f16, 0>(am, ep, p, s);
   }
   return hipErrorInvalidValue;
+}
+
+
+// ---------------------------------------------------------------------------------------
+// Fused macaron FFN for few rows (a clip or two, a streaming window), the f4 variant that
+// never writes the hidden activations: a workgroup takes 64 rows and one 256-unit chunk of
+// the hidden layer.
+//   phase 1: h = SiLU(y W1[chunk]^T + b1[chunk]) -> LDS, rounded to T as the unfused path
+//            rounds the hidden activations it stores;
+//   phase 2: its share of the output, h W2[:, chunk]^T, accumulated over the 256 units in
+//            fp32 and written as slice `chunk` of the partial sums [f/256][M][d].
+// The split-K reduce then adds the f/256 slices in order with b2 and the residual half step
+// (x += alpha (sum + b2)). Register-staged loads (the next k-tile is read into registers
+// while the current one is consumed), 32 x 32 x 16 MFMAs, 8 waves as 2 (rows) x 4 (columns).
+constexpr int kMlpChunk = 256;
+
+// WM row groups of 32 (BM = 32 WM rows per workgroup), 8 / WM column groups
+template <typename T, int D, int WM>
+__global__ void __launch_bounds__(512) k_mlp(MlpArgs a) {
+  constexpr int BM = 32 * WM, WN = 8 / WM;
+  constexpr int NI1 = kMlpChunk / WN / 32;       // phase-1 32-column blocks per wave
+  constexpr int NI2 = D / WN / 32;               // phase-2 32-column blocks per wave
+  constexpr int LDR1 = 9;                        // phase 1: 64-k rows, 8 slots + pad
+  constexpr int LDR2 = 5;                        // phase 2: 32-k rows, 4 slots + pad
+  constexpr int HS = kMlpChunk / 8 + 1;          // h rows: 32 slots + pad
+  constexpr int ST1 = (BM + kMlpChunk) * LDR1;   // slots per phase-1 stage
+  constexpr int ST2 = D * LDR2;                  // slots of the phase-2 stage
+  constexpr int SREG = 2 * ST1 > ST2 ? 2 * ST1 : ST2;
+  static_assert(NI1 >= 1 && NI2 >= 1 && BM * 8 <= 512, "mlp tile");
+  __shared__ u32x4 lds[SREG + BM * HS];
+  u32x4* hs = lds + SREG;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int fr = lane & 31, fk = lane >> 5;
+  const int m0 = blockIdx.x * BM, c0 = blockIdx.y * kMlpChunk;
+  const T* Y = (const T*)a.y;
+  const T* W1 = (const T*)a.W1;
+  const T* W2 = (const T*)a.W2;
+
+  // ---- phase 1: [BM x 256] = y[BM x D] W1[256 x D]^T, k-tiles of 64
+  const bool aload = tid < BM * 8;
+  const int ar = tid >> 3, ac = tid & 7;
+  const int arow = aload ? (m0 + ar < a.M ? m0 + ar : a.M - 1) : 0;
+  const T* asrc = Y + (long)arow * D + ac * 8;
+  const T* bsrc[4];
+  int brow[4], bcol[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid + 512 * i;
+    brow[i] = e >> 3;
+    bcol[i] = e & 7;
+    bsrc[i] = W1 + (long)(c0 + brow[i]) * D + bcol[i] * 8;
+  }
+  u32x4 ra, rb[4];
+  auto load1 = [&](int kt) {
+    if (aload) ra = *(const u32x4*)(asrc + kt * 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rb[i] = *(const u32x4*)(bsrc[i] + kt * 64);
+  };
+  auto store1 = [&](int buf) {
+    u32x4* st = lds + buf * ST1;
+    if (aload) st[ar * LDR1 + ac] = ra;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st[(BM + brow[i]) * LDR1 + bcol[i]] = rb[i];
+  };
+  f32x16 acc1[NI1];
+#pragma unroll
+  for (int ni = 0; ni < NI1; ++ni)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc1[ni][r] = 0.f;
+  constexpr int KT1 = D / 64;
+  load1(0);
+  store1(0);
+  __syncthreads();
+  for (int kt = 0; kt < KT1; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < KT1) load1(kt + 1);
+    const u32x4* st = lds + cur * ST1;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const u32x4 af = st[(wm * 32 + fr) * LDR1 + kc * 2 + fk];
+#pragma unroll
+      for (int ni = 0; ni < NI1; ++ni)
+        Mma<T>::run(acc1[ni], af, st[(BM + wn * NI1 * 32 + ni * 32 + fr) * LDR1 + kc * 2 + fk]);
+    }
+    if (kt + 1 < KT1) store1(cur ^ 1);
+    __syncthreads();
+  }
+  // h = SiLU(acc + b1) in T, into LDS rows [BM][256]
+  {
+    T* h = (T*)hs;
+#pragma unroll
+    for (int ni = 0; ni < NI1; ++ni) {
+      const int col = wn * NI1 * 32 + ni * 32 + fr;
+      const float bb = a.b1 ? a.b1[c0 + col] : 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * 32 + 8 * (r >> 2) + 4 * fk + (r & 3);
+        h[row * HS * 8 + col] = from_f32<T>(siluf_(acc1[ni][r] + bb));
+      }
+    }
+  }
+
+  // ---- phase 2: [BM x D] = h[BM x 256] W2[D x chunk]^T, k-tiles of 32, one LDS stage
+  constexpr int CH2 = D * 4 / 512;               // 16-byte chunks per thread per k-tile
+  const T* wsrc[CH2];
+  int wrow[CH2], wcol[CH2];
+#pragma unroll
+  for (int i = 0; i < CH2; ++i) {
+    const int e = tid + 512 * i;
+    wrow[i] = e >> 2;
+    wcol[i] = e & 3;
+    wsrc[i] = W2 + (long)wrow[i] * a.f + c0 + wcol[i] * 8;
+  }
+  u32x4 rw[CH2];
+  auto load2 = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < CH2; ++i) rw[i] = *(const u32x4*)(wsrc[i] + kt * 32);
+  };
+  f32x16 acc2[NI2];
+#pragma unroll
+  for (int ni = 0; ni < NI2; ++ni)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc2[ni][r] = 0.f;
+  constexpr int KT2 = kMlpChunk / 32;
+  load2(0);
+  for (int kt = 0; kt < KT2; ++kt) {
+    // the stage is free (the previous k-tile consumed; h written before the first)
+#pragma unroll
+    for (int i = 0; i < CH2; ++i) lds[wrow[i] * LDR2 + wcol[i]] = rw[i];
+    __syncthreads();
+    if (kt + 1 < KT2) load2(kt + 1);
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      const u32x4 af = hs[(wm * 32 + fr) * HS + kt * 4 + kc * 2 + fk];
+#pragma unroll
+      for (int ni = 0; ni < NI2; ++ni)
+        Mma<T>::run(acc2[ni], af, lds[(wn * NI2 * 32 + ni * 32 + fr) * LDR2 + kc * 2 + fk]);
+    }
+    __syncthreads();
+  }
+  GemmParams q = {};
+  q.M = a.M; q.N = D; q.C = a.part + blockIdx.y * (long)a.M * D; q.ldc = D; q.bias = nullptr;
+  epilogue<T, 1, NI2, E_F32>(q, (f32x16(&)[1][NI2])acc2, m0 + wm * 32, wn * NI2 * 32, 0, lane);
+}
+
+bool mlp_fusable(DType dt, int qbits, int M, int d, int f, long part_cap) {
+  return (dt == DT_F16 || dt == DT_BF16) && qbits == 0 && M >= 1 && M <= kMlpMaxRows &&
+         (d == 768 || d == 1024) && f % kMlpChunk == 0 &&
+         (long)(f / kMlpChunk) * M * d <= part_cap;
+}
+
+constexpr int kMlpWM = 1;                  // row groups of 32 per workgroup
+
+hipError_t launch_mlp(DType dt, const MlpArgs& a, const float* b2, float alpha, float* x,
+                      hipStream_t s) {
+  dim3 grid((a.M + 32 * kMlpWM - 1) / (32 * kMlpWM), a.f / kMlpChunk), blk(512);
+  if (dt == DT_F16) {
+    if (a.d == 768) hipLaunchKernelGGL((k_mlp<f16, 768, kMlpWM>), grid, blk, 0, s, a);
+    else hipLaunchKernelGGL((k_mlp<f16, 1024, kMlpWM>), grid, blk, 0, s, a);
+  } else {
+    if (a.d == 768) hipLaunchKernelGGL((k_mlp<bf16, 768, kMlpWM>), grid, blk, 0, s, a);
+    else hipLaunchKernelGGL((k_mlp<bf16, 1024, kMlpWM>), grid, blk, 0, s, a);
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  GemmParams r;
+  std::memset(&r, 0, sizeof r);
+  r.M = a.M; r.N = a.d; r.C = x; r.ldc = a.d; r.bias = b2; r.alpha = alpha; r.part = a.part;
+  return dt == DT_F16 ? run_splitk_reduce<f16>(E_RESID, a.f / kMlpChunk, r, s)
+                      : run_splitk_reduce<bf16>(E_RESID, a.f / kMlpChunk, r, s);
 }
 
 }  // namespace gg

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <climits>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -690,6 +691,14 @@ int run(gigaam_model* m, const float* pcm, const int32_t* lengths, int32_t B, in
                  float alpha = 1.f) {
     return gemm(M, N, K, A, lda, P + l.w, l.qb ? P + l.s : nullptr, (const float*)(P + l.b), Cp, ldc, alpha);
   };
+  // macaron FFN half step x += 1/2 (W2 SiLU(W1 y + b1) + b2) as two GEMMs; dks reports a
+  // split left to the next LayerNorm. (The fused few-row kernel behind gigaam_debug_mlp
+  // measured slower than this inside the encode, where each layer's weights come from HBM.)
+  auto ffn = [&](const Lin& l1, const Lin& l2, int* dks) -> int {
+    int rc2;
+    if ((rc2 = G("gemm.ffn_up", A_PLAIN, E_SILU, l1.qb, lin(l1, U_tot, f, d, y, d, hid, f)))) return rc2;
+    return G("gemm.ffn_down", A_PLAIN, E_RESID, l2.qb, lin(l2, U_tot, d, f, hid, f, x, d, 0.5f), dks);
+  };
   int rc;
 
   // ---- geometry to the device
@@ -736,9 +745,8 @@ int run(gigaam_model* m, const float* pcm, const int32_t* lengths, int32_t B, in
     const LayerOff& o = L.layers[li];
     const int tap = 1000 + 10 * li;
     // a5 FFN1 (half step)
-    if ((rc = G("gemm.ffn_up", A_PLAIN, E_SILU, o.ff1_1.qb, lin(o.ff1_1, U_tot, f, d, y, d, hid, f)))) return rc;
     int dks = 0;      // split-K slices of the last residual GEMM left for the next LayerNorm
-    if ((rc = G("gemm.ffn_down", A_PLAIN, E_RESID, o.ff1_2.qb, lin(o.ff1_2, U_tot, d, f, hid, f, x, d, 0.5f), &dks))) return rc;
+    if ((rc = ffn(o.ff1_1, o.ff1_2, &dks))) return rc;
     if (stage == tap + 0) return copy_out(x, (size_t)U_tot * d);
     // a6-a9 attention: LN + rope(y) -> [Q|K] from r, V from y -> flash attention -> out proj
     if ((rc = LN(LN_ROPE, o.att_g, o.att_b, nullptr, nullptr, y, r, dks, (const float*)(P + o.ff1_2.b), 0.5f))) return rc;
@@ -761,8 +769,7 @@ int run(gigaam_model* m, const float* pcm, const int32_t* lengths, int32_t B, in
     if (stage == tap + 2) return copy_out(x, (size_t)U_tot * d);
     // a13 FFN2 (half step) + final norm fused with the next block's first pre-norm
     if ((rc = LN(LN_PLAIN, o.ff2_g, o.ff2_b, nullptr, nullptr, y, nullptr, dks, (const float*)(P + o.pw2.b)))) return rc;
-    if ((rc = G("gemm.ffn_up", A_PLAIN, E_SILU, o.ff2_1.qb, lin(o.ff2_1, U_tot, f, d, y, d, hid, f)))) return rc;
-    if ((rc = G("gemm.ffn_down", A_PLAIN, E_RESID, o.ff2_2.qb, lin(o.ff2_2, U_tot, d, f, hid, f, x, d, 0.5f), &dks))) return rc;
+    if ((rc = ffn(o.ff2_1, o.ff2_2, &dks))) return rc;
     if (stage == tap + 3) return copy_out(x, (size_t)U_tot * d);
     const float* rb2 = (const float*)(P + o.ff2_2.b);
     if (li + 1 < c.n_layers) {
@@ -822,6 +829,22 @@ extern "C" int gigaam_debug_gemm(int32_t dtype, int32_t M, int32_t N, int32_t K,
   p.part_cap = part_dev ? (long)part_floats : 0;
   if (slices_host) *slices_host = gemm_split_slices((DType)dtype, qb, A_PLAIN, E_F32, p);
   HIP_TRY(launch_gemm((DType)dtype, qb, A_PLAIN, E_F32, p, (hipStream_t)hip_stream));
+  return GIGAAM_OK;
+}
+
+extern "C" int gigaam_debug_mlp(int32_t dtype, int32_t M, int32_t d, int32_t f, const void* y_dev,
+                                const void* W1_dev, const float* b1_dev, const void* W2_dev,
+                                const float* b2_dev, float alpha, float* x_dev, float* part_dev,
+                                size_t part_floats, void* hip_stream) {
+  if (dtype != GIGAAM_F16 && dtype != GIGAAM_BF16) return fail(GIGAAM_E_INVAL, "dtype %d", dtype);
+  if (!y_dev || !W1_dev || !W2_dev || !x_dev || !part_dev) return fail(GIGAAM_E_INVAL, "NULL pointer");
+  if (((uintptr_t)part_dev & 15) || ((uintptr_t)x_dev & 15))
+    return fail(GIGAAM_E_INVAL, "x / partial-sum buffer not 16-byte aligned");
+  if (!mlp_fusable((DType)dtype, 0, M, d, f, (long)std::min(part_floats, (size_t)LONG_MAX)))
+    return fail(GIGAAM_E_INVAL, "fused MLP shape %d x %d x %d or scratch of %zu floats unsupported",
+                M, d, f, part_floats);
+  MlpArgs ma{M, d, f, y_dev, W1_dev, b1_dev, W2_dev, part_dev};
+  HIP_TRY(launch_mlp((DType)dtype, ma, b2_dev, alpha, x_dev, (hipStream_t)hip_stream));
   return GIGAAM_OK;
 }
 

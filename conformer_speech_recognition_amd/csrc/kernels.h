@@ -52,6 +52,21 @@ hipError_t launch_gemm(DType dt, int qbits, AMode am, Epi ep, const GemmParams& 
 // K slices launch_gemm uses for these arguments (1: no split)
 int gemm_split_slices(DType dt, int qbits, AMode am, Epi ep, const GemmParams& p);
 
+// Fused macaron FFN for few rows: x += alpha * (W2 SiLU(W1 y + b1) + b2) without the hidden
+// activations in HBM (16-bit weights, d 768 or 1024, f a multiple of 256, at most
+// kMlpMaxRows rows; part holds (f / 256) * M * d floats of partial sums).
+struct MlpArgs {
+  int M, d, f;
+  const void* y;                   // T [M][d], the LayerNorm output
+  const void* W1; const float* b1; // [f][d], [f]
+  const void* W2;                  // [d][f]
+  float* part;                     // fp32 scratch
+};
+constexpr int kMlpMaxRows = 896;
+bool mlp_fusable(DType dt, int qbits, int M, int d, int f, long part_cap);
+hipError_t launch_mlp(DType dt, const MlpArgs& a, const float* b2, float alpha, float* x,
+                      hipStream_t s);
+
 // ---- meta -------------------------------------------------------------------------
 hipError_t launch_meta(const MetaArgs& a, const MetaDev& m, int T_tot, int S_tot, int U_tot,
                        hipStream_t s);

@@ -222,6 +222,19 @@ int gigaam_debug_gemm(int32_t dtype, int32_t M, int32_t N, int32_t K, const void
                       float* C_dev, float* part_dev, size_t part_floats, int32_t* slices_host,
                       void* hip_stream);
 
+/* Diagnostics: the fused macaron FFN that the encoder uses for few rows, on its own,
+ *   x[m][n] += alpha * (sum_j W2[n][j] h[m][j] + b2[n]),
+ *   h[m][j]  = T(SiLU(sum_k W1[j][k] y[m][k] + b1[j]))      (the hidden activations rounded
+ *                                                          to T, never stored in HBM)
+ * dtype GIGAAM_F16 or GIGAAM_BF16 (T); y_dev [M][d], W1_dev [f][d], W2_dev [d][f] in T;
+ * b1_dev float [f] or NULL, b2_dev float [d] or NULL; x_dev float [M][d], updated in place;
+ * part_dev float scratch (16-byte aligned) of at least (f / 256) * M * d floats.
+ * d = 768 or 1024, f a multiple of 256, 1 <= M <= 896. Errors: GIGAAM_E_INVAL, GIGAAM_E_HIP. */
+int gigaam_debug_mlp(int32_t dtype, int32_t M, int32_t d, int32_t f, const void* y_dev,
+                     const void* W1_dev, const float* b1_dev, const void* W2_dev,
+                     const float* b2_dev, float alpha, float* x_dev, float* part_dev,
+                     size_t part_floats, void* hip_stream);
+
 /* Diagnostics: the encoder's attention kernel on its own, over packed clips.
  * frames_host int32 [batch]: frames U_b of each clip (>= 1); qkv_dev [sum U_b][3 d_model]
  * holds q | k | v per frame in the storage type of `dtype` (fp32, fp16, bf16;

@@ -204,6 +204,18 @@ def test_encode_argument_errors_before_any_launch(gg):
     assert L.gigaam_debug_gemm(1, 4, 4, 100, fake, fake, None, None, fake, None, 0, None, None) == gg.E_INVAL
     assert L.gigaam_debug_gemm(1, 4, 4, 128, fake, fake, None, None, fake, fake + 4, 64, None,
                                None) == gg.E_INVAL                  # misaligned partial buffer
+    F = ctypes.c_float
+    big = 1 << 26
+    # fused FFN: fp32 dtype, unsupported width, too many rows, short scratch, NULL, misaligned
+    assert L.gigaam_debug_mlp(0, 64, 768, 3072, fake, fake, None, fake, None, F(0.5), fake, fake, big, None) == gg.E_INVAL
+    assert L.gigaam_debug_mlp(1, 64, 512, 3072, fake, fake, None, fake, None, F(0.5), fake, fake, big, None) == gg.E_INVAL
+    assert L.gigaam_debug_mlp(1, 897, 768, 3072, fake, fake, None, fake, None, F(0.5), fake, fake, big, None) == gg.E_INVAL
+    assert L.gigaam_debug_mlp(1, 64, 768, 3000, fake, fake, None, fake, None, F(0.5), fake, fake, big, None) == gg.E_INVAL
+    assert L.gigaam_debug_mlp(1, 64, 768, 3072, fake, fake, None, fake, None, F(0.5), fake, fake,
+                              12 * 64 * 768 - 1, None) == gg.E_INVAL
+    assert L.gigaam_debug_mlp(1, 64, 768, 3072, None, fake, None, fake, None, F(0.5), fake, fake, big, None) == gg.E_INVAL
+    assert L.gigaam_debug_mlp(1, 64, 768, 3072, fake, fake, None, fake, None, F(0.5), fake, fake + 4, big,
+                              None) == gg.E_INVAL
 
 
 def test_workspace_bound_covers_every_length_mix(gg):
