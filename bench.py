@@ -304,6 +304,46 @@ def mlp_variant(reps=64, sets=32):
     return out
 
 
+def library_gemm_leg(cfg, U, prof, reps=64, sets=16):
+    """The vendor library's plain product (torch.mm in the workload's 16-bit type, in and out, no bias or epilogue) on
+    each encoder GEMM role's shape at this workload's U rows, beside the encoder kernel's own
+    average launch for that role (which also applies its epilogue: SiLU, GLU, the residual
+    half step). Weights rotate over `sets` copies, as each layer's differ in an encode."""
+    import torch
+    d, f = cfg["d_model"], cfg["d_ff"]
+    shapes = {"gemm.ffn_up": (f, d, "bias + SiLU, fp16 out"),
+              "gemm.ffn_down": (d, f, "bias + residual half step into fp32 x"),
+              "gemm.qkv": (3 * d, d, "bias, fp16 out"),
+              "gemm.pw1_glu": (2 * d, d, "bias + GLU, fp16 out (half width)"),
+              "gemm.out_proj": (d, d, "bias + residual into fp32 x")}
+    ours = {r["name"]: r["avg_us"] for r in prof}
+    tt = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.half
+    g = torch.Generator(device="cuda").manual_seed(5)
+    st = torch.cuda.current_stream()
+    out = {}
+    for role, (N, K, epi) in shapes.items():
+        A = torch.randn(U, K, device="cuda", generator=g).to(tt)
+        Ws = [torch.randn(N, K, device="cuda", generator=g).to(tt) for _ in range(sets)]
+        C = torch.empty(U, N, device="cuda", dtype=tt)
+        for i in range(4):
+            torch.mm(A, Ws[i % sets].t(), out=C)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(st)
+        for i in range(reps):
+            torch.mm(A, Ws[i % sets].t(), out=C)
+        e1.record(st)
+        e1.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        fl = 2.0 * U * N * K
+        out[role] = {"M": U, "N": N, "K": K, "torch_mm_us": round(us, 1),
+                     "torch_mm_tflops": round(fl / us / 1e6, 1),
+                     "ours_us": ours.get(role), "ours_tflops": round(fl / ours[role] / 1e6, 1) if role in ours else None,
+                     "ours_epilogue": epi}
+        del A, Ws, C
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -322,6 +362,8 @@ def main():
                          "by a re-encode of the last <= 30 s")
     ap.add_argument("--sweep", action="store_true",
                     help="also report throughput versus chunk length and batch size")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="also time the vendor library's plain product on each GEMM role's shape")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {a.gpus}); the "
@@ -426,6 +468,8 @@ def main():
         line["stream"] = stream_leg(model, cfg)
     if a.sweep:
         line["sweep"] = sweep_leg(model)
+    if a.library_gemm:
+        line["library_gemm"] = library_gemm_leg(cfg, line["config"]["encoder_frames"], prof)
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(a.workload, a.cpu_budget)
     print(json.dumps(line), flush=True)
