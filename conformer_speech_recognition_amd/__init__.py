@@ -391,8 +391,8 @@ def debug_gemm(dtype: str, A, W, bias=None, scale=None, split: bool = False, str
 
 
 def debug_mlp(dtype: str, y, W1, b1, W2, b2, x, alpha: float = 0.5, stream=None):
-    """x += alpha * (W2 SiLU(W1 y + b1) + b2) with the encoder's fused few-row FFN kernel
-    ('f16' / 'bf16'; y [M][d], W1 [f][d], W2 [d][f] device tensors of that type; b1, b2, x
+    """x += alpha * (W2 SiLU(W1 y + b1) + b2) with the fused few-row FFN kernel (a measured
+    variant; the encoder runs the two GEMMs) ('f16' / 'bf16'; y [M][d], W1 [f][d], W2 [d][f] device tensors of that type; b1, b2, x
     float32 device tensors; x is updated in place)."""
     import torch
     M, d = y.shape

@@ -981,9 +981,9 @@ static hipError_t launch_gemm_impl(DType dt, int qbits, AMode am, Epi ep, const 
 
 
 // ---------------------------------------------------------------------------------------
-// Fused macaron FFN for few rows (a clip or two, a streaming window), the f4 variant that
-// never writes the hidden activations: a workgroup takes 64 rows and one 256-unit chunk of
-// the hidden layer.
+// Fused macaron FFN for few rows (a clip or two, a streaming window), a variant that never
+// writes the hidden activations (measured against the two GEMMs; the encoder does not use
+// it): a workgroup takes 32 WM rows and one 256-unit chunk of the hidden layer.
 //   phase 1: h = SiLU(y W1[chunk]^T + b1[chunk]) -> LDS, rounded to T as the unfused path
 //            rounds the hidden activations it stores;
 //   phase 2: its share of the output, h W2[:, chunk]^T, accumulated over the 256 units in

@@ -703,11 +703,11 @@ int run(gigaam_model* m, const float* pcm, const int32_t* lengths, int32_t B, in
 
   // ---- geometry to the device
   LAUNCH("meta", launch_meta(meta, md, T_tot, S_tot, U_tot, s));
-  // ---- a1 frontend
+  // ---- frontend (log-mel)
   LAUNCH("frontend", launch_frontend(pcm, stride, m->window, m->fb, md, T_tot, mel,
                                      (float*)(W + w.fe), (int*)(W + w.fe + 640 * 4), s));
   if (stage == GIGAAM_STAGE_MEL) return copy_out(mel, (size_t)T_tot * 64);
-  // ---- a2, a3 subsampling (implicit-GEMM Conv1d k5 s2 p2 + ReLU)
+  // ---- subsampling: two implicit-GEMM Conv1d k5 s2 p2 + ReLU
   {
     GemmParams g1 = gemm(S_tot, d, 5 * 64, mel, 0, P + L.conv1_w, nullptr, (const float*)(P + L.conv1_b), h1, d);
     g1.rowclip = md.rowS; g1.cu_in = md.cuT; g1.cu_out = md.cuS; g1.cin = 64;
@@ -717,7 +717,7 @@ int run(gigaam_model* m, const float* pcm, const int32_t* lengths, int32_t B, in
     if ((rc = G("gemm.conv2", A_CONV, E_RELU_F32, false, g2))) return rc;
   }
   if (stage == GIGAAM_STAGE_SUB) return copy_out(x, (size_t)U_tot * d);
-  // ---- a4 rotary tables for positions 0..U_max-1
+  // ---- rotary tables for positions 0..U_max-1
   LAUNCH("rope_table", launch_rope_table(cos_t, sin_t, U_max, dk, c.rope_base, s));
 
   LnParams ln;
@@ -744,11 +744,11 @@ int run(gigaam_model* m, const float* pcm, const int32_t* lengths, int32_t B, in
   for (int li = 0; li < c.n_layers; ++li) {
     const LayerOff& o = L.layers[li];
     const int tap = 1000 + 10 * li;
-    // a5 FFN1 (half step)
+    // first macaron FFN (half step)
     int dks = 0;      // split-K slices of the last residual GEMM left for the next LayerNorm
     if ((rc = ffn(o.ff1_1, o.ff1_2, &dks))) return rc;
     if (stage == tap + 0) return copy_out(x, (size_t)U_tot * d);
-    // a6-a9 attention: LN + rope(y) -> [Q|K] from r, V from y -> flash attention -> out proj
+    // attention: LN + rope(y) -> [Q|K] from r, V from y -> flash attention -> out proj
     if ((rc = LN(LN_ROPE, o.att_g, o.att_b, nullptr, nullptr, y, r, dks, (const float*)(P + o.ff1_2.b), 0.5f))) return rc;
     {
       GemmParams gq = lin(o.qkv, U_tot, 3 * d, d, r, d, qkv, 3 * d);
@@ -758,7 +758,7 @@ int run(gigaam_model* m, const float* pcm, const int32_t* lengths, int32_t B, in
     LAUNCH("attention", launch_attention(dt, dk, ap, s));
     if ((rc = G("gemm.out_proj", A_PLAIN, E_RESID, o.out.qb, lin(o.out, U_tot, d, d, ao, d, x, d), &dks))) return rc;
     if (stage == tap + 1) return copy_out(x, (size_t)U_tot * d);
-    // a10-a12 conv module
+    // convolution module
     if ((rc = LN(LN_PLAIN, o.cv_g, o.cv_b, nullptr, nullptr, y, nullptr, dks, (const float*)(P + o.out.b)))) return rc;
     if ((rc = G("gemm.pw1_glu", A_PLAIN, E_GLU, o.pw1.qb, lin(o.pw1, U_tot, 2 * d, d, y, d, hid, d)))) return rc;
     dp.w = (const float*)(P + o.dw_w); dp.b = (const float*)(P + o.dw_b);
@@ -767,7 +767,7 @@ int run(gigaam_model* m, const float* pcm, const int32_t* lengths, int32_t B, in
     LAUNCH("dwconv_bn_silu", launch_dwconv(dt, c.conv_kernel, dp, s));
     if ((rc = G("gemm.pw2", A_PLAIN, E_RESID, o.pw2.qb, lin(o.pw2, U_tot, d, d, hid2, d, x, d), &dks))) return rc;
     if (stage == tap + 2) return copy_out(x, (size_t)U_tot * d);
-    // a13 FFN2 (half step) + final norm fused with the next block's first pre-norm
+    // second macaron FFN (half step) + block-final norm fused with the next block's first pre-norm
     if ((rc = LN(LN_PLAIN, o.ff2_g, o.ff2_b, nullptr, nullptr, y, nullptr, dks, (const float*)(P + o.pw2.b)))) return rc;
     if ((rc = ffn(o.ff2_1, o.ff2_2, &dks))) return rc;
     if (stage == tap + 3) return copy_out(x, (size_t)U_tot * d);
@@ -780,7 +780,7 @@ int run(gigaam_model* m, const float* pcm, const int32_t* lengths, int32_t B, in
     }
     if (stage == GIGAAM_STAGE_LAYER + li) return copy_out(x, (size_t)U_tot * d);
   }
-  // ---- a14 CTC head + log-softmax + argmax, a15 greedy collapse
+  // ---- CTC head + log-softmax + argmax, then greedy collapse
   {
     GemmParams gh = gemm(U_tot, C, d, x, d, P + L.head_w, nullptr, (const float*)(P + L.head_b), logits, C);
     if ((rc = G("gemm.head", A_F32, E_F32, false, gh))) return rc;

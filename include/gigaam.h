@@ -222,7 +222,8 @@ int gigaam_debug_gemm(int32_t dtype, int32_t M, int32_t N, int32_t K, const void
                       float* C_dev, float* part_dev, size_t part_floats, int32_t* slices_host,
                       void* hip_stream);
 
-/* Diagnostics: the fused macaron FFN that the encoder uses for few rows, on its own,
+/* Diagnostics: a fused variant of the macaron FFN for few rows (hidden activations kept on
+ * chip), measured against the encoder's two GEMMs, which the encoder uses instead:
  *   x[m][n] += alpha * (sum_j W2[n][j] h[m][j] + b2[n]),
  *   h[m][j]  = T(SiLU(sum_k W1[j][k] y[m][k] + b1[j]))      (the hidden activations rounded
  *                                                          to T, never stored in HBM)
