@@ -487,6 +487,39 @@ __global__ void __launch_bounds__(64 * WGM * WGN, OCC) k_gemm_p(GemmParams p) {
     else fb[b][r - MI] = *(const u32x4*)(smem + off + brow + (r - MI) * 32 * RB);
   };
 
+  // epilogue geometry: the output is staged through LDS in chunks of CH rows
+  constexpr bool F32OUT = (EP == E_RESID || EP == E_F32);
+  constexpr int OES = F32OUT ? 4 : (int)sizeof(T);
+  constexpr int BNO = (EP == E_GLU) ? BN / 2 : BN;
+  constexpr int PITCH = BNO * OES + 16;
+  constexpr int CH = chunk_rows(BM, (S * STAGE) / PITCH);
+  constexpr int NCH = BM / CH;
+  constexpr int SEGS = BNO * OES / 16;
+  constexpr int PER = (CH * SEGS + NT - 1) / NT;
+  constexpr int EPS = 16 / OES;
+  static_assert(CH >= 32 && BM % CH == 0 && CH * PITCH <= S * STAGE, "epilogue chunking");
+  const int n0o = (EP == E_GLU) ? n0 / 2 : n0;
+  const int Nout = (EP == E_GLU) ? p.N / 2 : p.N;
+  const bool vec = ((long)p.ldc * OES) % 16 == 0;
+  // Residual epilogue, one workgroup per CU: the x segments this thread will update are read
+  // now, so that their HBM reads overlap the main loop rather than follow it (every tile of
+  // such a launch reaches its epilogue at about the same time). Loads complete in issue
+  // order, so these extra ones only make the k-tile waits below stricter, never looser.
+  constexpr bool PFX = EP == E_RESID && OCC == 1 && NCH * PER <= 16;
+  f32x4 xpre[PFX ? NCH * PER : 1];
+  if constexpr (PFX) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int e = tid + NT * i, rl = e / SEGS, sg = e % SEGS;
+        const int row = m0 + c * CH + rl, col = n0o + sg * EPS;
+        xpre[c * PER + i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (e < CH * SEGS && row < p.M && vec && col + EPS <= Nout)
+          xpre[c * PER + i] = *(const f32x4*)((const char*)p.C + ((long)row * p.ldc + col) * 4);
+      }
+  }
+
   // prologue: k-tiles 0 .. S-1 in flight, then k-tile 0 complete
 #pragma unroll
   for (int g = 0; g < S; ++g)
@@ -546,20 +579,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, OCC) k_gemm_p(GemmParams p) {
   }
 
   // ---- epilogue: stage through LDS in chunks of whole 32-row blocks, copy out rows
-  constexpr bool F32OUT = (EP == E_RESID || EP == E_F32);
-  constexpr int OES = F32OUT ? 4 : (int)sizeof(T);
-  constexpr int BNO = (EP == E_GLU) ? BN / 2 : BN;
-  constexpr int PITCH = BNO * OES + 16;
-  constexpr int CH = chunk_rows(BM, (S * STAGE) / PITCH);
-  constexpr int NCH = BM / CH;
-  constexpr int SEGS = BNO * OES / 16;
-  constexpr int PER = (CH * SEGS + NT - 1) / NT;
-  constexpr int EPS = 16 / OES;
-  static_assert(CH >= 32 && BM % CH == 0 && CH * PITCH <= S * STAGE, "epilogue chunking");
   const int lr = lane & 31, h4 = 4 * (lane >> 5);
-  const int n0o = (EP == E_GLU) ? n0 / 2 : n0;
-  const int Nout = (EP == E_GLU) ? p.N / 2 : p.N;
-  const bool vec = ((long)p.ldc * OES) % 16 == 0;
   // this lane's bias: 4 consecutive columns per (block, g), loaded once
   f32x4 bv[NI][4];
 #pragma unroll
@@ -627,8 +647,10 @@ __global__ void __launch_bounds__(64 * WGM * WGN, OCC) k_gemm_p(GemmParams p) {
       if (e >= CH * SEGS || row >= p.M || col >= Nout) continue;
       char* gd = (char*)p.C + ((long)row * p.ldc + col) * OES;
       if (vec && col + EPS <= Nout) {
-        if constexpr (EP == E_RESID)
-          *(f32x4*)gd = *(const f32x4*)gd + __builtin_bit_cast(f32x4, sv[i]);
+        if constexpr (EP == E_RESID) {
+          if constexpr (PFX) *(f32x4*)gd = xpre[c * PER + i] + __builtin_bit_cast(f32x4, sv[i]);
+          else *(f32x4*)gd = *(const f32x4*)gd + __builtin_bit_cast(f32x4, sv[i]);
+        }
         else
           *(u32x4*)gd = sv[i];
       } else {                                      // ragged last segment or unaligned rows
