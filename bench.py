@@ -344,6 +344,41 @@ def library_gemm_leg(cfg, U, prof, reps=64, sets=16):
     return out
 
 
+def measured_peaks(dtype: str):
+    """What this GPU sustains, beside the datasheet peaks: the vendor library's GEMM on a large
+    square product in the workload's compute type (16384^3, fp32: 8192^3), and a plain device
+    copy of 1 GiB (read + write bytes per second). Median of 5 timed calls after 2 warm-ups."""
+    import torch
+    tt = {"f32": torch.float32, "bf16": torch.bfloat16}.get(dtype, torch.float16)
+    n = 8192 if tt == torch.float32 else 16384
+    g = torch.Generator(device="cuda").manual_seed(3)
+    a = torch.randn(n, n, device="cuda", generator=g).to(tt)
+    b = torch.randn(n, n, device="cuda", generator=g).to(tt)
+    c = torch.empty(n, n, device="cuda", dtype=tt)
+
+    def med(fn):
+        for _ in range(2):
+            fn()
+        ts = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return float(np.median(ts))
+
+    t_mm = med(lambda: torch.mm(a, b, out=c))
+    del a, b, c
+    x = torch.empty(1 << 28, device="cuda")
+    y = torch.empty_like(x)
+    t_cp = med(lambda: y.copy_(x))
+    del x, y
+    return {"gemm_tflops": round(2.0 * n ** 3 / t_mm / 1e12, 1), "gemm_shape": f"{n}^3 {str(tt)[6:]}",
+            "copy_gbs": round(2.0 * (1 << 30) / t_cp / 1e9, 1), "copy_bytes": 1 << 30}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -436,6 +471,9 @@ def main():
                 "frac": round(achieved / PEAK_HBM_GBS, 4)}
     roof.update({"kernel": name, "avg_launch_us": dom["avg_us"], "launches": dom["launches"],
                  "traffic": measured_traffic(a.workload, name)})
+    peaks = measured_peaks(cfg["dtype"])
+    roof["measured_peak"] = peaks["gemm_tflops"] if roof["unit"] == "TFLOP/s" else peaks["copy_gbs"]
+    roof["frac_of_measured_peak"] = round(roof["achieved"] / roof["measured_peak"], 4)
 
     ms = 1e3 * elapsed / a.steps
     value = a.steps * audio_s / elapsed
@@ -460,6 +498,7 @@ def main():
         "fp16_mfma_roofline_frac": round(tflops / PEAK_TFLOPS["f16"], 4),
         "step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 4) for q in (10, 50, 90)],
         "roofline": roof,
+        "measured_peaks": peaks,
         "kernels": sorted(({"name": r["name"], "launches": r["launches"], "avg_us": r["avg_us"],
                             "total_ms": round(r["total_ms"] / a.profile_steps, 4)} for r in prof),
                           key=lambda r: -r["total_ms"]),
