@@ -139,9 +139,17 @@ def cpu_baseline(name, budget_s):
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu_model = next((l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")),
+                             cpu_model)
+    except OSError:
+        pass
     return {"value": round(audio / dt, 3), "unit": "audio-s/s", "cores": int(cores), "kind": "oracle",
             "sample": f"float64 oracle on {len(done)} of {len(lens)} clips of workload {name} "
-                      f"({audio:.2f} s of audio in {dt:.1f} s)"}
+                      f"({audio:.2f} s of audio in {dt:.1f} s)",
+            "cpu_model": cpu_model}
 
 
 def rnnt_leg(model, pcm_d, lens, cfg, steps, warmup):
