@@ -840,6 +840,8 @@ extern "C" int gigaam_debug_mlp(int32_t dtype, int32_t M, int32_t d, int32_t f, 
   if (!y_dev || !W1_dev || !W2_dev || !x_dev || !part_dev) return fail(GIGAAM_E_INVAL, "NULL pointer");
   if (((uintptr_t)part_dev & 15) || ((uintptr_t)x_dev & 15))
     return fail(GIGAAM_E_INVAL, "x / partial-sum buffer not 16-byte aligned");
+  if (((uintptr_t)y_dev & 15) || ((uintptr_t)W1_dev & 15) || ((uintptr_t)W2_dev & 15))
+    return fail(GIGAAM_E_INVAL, "y / W1 / W2 not 16-byte aligned");
   if (!mlp_fusable((DType)dtype, 0, M, d, f, (long)std::min(part_floats, (size_t)LONG_MAX)))
     return fail(GIGAAM_E_INVAL, "fused MLP shape %d x %d x %d or scratch of %zu floats unsupported",
                 M, d, f, part_floats);

@@ -228,7 +228,8 @@ int gigaam_debug_gemm(int32_t dtype, int32_t M, int32_t N, int32_t K, const void
  *   h[m][j]  = T(SiLU(sum_k W1[j][k] y[m][k] + b1[j]))      (the hidden activations rounded
  *                                                          to T, never stored in HBM)
  * dtype GIGAAM_F16 or GIGAAM_BF16 (T); y_dev [M][d], W1_dev [f][d], W2_dev [d][f] in T;
- * b1_dev float [f] or NULL, b2_dev float [d] or NULL; x_dev float [M][d], updated in place;
+ * (all three 16-byte aligned); b1_dev float [f] or NULL, b2_dev float [d] or NULL; x_dev
+ * float [M][d], 16-byte aligned, updated in place;
  * part_dev float scratch (16-byte aligned) of at least (f / 256) * M * d floats.
  * d = 768 or 1024, f a multiple of 256, 1 <= M <= 896. Errors: GIGAAM_E_INVAL, GIGAAM_E_HIP. */
 int gigaam_debug_mlp(int32_t dtype, int32_t M, int32_t d, int32_t f, const void* y_dev,

@@ -216,6 +216,11 @@ def test_encode_argument_errors_before_any_launch(gg):
     assert L.gigaam_debug_mlp(1, 64, 768, 3072, None, fake, None, fake, None, F(0.5), fake, fake, big, None) == gg.E_INVAL
     assert L.gigaam_debug_mlp(1, 64, 768, 3072, fake, fake, None, fake, None, F(0.5), fake, fake + 4, big,
                               None) == gg.E_INVAL
+    for i in range(3):                                  # y, W1, W2 read 16 bytes at a time
+        ptrs = [fake, fake, fake]
+        ptrs[i] = fake + 2
+        assert L.gigaam_debug_mlp(1, 64, 768, 3072, ptrs[0], ptrs[1], None, ptrs[2], None, F(0.5), fake,
+                                  fake, big, None) == gg.E_INVAL
 
 
 def test_workspace_bound_covers_every_length_mix(gg):
