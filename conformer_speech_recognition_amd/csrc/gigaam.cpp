@@ -824,6 +824,8 @@ extern "C" int gigaam_debug_gemm(int32_t dtype, int32_t M, int32_t N, int32_t K,
     return fail(GIGAAM_E_INVAL, "NULL pointer");
   if (part_dev && ((uintptr_t)part_dev & 15))
     return fail(GIGAAM_E_INVAL, "partial-sum buffer not 16-byte aligned");
+  if (((uintptr_t)A_dev & 15) || ((uintptr_t)W_dev & 15) || ((uintptr_t)C_dev & 15))
+    return fail(GIGAAM_E_INVAL, "A / W / C not 16-byte aligned");
   GemmParams p = gemm(M, N, K, A_dev, K, W_dev, scale_dev, bias_dev, C_dev, N);
   p.part = part_dev;
   p.part_cap = part_dev ? (long)part_floats : 0;

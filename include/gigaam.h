@@ -207,7 +207,7 @@ int gigaam_encode_stage(gigaam_model* model, const float* pcm_dev, const int32_t
  * A_dev [M][K] and W_dev [N][K] in the storage type of `dtype` (GIGAAM_F32: float,
  * GIGAAM_F16: fp16, GIGAAM_BF16: bf16; GIGAAM_W8F16 / W6F16 / W4F16: A fp16, W the
  * packed b-bit rows described above with scale_dev [N][K/64] fp16 scales); bias_dev
- * float[N] or NULL; C_dev float [M][N].
+ * float[N] or NULL; C_dev float [M][N]. A_dev, W_dev and C_dev must be 16-byte aligned.
  * part_dev: float [part_floats] scratch (16-byte aligned) for split-K partial sums, or
  * NULL. With it the kernel splits the K sum across workgroups when the output tiles
  * alone fill less than half the GPU, as the encoder does for small batches: each slice

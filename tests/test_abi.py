@@ -204,6 +204,11 @@ def test_encode_argument_errors_before_any_launch(gg):
     assert L.gigaam_debug_gemm(1, 4, 4, 100, fake, fake, None, None, fake, None, 0, None, None) == gg.E_INVAL
     assert L.gigaam_debug_gemm(1, 4, 4, 128, fake, fake, None, None, fake, fake + 4, 64, None,
                                None) == gg.E_INVAL                  # misaligned partial buffer
+    for i in range(3):                                  # A, W, C move 16 bytes at a time
+        ptrs = [fake, fake, fake]
+        ptrs[i] = fake + 4
+        assert L.gigaam_debug_gemm(1, 4, 4, 128, ptrs[0], ptrs[1], None, None, ptrs[2], None, 0, None,
+                                   None) == gg.E_INVAL
     F = ctypes.c_float
     big = 1 << 26
     # fused FFN: fp32 dtype, unsupported width, too many rows, short scratch, NULL, misaligned
