@@ -147,3 +147,16 @@ def test_int8_model_uses_dequantised_weights():
     np.testing.assert_array_equal(P["layers.0.ff1.linear1.weight"],
                                   oracle.dequantize_int8_g64(w["layers.0.ff1.linear1.weight_q"],
                                                              w["layers.0.ff1.linear1.weight_scale"]))
+
+
+def test_fp32_self_bound_at_the_multilingual_width():
+    """The same fp32-vs-fp64 self-bound at the 1024-wide shape (2 blocks of d 1024, 16
+    heads, FFN 4096, 129 classes; the 24-block model's block shape) on a 2 s clip."""
+    cfg = synth.model_config(2, 1024, 16, 4096, 31, 129, "f16")
+    w = synth.make_weights(cfg, 4)
+    pcm = synth.make_signal(np.random.default_rng(4), 32000)
+    r64 = oracle.encode_clip(pcm, w, cfg)
+    r32 = oracle.encode_clip(pcm, w, cfg, dtype=np.float32)
+    assert r64["enc_out"].shape == (50, 1024)
+    assert np.abs(r32["enc_out"] - r64["enc_out"]).max() < 1e-4
+    np.testing.assert_array_equal(r32["ids"], r64["ids"])

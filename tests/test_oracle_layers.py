@@ -304,3 +304,89 @@ def test_conv_module_glu_dw_bn_silu_chain():
     bn = (dw - m) / np.sqrt(v + 1e-5) * g + b
     expect = bn / (1.0 + np.exp(-bn))
     np.testing.assert_allclose(oracle.conv_module(x, P, "c.", 1e-5, 1e-5), expect, rtol=1e-10, atol=1e-12)
+
+
+# ------------------------------------------------------------------ macaron feed-forward
+
+LN3 = float(np.log(3.0))
+
+
+def ffn_closed_form_case():
+    """A 4-wide feed-forward module with non-zero weights whose output is a closed form.
+
+    Rows [1, 2, 3, 4] and [10, 13, 16, 19] have the same standardised values
+    n = [-3, -1, 1, 3] / sqrt(5) (LayerNorm with eps 0 ignores shift and positive scale).
+    Gain sqrt(5) ln3 [1/3, 1, 1, 1/3] and shift [0, ln3, 0, 0] make the norm output
+    y = ln3 [-1, 0, 1, 1]. linear1 takes unit i from y[(i + 1) mod 4] (a cyclic permutation,
+    so a transposed weight picks other entries) plus b1 = [0, 0, ln3, 0]:
+    pre-activation ln3 [0, 1, 2, -1]. The logistic function at k ln3 is 3^k / (3^k + 1), so
+    SiLU gives ln3 [0, 3/4, 9/5, -1/4] exactly. linear2 = diag(1, 2, 1, 1) plus 4 at
+    [0, 3] (not symmetric), b2 = [1, 0, 0, 0]: output [1 - ln3, 3/2 ln3, 9/5 ln3, -1/4 ln3].
+    A ReLU in place of SiLU, a missing LayerNorm, a transposed weight or a dropped bias
+    each moves at least one entry by more than 0.2."""
+    d = 4
+    P = {"f.norm.weight": np.sqrt(5.0) * LN3 * np.array([1 / 3, 1.0, 1.0, 1 / 3]),
+         "f.norm.bias": np.array([0.0, LN3, 0.0, 0.0])}
+    W1 = np.zeros((d, d))
+    for i in range(d):
+        W1[i, (i + 1) % d] = 1.0
+    P["f.linear1.weight"], P["f.linear1.bias"] = W1, np.array([0.0, 0.0, LN3, 0.0])
+    W2 = np.diag([1.0, 2.0, 1.0, 1.0])
+    W2[0, 3] = 4.0
+    P["f.linear2.weight"], P["f.linear2.bias"] = W2, np.array([1.0, 0.0, 0.0, 0.0])
+    x = np.array([[1.0, 2.0, 3.0, 4.0], [10.0, 13.0, 16.0, 19.0]])
+    row = np.array([1.0 - LN3, 1.5 * LN3, 1.8 * LN3, -0.25 * LN3])
+    return x, P, np.stack([row, row])
+
+
+def check_feed_forward_closed_form():
+    x, P, expect = ffn_closed_form_case()
+    np.testing.assert_allclose(oracle.feed_forward(x, P, "f.", 0.0), expect, rtol=1e-13, atol=1e-13)
+
+
+def test_feed_forward_closed_form():
+    check_feed_forward_closed_form()
+
+
+def check_block_with_live_ffn():
+    """A block whose only non-zero module is the first FFN (the closed-form one above, 4
+    wide): output = LN_out(x + FFN(x) / 2), so the half step acts on a non-constant,
+    SiLU-shaped module output."""
+    d, f, k = 4, 4, 5
+    cfg = dict(n_heads=1, rope_base=5000.0, ln_eps=0.0, bn_eps=1e-5)
+    P = _zero_block(d, f, k)
+    x, F, ffn = ffn_closed_form_case()
+    for n in ("norm.weight", "norm.bias", "linear1.weight", "linear1.bias", "linear2.weight",
+              "linear2.bias"):
+        P["layers.0.ff1." + n] = F["f." + n]
+    out = oracle.conformer_block(x, P, 0, cfg)
+    pre = x + 0.5 * ffn
+    mu = pre.mean(1, keepdims=True)
+    sd = np.sqrt(((pre - mu) ** 2).mean(1, keepdims=True))
+    np.testing.assert_allclose(out, (pre - mu) / sd, rtol=1e-12, atol=1e-12)
+
+
+def test_block_with_live_ffn():
+    check_block_with_live_ffn()
+
+
+# ------------------------------------------------------------------ subsampling
+
+def check_subsample_relu_between_convs():
+    """Two 1-channel stride-2 convs that pass the centre tap only (weight 1 at tap 2):
+    subsample(x)[u] = relu(relu(x[4u] + b1) + b2). With b1 = -1 and b2 = +1, an input of
+    [-3, 0, 3, ...] at the kept positions shows whether the ReLU sits after each conv:
+    with it, x[4u] = -3 gives relu(0) + ... = 1; without the inner one it gives -3."""
+    T = 13
+    x = np.zeros((T, 1))
+    x[0::4, 0] = [-3.0, 0.5, 3.0, -0.5]
+    w = np.zeros((1, 1, 5))
+    w[0, 0, 2] = 1.0
+    P = {"pre.conv1.weight": w, "pre.conv1.bias": np.array([-1.0]),
+         "pre.conv2.weight": w, "pre.conv2.bias": np.array([1.0])}
+    out = oracle.subsample(x, P)
+    np.testing.assert_array_equal(out[:, 0], [1.0, 1.0, 3.0, 1.0])
+
+
+def test_subsample_relu_between_convs():
+    check_subsample_relu_between_convs()

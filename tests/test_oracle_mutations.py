@@ -91,3 +91,68 @@ def test_wrong_subsampling_padding_is_caught(pad):
     # only padding 2 maps the printed 99 -> 25 and 1999 -> 500
     f = lambda n: oracle.conv_out_len(oracle.conv_out_len(n, pad=pad), pad=pad)
     assert (f(99), f(1999)) != (25, 500)
+
+
+# ---- feed-forward, half steps and subsampling (pins in test_oracle_layers.py)
+
+from test_oracle_layers import (check_block_with_live_ffn, check_feed_forward_closed_form,  # noqa: E402
+                                check_subsample_relu_between_convs, test_block_order_and_half_steps)
+
+
+def _fails(check):
+    try:
+        check()
+    except AssertionError:
+        return True
+    return False
+
+
+def test_relu_for_silu_is_caught(monkeypatch):
+    assert not _fails(check_feed_forward_closed_form)
+    monkeypatch.setattr(oracle, "silu", oracle.relu)
+    assert _fails(check_feed_forward_closed_form)
+    assert _fails(check_block_with_live_ffn)
+
+
+def test_ffn_without_layer_norm_is_caught(monkeypatch):
+    def bad(x, P, pre, eps):
+        h = oracle.silu(oracle.linear(x, P[pre + "linear1.weight"], P[pre + "linear1.bias"]))
+        return oracle.linear(h, P[pre + "linear2.weight"], P[pre + "linear2.bias"])
+    monkeypatch.setattr(oracle, "feed_forward", bad)
+    assert _fails(check_feed_forward_closed_form)
+    assert _fails(check_block_with_live_ffn)
+
+
+def test_ffn_transposed_weight_is_caught(monkeypatch):
+    def bad(x, P, pre, eps):
+        y = oracle.layer_norm(x, P[pre + "norm.weight"], P[pre + "norm.bias"], eps)
+        h = oracle.silu(y @ P[pre + "linear1.weight"] + P[pre + "linear1.bias"])
+        return oracle.linear(h, P[pre + "linear2.weight"], P[pre + "linear2.bias"])
+    monkeypatch.setattr(oracle, "feed_forward", bad)
+    assert _fails(check_feed_forward_closed_form)
+
+
+def test_full_ffn_step_is_caught(monkeypatch):
+    """The macaron half steps replaced by full residual adds."""
+    def bad(x, P, i, cfg):
+        p = f"layers.{i}."
+        eps, bn_eps = cfg["ln_eps"], cfg["bn_eps"]
+        x = x + oracle.feed_forward(x, P, p + "ff1.", eps)
+        y = oracle.layer_norm(x, P[p + "att.norm.weight"], P[p + "att.norm.bias"], eps)
+        x = x + oracle.mhsa_rope(y, P, p + "att.", cfg["n_heads"], cfg["rope_base"])
+        x = x + oracle.conv_module(x, P, p + "conv.", eps, bn_eps)
+        x = x + oracle.feed_forward(x, P, p + "ff2.", eps)
+        return oracle.layer_norm(x, P[p + "norm_out.weight"], P[p + "norm_out.bias"], eps)
+    assert not _fails(check_block_with_live_ffn)
+    monkeypatch.setattr(oracle, "conformer_block", bad)
+    assert _fails(check_block_with_live_ffn)
+    assert _fails(test_block_order_and_half_steps)
+
+
+def test_subsampling_without_inner_relu_is_caught(monkeypatch):
+    def bad(mel, P):
+        h = oracle.conv1d(mel, P["pre.conv1.weight"], P["pre.conv1.bias"], stride=2, pad=2)
+        return oracle.relu(oracle.conv1d(h, P["pre.conv2.weight"], P["pre.conv2.bias"], stride=2, pad=2))
+    assert not _fails(check_subsample_relu_between_convs)
+    monkeypatch.setattr(oracle, "subsample", bad)
+    assert _fails(check_subsample_relu_between_convs)
