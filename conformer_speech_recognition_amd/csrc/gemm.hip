@@ -944,6 +944,28 @@ int gemm_split_slices(DType dt, int qbits, AMode am, Epi ep, const GemmParams& p
   return splitk_slices(p, tile_count(p, BM, BN), KB, ep);
 }
 
+int gemm_shape_id(DType dt, int qbits, AMode am, Epi ep, const GemmParams& p) {
+  if (dt == DT_F32) {
+    if (am == A_F32) am = A_PLAIN;
+    if (am == A_CONV_F32) am = A_CONV;
+  }
+  bool direct = direct_path(dt, qbits, am, ep, p);
+  if (qbits != 0) direct = dequant_first(qbits, am, ep, p);
+  if (!direct) {
+    int BM, BN;
+    tiles_geometry(ep, p, BM, BN);
+    return BN == 64 ? GEMM_REG_128x64 : GEMM_REG_128x128;
+  }
+  GemmParams q = p;
+  if (qbits != 0) { q.part = nullptr; q.part_cap = 0; }   // the expanded weights fill it
+  switch (dl_shape(am, q)) {
+    case DL_WIDE: return GEMM_DMA_256x256;
+    case DL_DUAL: return GEMM_DMA_256x128_K32;
+    case DL_LONGK: return GEMM_DMA_256x128_K64;
+    default: return GEMM_DMA_128x128;
+  }
+}
+
 static hipError_t launch_gemm_impl(DType dt, int qbits, AMode am, Epi ep, const GemmParams& p,
                                    hipStream_t s);
 

@@ -314,7 +314,8 @@ Layout layout(const gigaam_config& c) {
     o.no_g = take(d * 4); o.no_b = take(d * 4);
     L.layers.push_back(o);
   }
-  L.head_w = take((size_t)c.n_classes * d * es);
+  // the CTC head stays fp32 whatever the encoder's type: its logits decide the argmax
+  L.head_w = take((size_t)c.n_classes * d * 4);
   L.head_b = take((size_t)c.n_classes * 4);
   L.total = off;
   return L;
@@ -491,7 +492,7 @@ extern "C" int gigaam_pack_weights(const gigaam_config* cfg, const float* canoni
   }
   {
     const float* w = P.get("head.weight");
-    for (size_t i = 0; i < (size_t)c.n_classes * d; ++i) P.put_w(L.head_w, i, w[i]);
+    for (size_t i = 0; i < (size_t)c.n_classes * d; ++i) P.put_f(L.head_w, i, w[i]);
     P.copy_f(L.head_b, "head.bias", c.n_classes);
   }
   if (P.err) return fail(GIGAAM_E_INVAL, "a quantised weight is not an integer in [-(2^(b-1)-1), 2^(b-1)-1]");
@@ -678,13 +679,14 @@ int run(gigaam_model* m, const float* pcm, const int32_t* lengths, int32_t B, in
   };
   // defer: a residual GEMM whose split-K slices (if it splits) the next LayerNorm adds
   auto G = [&](const char* name, AMode am, Epi ep, int wq, const GemmParams& gp,
-               int* defer = nullptr) -> int {
+               int* defer = nullptr, DType gdt = DT_F32, bool own_type = true) -> int {
     GemmParams q = gp;
     if (c.dtype != GIGAAM_F32) {
       q.part = (float*)(W + w.part);
       q.part_cap = kSplitPartFloats;
     }
-    LAUNCH(name, launch_gemm(dt, wq, am, ep, q, s, stage == STAGE_NONE ? defer : nullptr));
+    const DType t = own_type ? dt : gdt;
+    LAUNCH(name, launch_gemm(t, wq, am, ep, q, s, stage == STAGE_NONE ? defer : nullptr));
     return GIGAAM_OK;
   };
   auto lin = [&](const Lin& l, int M, int N, int K, const void* A, int lda, void* Cp, int ldc,
@@ -782,8 +784,10 @@ int run(gigaam_model* m, const float* pcm, const int32_t* lengths, int32_t B, in
   }
   // ---- CTC head + log-softmax + argmax, then greedy collapse
   {
+    // fp32 operands and weights for every encoder type (the fp32 residual stream x is
+    // read as it is, not rounded to the 16-bit type)
     GemmParams gh = gemm(U_tot, C, d, x, d, P + L.head_w, nullptr, (const float*)(P + L.head_b), logits, C);
-    if ((rc = G("gemm.head", A_F32, E_F32, false, gh))) return rc;
+    if ((rc = G("gemm.head", A_PLAIN, E_F32, 0, gh, nullptr, DT_F32, false))) return rc;
   }
   LAUNCH("logsoftmax_argmax", launch_logsoftmax_argmax(logits, C, B, U_max, md.cuU, log_probs, fids, s));
   LAUNCH("ctc_collapse", launch_collapse(fids, B, U_max, md.cuU, C - 1, token_ids, n_tokens, s));
@@ -834,6 +838,48 @@ extern "C" int gigaam_debug_gemm(int32_t dtype, int32_t M, int32_t N, int32_t K,
   return GIGAAM_OK;
 }
 
+extern "C" int gigaam_debug_gemm_role(int32_t dtype, int32_t a_mode, int32_t epilogue, int32_t M,
+                                      int32_t N, int32_t K, const void* A_dev, const void* A2_dev,
+                                      int32_t nsplit, const void* W_dev, const void* scale_dev,
+                                      const float* bias_dev, float alpha, void* C_dev, float* part_dev,
+                                      size_t part_floats, int32_t* slices_host, int32_t* shape_host,
+                                      void* hip_stream) {
+  if (dtype < GIGAAM_F32 || dtype > GIGAAM_W4F16) return fail(GIGAAM_E_INVAL, "dtype %d", dtype);
+  if (a_mode != GIGAAM_GEMM_A_PLAIN && a_mode != GIGAAM_GEMM_A_DUAL)
+    return fail(GIGAAM_E_INVAL, "a_mode %d", a_mode);
+  if (epilogue != GIGAAM_GEMM_E_STORE && epilogue != GIGAAM_GEMM_E_SILU && epilogue != GIGAAM_GEMM_E_GLU &&
+      epilogue != GIGAAM_GEMM_E_RESID && epilogue != GIGAAM_GEMM_E_F32)
+    return fail(GIGAAM_E_INVAL, "epilogue %d", epilogue);
+  if (M < 1 || N < 1 || K < 1) return fail(GIGAAM_E_INVAL, "bad shape %d x %d x %d", M, N, K);
+  if (K % (dtype == GIGAAM_F32 ? 32 : 64)) return fail(GIGAAM_E_INVAL, "K %d not a multiple of the k-tile", K);
+  if (N % 4) return fail(GIGAAM_E_INVAL, "N %d not a multiple of 4", N);
+  const int qb = qbits_of(dtype);
+  if (!A_dev || !W_dev || !C_dev || (qb && !scale_dev)) return fail(GIGAAM_E_INVAL, "NULL pointer");
+  if (a_mode == GIGAAM_GEMM_A_DUAL) {
+    if (!A2_dev) return fail(GIGAAM_E_INVAL, "NULL A2 for the dual mode");
+    if (nsplit <= 0 || nsplit >= N || nsplit % 128) return fail(GIGAAM_E_INVAL, "nsplit %d", nsplit);
+    if (epilogue != GIGAAM_GEMM_E_STORE) return fail(GIGAAM_E_INVAL, "dual mode stores only");
+    if ((uintptr_t)A2_dev & 15) return fail(GIGAAM_E_INVAL, "A2 not 16-byte aligned");
+  }
+  if (epilogue == GIGAAM_GEMM_E_GLU && N % 64) return fail(GIGAAM_E_INVAL, "GLU needs N %% 64 == 0");
+  if (part_dev && ((uintptr_t)part_dev & 15))
+    return fail(GIGAAM_E_INVAL, "partial-sum buffer not 16-byte aligned");
+  if (((uintptr_t)A_dev & 15) || ((uintptr_t)W_dev & 15) || ((uintptr_t)C_dev & 15))
+    return fail(GIGAAM_E_INVAL, "A / W / C not 16-byte aligned");
+  const int ldc = epilogue == GIGAAM_GEMM_E_GLU ? N / 2 : N;
+  GemmParams p = gemm(M, N, K, A_dev, K, W_dev, scale_dev, bias_dev, C_dev, ldc, alpha);
+  p.A2 = A2_dev;
+  p.nsplit = nsplit;
+  p.part = part_dev;
+  p.part_cap = part_dev ? (long)std::min(part_floats, (size_t)LONG_MAX) : 0;
+  const AMode am = (AMode)a_mode;
+  const Epi ep = (Epi)epilogue;
+  if (slices_host) *slices_host = gemm_split_slices((DType)dtype, qb, am, ep, p);
+  if (shape_host) *shape_host = gemm_shape_id((DType)dtype, qb, am, ep, p);
+  HIP_TRY(launch_gemm((DType)dtype, qb, am, ep, p, (hipStream_t)hip_stream));
+  return GIGAAM_OK;
+}
+
 extern "C" int gigaam_debug_mlp(int32_t dtype, int32_t M, int32_t d, int32_t f, const void* y_dev,
                                 const void* W1_dev, const float* b1_dev, const void* W2_dev,
                                 const float* b2_dev, float alpha, float* x_dev, float* part_dev,
@@ -859,6 +905,8 @@ extern "C" int gigaam_debug_attention(int32_t dtype, int32_t d_model, int32_t n_
   if (batch < 1 || batch > GIGAAM_MAX_BATCH) return fail(GIGAAM_E_INVAL, "batch %d", batch);
   if (!frames_host || !qkv_dev || !out_dev || !workspace) return fail(GIGAAM_E_INVAL, "NULL pointer");
   if ((uintptr_t)workspace & 255) return fail(GIGAAM_E_INVAL, "workspace not 256-B aligned");
+  if (((uintptr_t)qkv_dev & 15) || ((uintptr_t)out_dev & 15))
+    return fail(GIGAAM_E_INVAL, "qkv / out not 16-byte aligned");
   if (n_heads < 1 || d_model % n_heads) return fail(GIGAAM_E_INVAL, "d_model %d / n_heads %d", d_model, n_heads);
   const int dk = d_model / n_heads;
   if (dk != 48 && dk != 64) return fail(GIGAAM_E_UNSUPPORTED, "head size %d", dk);

@@ -51,6 +51,12 @@ hipError_t launch_gemm(DType dt, int qbits, AMode am, Epi ep, const GemmParams& 
                        hipStream_t s, int* deferred_ks = nullptr);
 // K slices launch_gemm uses for these arguments (1: no split)
 int gemm_split_slices(DType dt, int qbits, AMode am, Epi ep, const GemmParams& p);
+// Kernel shape launch_gemm uses for these arguments (the GIGAAM_GEMM_* ids of gigaam.h)
+enum GemmShape {
+  GEMM_REG_128x64 = 1, GEMM_REG_128x128 = 2, GEMM_DMA_256x256 = 3, GEMM_DMA_256x128_K32 = 4,
+  GEMM_DMA_256x128_K64 = 5, GEMM_DMA_128x128 = 6
+};
+int gemm_shape_id(DType dt, int qbits, AMode am, Epi ep, const GemmParams& p);
 
 // Fused macaron FFN for few rows: x += alpha * (W2 SiLU(W1 y + b1) + b2) without the hidden
 // activations in HBM (16-bit weights, d 768 or 1024, f a multiple of 256, at most

@@ -88,6 +88,12 @@ __device__ __forceinline__ void ln_finish(const LnParams& p, float (&v)[4 * NI],
       cs[lane] = cv;
       cs[HALF + lane] = sv;
     }
+    // the reads below take other lanes' entries: order them after every lane's stores
+    // (wavefront-scope release / acquire around a wave barrier, so the compiler may not
+    // move an LDS read above the stores it depends on)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // a lane's 4 consecutive features sit in one half of one head (4 divides d_k / 2), so
     // their partners, cosines and sines are 16-byte LDS reads
     float r[4 * NI];

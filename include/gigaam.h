@@ -50,7 +50,8 @@ enum {
 };
 
 /* Arithmetic of the encoder GEMMs and attention. Residual stream, norms, soft-max,
- * frontend and head soft-max are always fp32.                                        */
+ * frontend and the CTC head (its weights, its product with the fp32 encoder output, and
+ * the log-softmax) are always fp32.                                                  */
 enum {
   GIGAAM_F32 = 0,    /* fp32 weights and operands (fp32 MFMA)                         */
   GIGAAM_F16 = 1,    /* fp16 weights and GEMM/attention operands, fp32 accumulate     */
@@ -96,9 +97,15 @@ int32_t gigaam_version(void);
 const char* gigaam_last_error(void);
 
 /* Host arithmetic, no GPU: frame counts of one clip of n_samples samples.
- * mel = floor((n - 320)/160) + 1 (un-centred STFT), sub = floor((mel - 1)/2) + 1,
- * enc = floor((sub - 1)/2) + 1 (each Conv1d k5 s2 p2). Any output pointer may be NULL.
- * Error: GIGAAM_E_INVAL if n_samples < 320.                                           */
+ * mel = floor((n - 320)/160) + 1: window 320, hop 160, no centring ("GigaAM v3 MLX"
+ * card, Frontend configuration); sub = floor((mel - 1)/2) + 1 and
+ * enc = floor((sub - 1)/2) + 1: each of the two Conv1d (kernel 5, stride 2, padding 2)
+ * halves the frames, a subsampling factor of 4 (same section; "GigaAM on MLX: the
+ * transcripts matched, but the model was broken", What we're porting). The padding is
+ * the one that reproduces the printed shapes: 1 s gives 99 mel frames and 25 encoder
+ * frames ("GigaAM v3 MLX" card, Selected validation results), 20 s gives 1,999 and about
+ * 500 ("GigaAM MLX port for Mac", Where the time goes). Any output pointer may be NULL.
+ * Error: GIGAAM_E_INVAL if n_samples < 320 (no complete window).                     */
 int gigaam_frames(int32_t n_samples, int32_t* mel_frames, int32_t* sub_frames,
                   int32_t* enc_frames);
 
@@ -164,7 +171,14 @@ int gigaam_workspace_bytes(const gigaam_model* model, int32_t batch, int32_t max
                            size_t* bytes);
 
 /* ---------------------------------------------------------------------------------
- * Encode a padded batch.
+ * Encode a padded batch: the whole path of the file header for every clip, log-mel
+ * frontend ("GigaAM v3 MLX" card, Frontend configuration), two stride-2 Conv1d and the
+ * Conformer blocks ("GigaAM on MLX: the transcripts matched, but the model was broken",
+ * What we're porting, Trap 1 and Trap 2; "GigaAM MLX port for Mac", What is inside the
+ * model), CTC log-softmax and greedy collapse with blank = n_classes - 1 ("GigaAM v3
+ * RNNT - MLX" card, Notes for other runtimes). A clip's outputs are those of the clip
+ * encoded alone on its valid samples: padding never reaches a valid output (each time
+ * convolution sees zeros outside the clip, attention masks the keys past its end).
  *   pcm_dev      float [batch][pcm_stride] 16 kHz samples; clip b uses its first
  *                lengths_host[b] samples (the rest is never read).
  *   lengths_host int32 [batch], each in [320, pcm_stride].
@@ -222,6 +236,41 @@ int gigaam_debug_gemm(int32_t dtype, int32_t M, int32_t N, int32_t K, const void
                       float* C_dev, float* part_dev, size_t part_floats, int32_t* slices_host,
                       void* hip_stream);
 
+/* Diagnostics: one encoder GEMM role on its own, with the A operand mode and the fused
+ * epilogue the encoder launches it with, through the same kernel selection:
+ *   P[m][n] = sum_k A'[m][k] * W[n][k] + bias[n]           (fp32 accumulate)
+ * a_mode:  GIGAAM_GEMM_A_PLAIN  A' = A_dev [M][K];
+ *          GIGAAM_GEMM_A_DUAL   A' row m = A_dev row m for output columns n < nsplit and
+ *                               A2_dev row m for the others (the q/k/v projection: q and k
+ *                               from the rotated LayerNorm output, v from the plain one);
+ *                               nsplit a multiple of 128 in (0, N); epilogue STORE only.
+ * epilogue: GIGAAM_GEMM_E_STORE C T [M][N]    = T(P)
+ *           GIGAAM_GEMM_E_SILU  C T [M][N]    = T(P * sigmoid(P))              (FFN up)
+ *           GIGAAM_GEMM_E_GLU   C T [M][N/2]  = T(value * sigmoid(gate)): W's rows come in
+ *                               groups of 64, 32 value rows then their 32 gate rows; the
+ *                               output column of value row 64 q + j is 32 q + j (N % 64 == 0)
+ *           GIGAAM_GEMM_E_RESID C float [M][N] += alpha * P (in place: the residual stream)
+ *           GIGAAM_GEMM_E_F32   C float [M][N] = P
+ * T = the storage type of `dtype` (GIGAAM_F32: fp32 everything; GIGAAM_F16 / BF16; the
+ * quantised dtypes: fp16 A and C, W the packed rows with scale_dev as in
+ * gigaam_debug_gemm). A_dev, A2_dev, W_dev, C_dev 16-byte aligned; bias_dev float [N] or
+ * NULL; part_dev / part_floats / slices_host as in gigaam_debug_gemm (a split K sum is
+ * always finished by the reduce kernel here). shape_host (may be NULL) receives the
+ * kernel shape used, one of GIGAAM_GEMM_REG_* (register-staged loads, 4 waves) or
+ * GIGAAM_GEMM_DMA_* (direct-to-LDS pipeline, 8 waves). K must be a multiple of 64 (32
+ * for GIGAAM_F32). Errors: GIGAAM_E_INVAL, GIGAAM_E_HIP.                             */
+enum { GIGAAM_GEMM_A_PLAIN = 0, GIGAAM_GEMM_A_DUAL = 2 };
+enum { GIGAAM_GEMM_E_STORE = 0, GIGAAM_GEMM_E_SILU = 1, GIGAAM_GEMM_E_GLU = 4,
+       GIGAAM_GEMM_E_RESID = 5, GIGAAM_GEMM_E_F32 = 6 };
+enum { GIGAAM_GEMM_REG_128x64 = 1, GIGAAM_GEMM_REG_128x128 = 2, GIGAAM_GEMM_DMA_256x256 = 3,
+       GIGAAM_GEMM_DMA_256x128_K32 = 4, GIGAAM_GEMM_DMA_256x128_K64 = 5,
+       GIGAAM_GEMM_DMA_128x128 = 6 };
+int gigaam_debug_gemm_role(int32_t dtype, int32_t a_mode, int32_t epilogue, int32_t M, int32_t N,
+                           int32_t K, const void* A_dev, const void* A2_dev, int32_t nsplit,
+                           const void* W_dev, const void* scale_dev, const float* bias_dev,
+                           float alpha, void* C_dev, float* part_dev, size_t part_floats,
+                           int32_t* slices_host, int32_t* shape_host, void* hip_stream);
+
 /* Diagnostics: a fused variant of the macaron FFN for few rows (hidden activations kept on
  * chip), measured against the encoder's two GEMMs, which the encoder uses instead:
  *   x[m][n] += alpha * (sum_j W2[n][j] h[m][j] + b2[n]),
@@ -240,7 +289,8 @@ int gigaam_debug_mlp(int32_t dtype, int32_t M, int32_t d, int32_t f, const void*
 /* Diagnostics: the encoder's attention kernel on its own, over packed clips.
  * frames_host int32 [batch]: frames U_b of each clip (>= 1); qkv_dev [sum U_b][3 d_model]
  * holds q | k | v per frame in the storage type of `dtype` (fp32, fp16, bf16;
- * the quantised dtypes = fp16); out_dev [sum U_b][d_model] the same type. d_model / n_heads must
+ * the quantised dtypes = fp16); out_dev [sum U_b][d_model] the same type. qkv_dev and
+ * out_dev must be 16-byte aligned (the kernel moves 16 bytes per access). d_model / n_heads must
  * be 48 or 64. workspace: device memory of at least
  *   16 * (batch + 1) + 16 * sum U_b + 4096 bytes (256-B aligned).
  * Errors: GIGAAM_E_INVAL, GIGAAM_E_WORKSPACE, GIGAAM_E_UNSUPPORTED, GIGAAM_E_HIP.        */

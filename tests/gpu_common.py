@@ -19,12 +19,32 @@ import oracle  # noqa: E402
 import synth  # noqa: E402
 
 # fp32 path: encoder output within 1e-4 and token ids bit-exact; fp16/bf16/int8 paths:
-# encoder output within 5e-2 and >= 99.5% per-frame argmax agreement, where a frame whose
-# oracle top choices lie closer together than the path's own log-prob deviation counts as
-# agreeing when the GPU picks one of them (random-init heads have many such near-ties).
+# encoder output within 5e-2 and >= 99.5% per-frame argmax agreement.
 TOL_F32 = 1e-4
 TOL_LOW = 5e-2
 ARGMAX_AGREE = 0.995
+
+# Near-tie bound of the argmax check, fixed from the arithmetic before any run (it never
+# depends on the deviation a run measures). A 16-bit path rounds every GEMM and attention
+# operand to its type: unit roundoff u = 2^-11 (fp16; also the activations of the
+# weight-only quantised paths) or 2^-8 (bf16). The encoder output is a LayerNorm output of
+# unit scale, so its error is of order u, and it moves a CTC logit by about u * sigma_z,
+# sigma_z = the spread (standard deviation over the classes) of the oracle's logits of the
+# frame, i.e. the head's logit scale. The two logits of a flipped pair can move apart by
+# twice that, and the errors of the 16 to 24 blocks add up: tau = 4 u sigma_z. A frame
+# whose oracle top-2 margin is below tau may legitimately resolve either way at that
+# precision ("classified" agreement excuses only those); a flip across a wider margin is a
+# wrong answer. The raw agreement (identical ids) is asserted beside it.
+UNIT_ROUNDOFF = {"f32": 2.0 ** -24, "f16": 2.0 ** -11, "bf16": 2.0 ** -8,
+                 "w8f16": 2.0 ** -11, "w6f16": 2.0 ** -11, "w4f16": 2.0 ** -11}
+NEAR_TIE_FACTOR = 4.0
+# raw floors: fp16 activations (including the quantised-weight paths) keep the north-star
+# 99.5% on identical ids; bf16 activations carry 8 significant bits, and with the logit
+# margins of random heads (median ~0.1) a bf16 encoder flips ~1% of the frames whose
+# margin is a few thousandths, so its raw floor is 98.5% and the 99.5% bar applies to the
+# classified agreement.
+RAW_FLOOR = {"f16": 0.995, "w8f16": 0.995, "w6f16": 0.995, "w4f16": 0.995, "bf16": 0.985}
+MARGIN_EDGES = (1e-3, 3e-3, 1e-2, 3e-2, 1e-1)
 
 
 def say(msg: str):
@@ -63,20 +83,71 @@ def clip_rows(lens, b, which=2):
     return start, start + fr[b][which]
 
 
-def argmax_agreement(gpu_ids: np.ndarray, ref_logp: np.ndarray, lp_dev: float = 0.0):
+def near_tie_bound(ref_logp: np.ndarray, dtype: str) -> np.ndarray:
+    """tau per frame: NEAR_TIE_FACTOR * u(dtype) * (std of the oracle's logits over the
+    classes; log-probs differ from logits by a per-frame constant)."""
+    ref_logp = np.asarray(ref_logp, dtype=np.float64)
+    return NEAR_TIE_FACTOR * UNIT_ROUNDOFF[dtype] * ref_logp.std(axis=1)
+
+
+def top2_margins(ref_logp: np.ndarray) -> np.ndarray:
+    """Oracle gap between the best and the second-best class of each frame."""
+    s = np.sort(np.asarray(ref_logp, dtype=np.float64), axis=1)
+    return s[:, -1] - s[:, -2]
+
+
+def margin_histogram(margins: np.ndarray) -> str:
+    edges = (0.0,) + MARGIN_EDGES + (np.inf,)
+    counts = np.histogram(margins, bins=edges)[0]
+    labels = [f"<{e:g}" for e in MARGIN_EDGES] + [f">={MARGIN_EDGES[-1]:g}"]
+    return " ".join(f"{l}:{c}" for l, c in zip(labels, counts))
+
+
+def argmax_agreement(gpu_ids: np.ndarray, ref_logp: np.ndarray, dtype: str):
     """Per-frame greedy-id agreement with the oracle.
 
-    Returns (raw, tie_aware, gap, flips): raw is the fraction of frames with identical
-    ids; gap[t] is how far below the oracle's best log-prob the GPU's pick lies (0 where
-    they agree); flips are the disagreeing frames.  When every log-prob of a frame is
-    within lp_dev of the oracle's, the GPU's pick can only differ where gap <= 2 lp_dev,
-    and there both picks are correct at that precision: tie_aware counts such frames as
-    agreeing (a flip with a larger gap is a wrong answer and counts against it)."""
+    Returns a dict: raw = fraction of frames with identical ids; classified = fraction
+    that agree or whose oracle gap between the two picks is below the fixed near-tie
+    bound tau (near_tie_bound); gap[t] = how far below the oracle's best log-prob the
+    GPU's pick lies (0 where they agree); flips = disagreeing frames; wide = flips whose
+    gap exceeds tau (wrong answers); margins = oracle top-2 margins; tau per frame."""
     ref_logp = np.asarray(ref_logp, dtype=np.float64)
     ref = oracle.greedy_ids(ref_logp)
+    gpu_ids = np.asarray(gpu_ids)
     rows = np.arange(len(ref))
-    gap = ref_logp[rows, ref] - ref_logp[rows, np.asarray(gpu_ids)]
+    gap = ref_logp[rows, ref] - ref_logp[rows, gpu_ids]
+    tau = near_tie_bound(ref_logp, dtype)
     flips = np.nonzero(gpu_ids != ref)[0]
-    raw = float(np.mean(gpu_ids == ref))
-    tie = float(np.mean((gpu_ids == ref) | (gap <= 2.0 * lp_dev)))
-    return raw, tie, gap, flips
+    wide = flips[gap[flips] > tau[flips]]
+    return dict(raw=float(np.mean(gpu_ids == ref)),
+                classified=1.0 - len(wide) / max(len(ref), 1),
+                gap=gap, flips=flips, wide=wide, margins=top2_margins(ref_logp), tau=tau,
+                n=len(ref))
+
+
+class Agreement:
+    """Accumulates argmax agreement over clips and asserts the bars for one dtype."""
+
+    def __init__(self, dtype: str):
+        self.dtype = dtype
+        self.n = self.same = self.wide = 0
+        self.margins = []
+        self.flip_gaps = []
+
+    def add(self, a: dict):
+        self.n += a["n"]
+        self.same += int(round(a["raw"] * a["n"]))
+        self.wide += len(a["wide"])
+        self.margins.append(a["margins"])
+        self.flip_gaps += a["gap"][a["flips"]].tolist()
+
+    def report(self, tag: str):
+        m = np.concatenate(self.margins) if self.margins else np.zeros(0)
+        say(f"[{tag}] argmax over {self.n} frames: raw {self.same / self.n:.4f}, classified "
+            f"{1 - self.wide / self.n:.4f} ({self.wide} flips past the near-tie bound); oracle "
+            f"top-2 margins {margin_histogram(m)}; flip gaps "
+            f"{np.round(sorted(self.flip_gaps), 4).tolist()[:40]}")
+
+    def check(self):
+        assert 1 - self.wide / self.n >= ARGMAX_AGREE, (self.wide, self.n)
+        assert self.same / self.n >= RAW_FLOOR[self.dtype], (self.same, self.n)

@@ -228,6 +228,19 @@ def test_encode_argument_errors_before_any_launch(gg):
                                   fake, big, None) == gg.E_INVAL
 
 
+def test_debug_attention_rejects_misaligned_operands(gg):
+    """The attention kernel moves 16 bytes per access: q/k/v and out pointers that are not
+    16-byte aligned are refused before the launch (no GPU needed)."""
+    L = gg.lib()
+    fake = 1 << 20
+    frames = (ctypes.c_int32 * 2)(70, 5)
+    ok = 1 << 16
+    for qkv, out in ((fake + 2, fake), (fake, fake + 8), (fake + 4, fake + 4)):
+        assert L.gigaam_debug_attention(1, 768, 16, 2, frames, qkv, out, fake, ok, None) == gg.E_INVAL
+        assert "aligned" in L.gigaam_last_error().decode()
+    assert L.gigaam_debug_attention(1, 768, 16, 2, frames, fake, fake, fake + 16, ok, None) == gg.E_INVAL
+
+
 def test_workspace_bound_covers_every_length_mix(gg):
     L = gg.lib()
     c = gg.make_config(synth.workload_config("batch32"))
@@ -239,3 +252,29 @@ def test_workspace_bound_covers_every_length_mix(gg):
     assert L.gigaam_workspace_bytes(h, 32, 16000, ctypes.byref(nb)) == 0
     assert nb.value < big
     L.gigaam_destroy(h)
+
+
+def test_debug_gemm_role_validation(gg):
+    """Mode, epilogue, shape and alignment checks of the role entry happen before any
+    launch (no GPU needed)."""
+    L = gg.lib()
+    fake = 1 << 20
+    F = ctypes.c_float
+
+    def call(dt=1, am=0, ep=1, M=64, N=256, K=128, A=fake, A2=None, ns=0, W=fake, C=fake, part=None):
+        return L.gigaam_debug_gemm_role(dt, am, ep, M, N, K, A, A2, ns, W, None, None, F(1.0), C, part,
+                                        0, None, None, None)
+    assert call(dt=9) == gg.E_INVAL
+    assert call(am=1) == gg.E_INVAL                      # not a role mode
+    assert call(ep=3) == gg.E_INVAL                      # not a role epilogue
+    assert call(K=100) == gg.E_INVAL
+    assert call(N=250) == gg.E_INVAL
+    assert call(am=2, ep=0, A2=None, ns=128) == gg.E_INVAL          # dual without A2
+    assert call(am=2, ep=0, A2=fake, ns=100) == gg.E_INVAL          # split not 128-aligned
+    assert call(am=2, ep=0, A2=fake, ns=256) == gg.E_INVAL          # split not inside N
+    assert call(am=2, ep=1, A2=fake, ns=128) == gg.E_INVAL          # dual stores only
+    assert call(am=2, ep=0, A2=fake + 8, ns=128) == gg.E_INVAL      # misaligned A2
+    assert call(ep=4, N=96) == gg.E_INVAL                           # GLU needs 64-row groups
+    assert call(A=fake + 2) == gg.E_INVAL and call(W=fake + 2) == gg.E_INVAL and call(C=fake + 4) == gg.E_INVAL
+    assert call(part=fake + 4) == gg.E_INVAL
+    assert call(dt=3) == gg.E_INVAL                                  # quantised weights need scales

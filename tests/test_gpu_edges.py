@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_common import ARGMAX_AGREE, TOL_F32, TOL_LOW, argmax_agreement, model, say, workload
+from gpu_common import TOL_F32, TOL_LOW, Agreement, argmax_agreement, model, say, workload
 
 pytestmark = pytest.mark.gpu
 
@@ -22,7 +22,7 @@ def _batch(lengths, seed):
     return synth.pad_batch(sig)
 
 
-def _check_clip(out, b, ref, dtype):
+def _check_clip(out, b, ref, dtype, agg=None):
     u = ref["enc_out"].shape[0]
     assert out["n_frames"][b] == u
     enc = out["enc_out"][b, :u]
@@ -34,11 +34,11 @@ def _check_clip(out, b, ref, dtype):
         assert err <= TOL_F32, (b, u, err)
         np.testing.assert_array_equal(ids, oracle.greedy_ids(ref["log_probs"]))
         assert out["token_ids"][b, :n].tolist() == ref["tokens"]
-        return err, 1.0
+        return err
     lp_err = np.abs(out["log_probs"][b, :u] - ref["log_probs"]).max()
-    raw, tie, _, _ = argmax_agreement(ids, ref["log_probs"], lp_err)
+    agg.add(argmax_agreement(ids, ref["log_probs"], dtype))
     assert err <= TOL_LOW and lp_err <= TOL_LOW, (b, u, err, lp_err)
-    return err, tie
+    return err
 
 
 def _encode(name, pcm, lens):
@@ -56,16 +56,15 @@ def test_ragged_extremes(name):
     say(f"[edges] {name}: {len(lens)} clips, encoder frames "
         f"{[oracle.encoder_frames(int(n))[2] for n in lens]}")
     out = _encode(name, pcm, lens)
-    dtype = "f32" if cfg["dtype"] == "f32" else "low"
-    agree, frames = 0.0, 0
+    dtype = cfg["dtype"]
+    agg = Agreement(dtype) if dtype != "f32" else None
     for b, L in enumerate(lens):
         ref = oracle.encode_clip(pcm[b, :L], w, cfg)
-        err, tie = _check_clip(out, b, ref, dtype)
-        u = ref["enc_out"].shape[0]
-        agree += tie * u
-        frames += u
-        say(f"[edges] {name} clip {b} U={u}: enc max|d| {err:.3e}")
-    assert agree / frames >= ARGMAX_AGREE
+        err = _check_clip(out, b, ref, dtype, agg)
+        say(f"[edges] {name} clip {b} U={ref['enc_out'].shape[0]}: enc max|d| {err:.3e}")
+    if agg is not None:
+        agg.report(f"edges {name}")
+        agg.check()
 
 
 def test_largest_batch():

@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_common import ARGMAX_AGREE, TOL_F32, TOL_LOW, argmax_agreement, model, say, workload
+from gpu_common import TOL_F32, TOL_LOW, Agreement, argmax_agreement, model, say, workload
 from oracle import stream as ostream
 
 pytestmark = pytest.mark.gpu
@@ -91,8 +91,9 @@ def test_stream_at_thirty_seconds():
     u = ref["enc_out"].shape[0]
     err = np.abs(out["enc_out"][0, :u] - ref["enc_out"]).max()
     lp_err = np.abs(out["log_probs"][0, :u] - ref["log_probs"]).max()
-    raw, tie, gap, flips = argmax_agreement(out["frame_ids"][0, :u], ref["log_probs"], lp_err)
-    say(f"[stream] v3 30 s window: enc max|d| {err:.3e}, logp max|d| {lp_err:.3e}, "
-        f"agree {raw:.4f} (tie-aware {tie:.4f})")
+    agg = Agreement(cfg["dtype"])
+    agg.add(argmax_agreement(out["frame_ids"][0, :u], ref["log_probs"], cfg["dtype"]))
+    say(f"[stream] v3 30 s window: enc max|d| {err:.3e}, logp max|d| {lp_err:.3e}")
+    agg.report("stream v3 30 s")
     assert err <= TOL_LOW and lp_err <= TOL_LOW
-    assert tie >= ARGMAX_AGREE and raw >= 0.98
+    agg.check()

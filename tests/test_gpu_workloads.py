@@ -1,18 +1,18 @@
 """GPU parity at the full workload sizes, in the launch configuration the benchmark
-times (the whole padded batch in one gigaam_encode call). The oracle recomputes a
-sample of clips one by one (shortest, longest and one in between); every clip is also
-checked for shape, padding and CTC-collapse consistency.
+times (the whole padded batch in one gigaam_encode call). The oracle recomputes every clip
+of the two 32-clip batches, and a sample of the others (both ends of the long-form chunks,
+first / middle / last of the 64-clip batches); every clip is also checked for shape,
+padding and CTC-collapse consistency.
 
-Acceptance: encoder output and log-probs max|d| <= 5e-2 and >= 99.5% per-frame argmax
-agreement for the fp16 / bf16 / int8 / int6 / int4 paths, a disagreement counting as agreement only
-where the oracle's log-prob of the GPU's pick is within twice the clip's log-prob
-deviation of its best (a near-tie both precisions resolve correctly); the raw agreement
-is reported and must stay >= 98%."""
+Acceptance: encoder output and log-probs max|d| <= 5e-2; per-frame argmax agreement
+>= 99.5% where only flips across an oracle margin below the near-tie bound fixed from the
+arithmetic (gpu_common.near_tie_bound) are excused, and raw agreement (identical ids) at
+least the type's floor (99.5% for fp16 activations, 98.5% for bf16)."""
 import numpy as np
 import pytest
 
-from gpu_common import (ARGMAX_AGREE, TOL_LOW, argmax_agreement, device_pcm, model,
-                        oracle_clip, say, workload)
+from gpu_common import (TOL_LOW, Agreement, argmax_agreement, device_pcm, model, oracle_clip,
+                        say, workload)
 
 import oracle
 
@@ -20,18 +20,24 @@ pytestmark = pytest.mark.gpu
 
 CASES = {
     "v3_20s": [0],
-    "batch32": None,          # None: shortest, longest and median-length clip
-    "batch32_bf16": None,
-    "ml_long": [0],
-    "int8_b64": [0, 63],
-    "int6_b64": [0, 63],
-    "int4_b64": [0, 63],
+    "batch32": "all",
+    "batch32_bf16": "all",
+    "ml_long": [0, 9],
+    "int8_b64": [0, 31, 63],
+    "int6_b64": [0, 31, 63],
+    "int4_b64": [0, 31, 63],
 }
 
 
 def _sample(name):
-    if CASES[name] is not None:
-        return CASES[name]
+    lens = workload(name)[2]
+    if CASES[name] == "all":
+        return list(range(len(lens)))
+    return CASES[name]
+
+
+def _short_sample(name):
+    """shortest, longest and median-length clip"""
     lens = workload(name)[2]
     order = np.argsort(lens)
     return sorted({int(order[0]), int(order[-1]), int(order[len(order) // 2])})
@@ -74,27 +80,25 @@ def _check_structure(name, out):
 def test_workload_parity(name):
     out = _run(name)
     _check_structure(name, out)
-    worst, raw_n, agree_n, tot = 0.0, 0, 0, 0
+    dtype = workload(name)[0]["dtype"]
+    agg = Agreement(dtype)
+    worst = 0.0
     for b in _sample(name):
         ref = oracle_clip(name, b)
         u = ref["enc_out"].shape[0]
         err = np.abs(out["enc_out"][b, :u] - ref["enc_out"]).max()
         lp_err = np.abs(out["log_probs"][b, :u] - ref["log_probs"]).max()
-        raw, tie, gap, flips = argmax_agreement(out["frame_ids"][b, :u], ref["log_probs"],
-                                                lp_err)
+        a = argmax_agreement(out["frame_ids"][b, :u], ref["log_probs"], dtype)
+        agg.add(a)
         say(f"[{name}] clip {b} U={u}: enc max|d| {err:.3e}, logp max|d| {lp_err:.3e}, "
-            f"argmax agree {raw:.4f} (tie-aware {tie:.4f}), flips at oracle gaps "
-            f"{np.round(gap[flips], 4).tolist()}")
+            f"argmax raw {a['raw']:.4f} classified {a['classified']:.4f}, flips at oracle gaps "
+            f"{np.round(a['gap'][a['flips']], 4).tolist()} (tau {float(a['tau'].mean()):.2e})")
         assert lp_err <= TOL_LOW
         worst = max(worst, err)
-        raw_n += int(round(raw * u))
-        agree_n += int(round(tie * u))
-        tot += u
-    say(f"[{name}] worst enc max|d| {worst:.3e}, argmax agreement {raw_n / tot:.4f} "
-        f"(tie-aware {agree_n / tot:.4f})")
+    say(f"[{name}] worst enc max|d| {worst:.3e}")
+    agg.report(name)
     assert worst <= TOL_LOW
-    assert agree_n / tot >= ARGMAX_AGREE
-    assert raw_n / tot >= 0.98
+    agg.check()
 
 
 def test_clip_alone_matches_its_batch():
@@ -107,7 +111,8 @@ def test_clip_alone_matches_its_batch():
     out = _run(name)
     m = model(name)
     _, pcm, lens, _ = workload(name)
-    for b in _sample(name):
+    agg = Agreement("f16")
+    for b in _short_sample(name):
         L = int(lens[b])
         d = torch.from_numpy(pcm[b:b + 1, :L].copy()).cuda()
         one = m.encode(d, [L], want_enc=True)
@@ -121,11 +126,13 @@ def test_clip_alone_matches_its_batch():
         ref = oracle_clip(name, b)
         err = np.abs(enc - ref["enc_out"]).max()
         lp_err = np.abs(lp - ref["log_probs"]).max()
-        raw, tie, _, _ = argmax_agreement(one["frame_ids"].cpu().numpy()[0], ref["log_probs"], lp_err)
+        a = argmax_agreement(one["frame_ids"].cpu().numpy()[0], ref["log_probs"], "f16")
+        agg.add(a)
         say(f"[{name}] clip {b} alone U={u}: vs batch max|d| {d_batch:.3e}, vs oracle {err:.3e}, "
-            f"agree {raw:.4f} (tie-aware {tie:.4f})")
+            f"argmax raw {a['raw']:.4f} classified {a['classified']:.4f}")
         assert d_batch <= TOL_LOW and err <= TOL_LOW and lp_err <= TOL_LOW
-        assert tie >= ARGMAX_AGREE and raw >= 0.98
+    agg.report(name + " alone")
+    agg.check()
 
 
 def test_deterministic_and_poisoned_workspace():
