@@ -23,6 +23,7 @@ OK, E_INVAL, E_WORKSPACE, E_UNSUPPORTED, E_HIP = 0, -1, -2, -3, -4
 DTYPES = {"f32": 0, "f16": 1, "bf16": 2, "w8f16": 3, "w6f16": 4, "w4f16": 5}
 STAGE_MEL, STAGE_SUB, STAGE_LAYER = 0, 1, 2
 MAX_BATCH = 256
+NOALLOC_SCRATCH_BYTES = 64 << 20      # GIGAAM_NOALLOC_SCRATCH_BYTES
 
 
 def stage_sublayer(layer: int, part: int) -> int:
@@ -103,6 +104,7 @@ _SIGNATURES = {
     "gigaam_workspace_bytes": (ctypes.c_int, [_P, _I, _I, ctypes.POINTER(_SZ)]),
     "gigaam_encode": (ctypes.c_int, [_P, _P, _IP, _I, _I, _P, _SZ, _P, _P, _P, _P, _P, _IP, _P]),
     "gigaam_encode_stage": (ctypes.c_int, [_P, _P, _IP, _I, _I, _P, _SZ, _I, _P, _SZ, _P]),
+    "gigaam_encode_noalloc": (ctypes.c_int, [_P, _P, _IP, _I, _I, _P, _P, _P, _P, _P, _IP, _P]),
     "gigaam_debug_gemm": (ctypes.c_int, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _SZ, _IP, _P]),
     "gigaam_debug_gemm_role": (ctypes.c_int, [_I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P,
                                               ctypes.c_float, _P, _P, _SZ, _IP, _IP, _P]),
@@ -291,6 +293,22 @@ class Model:
                                    out["log_probs"].data_ptr(), out["token_ids"].data_ptr(),
                                    out["n_tokens"].data_ptr(), _ptr(out.get("frame_ids")),
                                    _ptr(out.get("enc_out")), nfr.ctypes.data_as(_IP), s))
+        out["n_frames"] = nfr
+        return out
+
+    def encode_noalloc(self, pcm, lengths, out: dict, stream=None) -> dict:
+        """gigaam_encode_noalloc into caller-provided outputs (``out`` holds log_probs,
+        token_ids, n_tokens and optionally frame_ids / enc_out device tensors shaped as
+        encode() returns them); the library uses its fixed scratch and allocates nothing."""
+        import torch
+        lens, lp = self._args(pcm, lengths)
+        B, stride = pcm.shape
+        nfr = np.zeros(B, dtype=np.int32)
+        s = (stream or torch.cuda.current_stream(self.device)).cuda_stream
+        _check(lib().gigaam_encode_noalloc(self._h, pcm.data_ptr(), lp, B, stride,
+                                           out["log_probs"].data_ptr(), out["token_ids"].data_ptr(),
+                                           out["n_tokens"].data_ptr(), _ptr(out.get("frame_ids")),
+                                           _ptr(out.get("enc_out")), nfr.ctypes.data_as(_IP), s))
         out["n_frames"] = nfr
         return out
 

@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <climits>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -570,9 +571,18 @@ Ws plan(const gigaam_config& c, int B, int T_tot, int S_tot, int U_tot, int nQ, 
   return w;
 }
 
+// packed mel rows past this (B clips of the longest length) overflow the row counters
+constexpr long long kMaxPackedRows = INT_MAX / 2;
+
 Ws plan_bound(const gigaam_config& c, int B, int max_samples) {
   int T, S, U;
   frame_counts(max_samples, T, S, U);
+  if ((long long)B * T > kMaxPackedRows) {       // no such batch fits a GPU: bound = "never"
+    Ws w;
+    std::memset(&w, 0, sizeof w);
+    w.total = SIZE_MAX;
+    return w;
+  }
   const int nQ = B * ((U + kQTile - 1) / kQTile);
   return plan(c, B, B * T, B * S, B * U, nQ, U);
 }
@@ -584,7 +594,9 @@ extern "C" int gigaam_workspace_bytes(const gigaam_model* m, int32_t batch, int3
   if (!m || !bytes) return fail(GIGAAM_E_INVAL, "NULL argument");
   if (batch < 1 || batch > GIGAAM_MAX_BATCH) return fail(GIGAAM_E_INVAL, "batch %d out of [1, %d]", batch, GIGAAM_MAX_BATCH);
   if (max_samples < 320) return fail(GIGAAM_E_INVAL, "max_samples %d < 320", max_samples);
-  *bytes = plan_bound(m->cfg, batch, max_samples).total;
+  const size_t total = plan_bound(m->cfg, batch, max_samples).total;
+  if (total == SIZE_MAX) return fail(GIGAAM_E_INVAL, "batch %d x %d samples too large", batch, max_samples);
+  *bytes = total;
   return GIGAAM_OK;
 }
 
@@ -814,6 +826,61 @@ extern "C" int gigaam_encode_stage(gigaam_model* model, const float* pcm_dev, co
   if (stage < 0) return fail(GIGAAM_E_INVAL, "stage %d out of range", stage);
   return run(model, pcm_dev, lengths_host, batch, pcm_stride, workspace, workspace_bytes, stage,
              out_dev, out_floats, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, hip_stream);
+}
+
+// --------------------------------------------------------------------------- fixed scratch
+// The workspace of gigaam_encode_noalloc, for callers that cannot allocate device memory:
+// a fixed array in the library's own device memory, one copy per GPU, held until the process
+// ends. Its name is a host-side stand-in in host code: every host use goes through the
+// device address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) char scratch[GIGAAM_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// device address of the current device's scratch (looked up once per device)
+int scratch_for_current_device(void** out) {
+  int dev = -1;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(GIGAAM_E_UNSUPPORTED, "device %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+    if (!ptr || ((uintptr_t)ptr & 255)) return fail(GIGAAM_E_HIP, "scratch address %p not 256-B aligned", ptr);
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return GIGAAM_OK;
+}
+}  // namespace
+
+extern "C" int gigaam_encode_noalloc(gigaam_model* model, const float* pcm_dev,
+                                     const int32_t* lengths_host, int32_t batch, int32_t pcm_stride,
+                                     float* log_probs_dev, int32_t* token_ids_dev, int32_t* n_tokens_dev,
+                                     int32_t* frame_ids_dev, float* enc_out_dev, int32_t* n_frames_host,
+                                     void* hip_stream) {
+  if (!model) return fail(GIGAAM_E_INVAL, "model is NULL");
+  if (!lengths_host) return fail(GIGAAM_E_INVAL, "NULL lengths");
+  if (batch < 1 || batch > GIGAAM_MAX_BATCH) return fail(GIGAAM_E_INVAL, "batch %d out of [1, %d]", batch, GIGAAM_MAX_BATCH);
+  int maxlen = 320;
+  for (int b = 0; b < batch; ++b) {
+    if (lengths_host[b] < 320 || lengths_host[b] > pcm_stride)
+      return fail(GIGAAM_E_INVAL, "lengths[%d] = %d outside [320, pcm_stride = %d]", b, lengths_host[b], pcm_stride);
+    maxlen = lengths_host[b] > maxlen ? lengths_host[b] : maxlen;
+  }
+  const size_t need = plan_bound(model->cfg, batch, maxlen).total;
+  if (need > (size_t)GIGAAM_NOALLOC_SCRATCH_BYTES)
+    return fail(GIGAAM_E_WORKSPACE, "this call needs %zu bytes of workspace, more than the %zu-byte fixed "
+                "scratch of the allocation-free entry point", need, (size_t)GIGAAM_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  int rc = scratch_for_current_device(&ws);
+  if (rc) return rc;
+  return run(model, pcm_dev, lengths_host, batch, pcm_stride, ws, GIGAAM_NOALLOC_SCRATCH_BYTES, STAGE_NONE,
+             nullptr, 0, log_probs_dev, token_ids_dev, n_tokens_dev, frame_ids_dev, enc_out_dev,
+             n_frames_host, hip_stream);
 }
 
 extern "C" int gigaam_debug_gemm(int32_t dtype, int32_t M, int32_t N, int32_t K, const void* A_dev,

@@ -203,6 +203,23 @@ int gigaam_encode(gigaam_model* model, const float* pcm_dev, const int32_t* leng
                   int32_t* frame_ids_dev, float* enc_out_dev, int32_t* n_frames_host,
                   void* hip_stream);
 
+/* Allocation-free variant of gigaam_encode, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments and outputs without the workspace pair. Its workspace is a fixed
+ * scratch array of GIGAAM_NOALLOC_SCRATCH_BYTES in the library's own device memory, one
+ * per GPU, held until the process ends (for example one clip of up to 30 s at d_model
+ * 1024, or any batch whose gigaam_workspace_bytes is at most that size). Calls needing
+ * more are refused with GIGAAM_E_WORKSPACE before any launch. The call allocates nothing.
+ * Every call on one GPU uses that GPU's single array: calls that overlap on one GPU (two
+ * streams, two threads) race and must be serialised by the caller. The array keeps the
+ * last call's contents; the encode never reads scratch it has not written in the same
+ * call, so nothing needs clearing.                                                     */
+#define GIGAAM_NOALLOC_SCRATCH_BYTES (64u << 20)
+int gigaam_encode_noalloc(gigaam_model* model, const float* pcm_dev, const int32_t* lengths_host,
+                          int32_t batch, int32_t pcm_stride, float* log_probs_dev,
+                          int32_t* token_ids_dev, int32_t* n_tokens_dev, int32_t* frame_ids_dev,
+                          float* enc_out_dev, int32_t* n_frames_host, void* hip_stream);
+
 /* Stage taps for parity diagnostics: run the path up to `stage` and copy that
  * tensor, packed over clips (rows of clip b follow those of clip b-1), as float32:
  *   GIGAAM_STAGE_MEL     [sum_b T_b][n_mels]     log-mel

@@ -278,3 +278,32 @@ def test_debug_gemm_role_validation(gg):
     assert call(A=fake + 2) == gg.E_INVAL and call(W=fake + 2) == gg.E_INVAL and call(C=fake + 4) == gg.E_INVAL
     assert call(part=fake + 4) == gg.E_INVAL
     assert call(dt=3) == gg.E_INVAL                                  # quantised weights need scales
+
+
+def test_noalloc_entry_validates_before_touching_the_gpu(gg):
+    """gigaam_encode_noalloc: bad lengths and batches larger than its fixed scratch are
+    refused before any device call (works without a GPU); the scratch size in the header
+    is the binding's."""
+    hdr = open(HEADER).read()
+    m = re.search(r"#define GIGAAM_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", hdr)
+    assert m and int(m.group(1)) << int(m.group(2)) == gg.NOALLOC_SCRATCH_BYTES
+    L = gg.lib()
+    c = gg.make_config(synth.workload_config("v3_20s"))
+    h = ctypes.c_void_p()
+    fake = 1 << 20
+    assert L.gigaam_create(ctypes.byref(c), fake, fake, fake, ctypes.byref(h)) == 0
+    I = ctypes.c_int32
+
+    def call(lengths, stride=320000):
+        n = len(lengths)
+        return L.gigaam_encode_noalloc(h, fake, (I * n)(*lengths), n, stride, fake, fake, fake, None, None,
+                                       None, None)
+    assert call([320000, 100]) == gg.E_INVAL
+    assert call([320001]) == gg.E_INVAL                                    # past the stride
+    assert call([320000] * 8) == gg.E_WORKSPACE                            # > 64 MiB of workspace
+    assert "scratch" in L.gigaam_last_error().decode()
+    nb = ctypes.c_size_t()
+    assert L.gigaam_workspace_bytes(h, 1, 480000, ctypes.byref(nb)) == 0
+    assert nb.value <= gg.NOALLOC_SCRATCH_BYTES                            # one 30 s clip fits
+    assert L.gigaam_workspace_bytes(h, 256, 2 ** 31 - 1, ctypes.byref(nb)) == gg.E_INVAL
+    L.gigaam_destroy(h)
