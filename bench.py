@@ -364,6 +364,62 @@ def library_gemm_leg(cfg, U, prof, reps=64, sets=16):
     return out
 
 
+def gemm_variants_leg(cfg, U, reps=30, sets=8):
+    """Each encoder GEMM role at this workload's U rows with every direct-load tile variant the
+    library builds (gigaam_debug_gemm_role with a shape request), beside the variant the encoder
+    picks. Weights rotate over `sets` copies; operands random; median of three timed loops of
+    `reps` launches, interleaved over the variants so that clock drift hits all alike."""
+    import torch
+    import conformer_speech_recognition_amd as gg
+    d, f = cfg["d_model"], cfg["d_ff"]
+    tt = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.half
+    dt = "bf16" if cfg["dtype"] == "bf16" else "f16"
+    roles = [("gemm.ffn_up", "plain", "silu", f, d), ("gemm.pw1_glu", "plain", "glu", 2 * d, d),
+             ("gemm.qkv", "dual", "store", 3 * d, d), ("gemm.ffn_down", "plain", "resid", d, f),
+             ("gemm.out_proj", "plain", "resid", d, d)]
+    st = torch.cuda.current_stream()
+    g = torch.Generator(device="cuda").manual_seed(9)
+    out = {}
+    for name, am, ep, N, K in roles:
+        A = torch.randn(U, K, device="cuda", generator=g).to(tt)
+        A2 = torch.randn(U, K, device="cuda", generator=g).to(tt) if am == "dual" else None
+        Ws = [(0.05 * torch.randn(N, K, device="cuda", generator=g)).to(tt) for _ in range(sets)]
+        b = torch.randn(N, device="cuda", generator=g)
+        C = (torch.zeros(U, N, device="cuda") if ep == "resid" else
+             torch.empty(U, N // 2 if ep == "glu" else N, device="cuda", dtype=tt))
+        times, chosen = {}, None
+        for v in [None] + list(gg.GEMM_SHAPE_IDS):
+            if v is not None and not v.startswith("dma_"):
+                continue
+            try:
+                chosen_v = gg.debug_gemm_role(dt, am, ep, A, Ws[0], C, bias=b, A2=A2,
+                                              nsplit=2 * d if am == "dual" else 0, split=False, shape=v)[2]
+            except gg.GigaamError:
+                continue
+            if v is None:
+                chosen = chosen_v
+                continue
+            times[v] = []
+        for _ in range(3):
+            for v in times:
+                for i in range(3):
+                    gg.debug_gemm_role(dt, am, ep, A, Ws[i % sets], C, bias=b, A2=A2,
+                                       nsplit=2 * d if am == "dual" else 0, split=False, shape=v)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                e0.record(st)
+                for i in range(reps):
+                    gg.debug_gemm_role(dt, am, ep, A, Ws[i % sets], C, bias=b, A2=A2,
+                                       nsplit=2 * d if am == "dual" else 0, split=False, shape=v)
+                e1.record(st)
+                e1.synchronize()
+                times[v].append(e0.elapsed_time(e1) * 1e3 / reps)
+        out[name] = {"M": U, "N": N, "K": K, "encoder_variant": chosen,
+                     "us_median": {v: round(float(np.median(t)), 2) for v, t in times.items()}}
+        del A, A2, Ws, C
+    return out
+
+
 def measured_peaks(dtype: str):
     """What this GPU sustains, beside the datasheet peaks: the vendor library's GEMM on a large
     square product in the workload's compute type (16384^3, fp32: 8192^3), and a plain device
@@ -409,6 +465,8 @@ def main():
     ap.add_argument("--graph", action="store_true", help="replay the encode as a captured graph")
     ap.add_argument("--cpu-budget", type=float, default=24.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the vendor-library GEMM and copy peak measurements (profiled runs)")
     ap.add_argument("--rnnt", action="store_true",
                     help="also time greedy RNNT decoding (character head, 34 classes) of every "
                          "encoded batch and report it beside the encoder line")
@@ -419,6 +477,8 @@ def main():
                     help="also report throughput versus chunk length and batch size")
     ap.add_argument("--library-gemm", action="store_true",
                     help="also time the vendor library's plain product on each GEMM role's shape")
+    ap.add_argument("--gemm-variants", action="store_true",
+                    help="also time every direct-load tile variant on each GEMM role's shape")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {a.gpus}); the "
@@ -491,9 +551,10 @@ def main():
                 "frac": round(achieved / PEAK_HBM_GBS, 4)}
     roof.update({"kernel": name, "avg_launch_us": dom["avg_us"], "launches": dom["launches"],
                  "traffic": measured_traffic(a.workload, name)})
-    peaks = measured_peaks(cfg["dtype"])
-    roof["measured_peak"] = peaks["gemm_tflops"] if roof["unit"] == "TFLOP/s" else peaks["copy_gbs"]
-    roof["frac_of_measured_peak"] = round(roof["achieved"] / roof["measured_peak"], 4)
+    peaks = None if a.no_peaks else measured_peaks(cfg["dtype"])
+    if peaks:
+        roof["measured_peak"] = peaks["gemm_tflops"] if roof["unit"] == "TFLOP/s" else peaks["copy_gbs"]
+        roof["frac_of_measured_peak"] = round(roof["achieved"] / roof["measured_peak"], 4)
 
     ms = 1e3 * elapsed / a.steps
     value = a.steps * audio_s / elapsed
@@ -531,6 +592,8 @@ def main():
         line["sweep"] = sweep_leg(model)
     if a.library_gemm:
         line["library_gemm"] = library_gemm_leg(cfg, line["config"]["encoder_frames"], prof)
+    if a.gemm_variants:
+        line["gemm_variants"] = gemm_variants_leg(cfg, line["config"]["encoder_frames"])
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(a.workload, a.cpu_budget)
     print(json.dumps(line), flush=True)

@@ -107,7 +107,7 @@ _SIGNATURES = {
     "gigaam_encode_noalloc": (ctypes.c_int, [_P, _P, _IP, _I, _I, _P, _P, _P, _P, _P, _IP, _P]),
     "gigaam_debug_gemm": (ctypes.c_int, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _SZ, _IP, _P]),
     "gigaam_debug_gemm_role": (ctypes.c_int, [_I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P,
-                                              ctypes.c_float, _P, _P, _SZ, _IP, _IP, _P]),
+                                              ctypes.c_float, _P, _P, _SZ, _I, _IP, _IP, _P]),
     "gigaam_debug_attention": (ctypes.c_int, [_I, _I, _I, _I, _IP, _P, _P, _P, _SZ, _P]),
     "gigaam_debug_mlp": (ctypes.c_int, [_I, _I, _I, _I, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P,
                                         _SZ, _P]),
@@ -413,16 +413,19 @@ def debug_gemm(dtype: str, A, W, bias=None, scale=None, split: bool = False, str
 GEMM_A = {"plain": 0, "dual": 2}
 GEMM_E = {"store": 0, "silu": 1, "glu": 4, "resid": 5, "f32": 6}
 GEMM_SHAPES = {1: "reg_128x64", 2: "reg_128x128", 3: "dma_256x256", 4: "dma_256x128_k32",
-               5: "dma_256x128_k64", 6: "dma_128x128"}
+               5: "dma_256x128_k64", 6: "dma_128x128", 7: "dma_256x192", 8: "dma_256x128_w4",
+               9: "dma_256x128_w4s", 10: "dma_128x256"}
+GEMM_SHAPE_IDS = {v: k for k, v in GEMM_SHAPES.items()}
 
 
 def debug_gemm_role(dtype: str, a_mode: str, epilogue: str, A, W, C, bias=None, A2=None,
                     nsplit: int = 0, alpha: float = 1.0, scale=None, split: bool = True,
-                    stream=None):
+                    shape: str | None = None, stream=None):
     """One encoder GEMM role (gigaam_debug_gemm_role): A [M][K] (and A2 for 'dual'), W
     [N][K] device tensors in the storage type of ``dtype``; C the output tensor the
     epilogue writes ('store' / 'silu': T [M][N], 'glu': T [M][N/2], 'resid': float [M][N]
-    updated in place, 'f32': float [M][N]). Returns (C, K slices, kernel shape name)."""
+    updated in place, 'f32': float [M][N]). ``shape`` names a direct-load variant to run
+    instead of the encoder's choice. Returns (C, K slices, kernel shape name)."""
     import torch
     M, K = A.shape
     N = W.shape[0]
@@ -433,7 +436,8 @@ def debug_gemm_role(dtype: str, a_mode: str, epilogue: str, A, W, C, bias=None, 
     _check(lib().gigaam_debug_gemm_role(DTYPES[dtype], GEMM_A[a_mode], GEMM_E[epilogue], M, N, K,
                                         A.data_ptr(), _ptr(A2), nsplit, W.data_ptr(), _ptr(scale),
                                         _ptr(bias), alpha, C.data_ptr(), _ptr(part),
-                                        part.numel() if split else 0, ks.ctypes.data_as(_IP),
+                                        part.numel() if split else 0,
+                                        GEMM_SHAPE_IDS[shape] if shape else 0, ks.ctypes.data_as(_IP),
                                         sh.ctypes.data_as(_IP), s))
     return C, int(ks[0]), GEMM_SHAPES[int(sh[0])]
 

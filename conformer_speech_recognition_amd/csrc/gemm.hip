@@ -378,6 +378,9 @@ __global__ void __launch_bounds__(256) k_gemm(GemmParams p) {
 __device__ __forceinline__ uint32_t lds_u32(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
+// (m0 carries the LDS destination. It is a reserved register for the compiler, which sets
+// it afresh before every instruction that reads it and never keeps a value in it, so
+// overwriting it here cannot disturb compiled code.)
 __device__ __forceinline__ void dma16(uint32_t lds, const void* g) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory");
 }
@@ -808,6 +811,9 @@ static hipError_t run_tiles(AMode am, Epi ep, const GemmParams& p, hipStream_t s
 
 template <typename T, int BM, int BN, int WGM, int WGN, int S, int KB, int OCC>
 static hipError_t run_dl(AMode am, Epi ep, const GemmParams& p, hipStream_t s) {
+  constexpr bool GLU_OK = ((BN / WGN) / 32) % 2 == 0;     // value / gate block pairs per wave
+  if (ep == E_GLU && !GLU_OK) return hipErrorInvalidValue;
+  if (am == A_DUAL && p.nsplit % BN != 0) return hipErrorInvalidValue;
   const long tiles = (long)((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   const int ks = splitk_slices(p, tiles, KB, ep);
   dim3 blk(64 * WGM * WGN);
@@ -834,8 +840,9 @@ static hipError_t run_dl(AMode am, Epi ep, const GemmParams& p, hipStream_t s) {
     hipLaunchKernelGGL((k_gemm_p<T, BM, BN, WGM, WGN, S, KB, AMv, EPv, OCC>), grid, blk, 0, s, p); \
     return hipGetLastError();                                                                      \
   }
-  GG_DL(A_PLAIN, E_STORE) GG_DL(A_PLAIN, E_SILU) GG_DL(A_PLAIN, E_RESID) GG_DL(A_PLAIN, E_GLU)
-  GG_DL(A_PLAIN, E_F32) GG_DL(A_DUAL, E_STORE)
+  GG_DL(A_PLAIN, E_STORE) GG_DL(A_PLAIN, E_SILU) GG_DL(A_PLAIN, E_RESID) GG_DL(A_PLAIN, E_F32)
+  GG_DL(A_DUAL, E_STORE)
+  if constexpr (GLU_OK) { GG_DL(A_PLAIN, E_GLU) }
 #undef GG_DL
   return hipErrorInvalidValue;
 }
@@ -857,38 +864,70 @@ static long tile_count(const GemmParams& p, int BM, int BN) {
   return (long)((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
 }
 constexpr long kNarrowBelow = 160;
-enum DlShape { DL_WIDE, DL_DUAL, DL_LONGK, DL_NARROW };
-static DlShape dl_shape(AMode am, const GemmParams& p) {
-  DlShape sh = DL_NARROW;
-  if (p.N > 1024 && am != A_DUAL) sh = DL_WIDE;
-  else if (p.N > 1024) sh = DL_DUAL;
-  else if (p.K > 1024) sh = DL_LONGK;
-  if (sh == DL_WIDE && tile_count(p, 256, 256) * splitk_slices(p, tile_count(p, 256, 256), 64, E_STORE) < kNarrowBelow)
-    sh = DL_NARROW;
-  if (sh == DL_DUAL && tile_count(p, 256, 128) * splitk_slices(p, tile_count(p, 256, 128), 32, E_STORE) < kNarrowBelow)
-    sh = DL_NARROW;
-  if (sh == DL_LONGK && tile_count(p, 256, 128) * splitk_slices(p, tile_count(p, 256, 128), 64, E_STORE) < kNarrowBelow)
-    sh = DL_NARROW;
-  return sh;
+
+// Direct-load kernel variants (the GemmShape ids): tile BM x BN, WGM x WGN waves, S stages of
+// KB-element k-tiles, OCC workgroups per CU.
+struct DlGeom { int id, BM, BN, KB; };
+constexpr DlGeom kDlGeom[] = {
+  {GEMM_DMA_256x256, 256, 256, 64},     // 8 waves, 2 stages, 1 per CU (128 KiB)
+  {GEMM_DMA_256x128_K32, 256, 128, 32}, // 8 waves, 3 stages, 2 per CU
+  {GEMM_DMA_256x128_K64, 256, 128, 64}, // 8 waves, 3 stages, 1 per CU (144 KiB)
+  {GEMM_DMA_128x128, 128, 128, 64},     // 8 waves, 2 stages, 2 per CU
+  {GEMM_DMA_256x192, 256, 192, 64},     // 8 waves (64 x 96 each), 2 stages, 1 per CU (112 KiB)
+  {GEMM_DMA_256x128_W4, 256, 128, 32},  // 4 waves of 64 x 128, 3 stages, 2 per CU
+  {GEMM_DMA_256x128_W4S, 256, 128, 32}, // 4 waves of 128 x 64, 3 stages, 2 per CU
+  {GEMM_DMA_128x256, 128, 256, 32},     // 8 waves (64 x 64 each), 2 stages, 2 per CU
+};
+static const DlGeom* dl_geom(int id) {
+  for (const DlGeom& g : kDlGeom) if (g.id == id) return &g;
+  return nullptr;
 }
-// Geometry {BM, BN, KB} of each, for the split-K planning:
-static void dl_geometry(AMode am, const GemmParams& p, int& BM, int& BN, int& KB) {
-  switch (dl_shape(am, p)) {
-    case DL_WIDE: BM = 256; BN = 256; KB = 64; break;
-    case DL_DUAL: BM = 256; BN = 128; KB = 32; break;
-    case DL_LONGK: BM = 256; BN = 128; KB = 64; break;
-    default: BM = 128; BN = 128; KB = 64; break;
+
+// A diagnostic override of the variant (gigaam_debug_gemm_role); 0: the encoder's choice.
+static thread_local int g_force_variant = 0;
+
+// The encoder's choice:
+//   single-source outputs wider than 1024 (FFN up, pointwise-1): 256 x 256;
+//   the q/k/v projection (two A sources split at a column multiple of the tile): 256 x 128,
+//     3 stages of 32 k, two workgroups per CU;
+//   outputs of at most 1024 columns with long K (FFN down): 256 x 128, 3 stages of 64 k
+//     (half the barriers of 32-k tiles: 59.9 -> 54.5 us);
+//   outputs of at most 1024 columns with K <= 1024 (out-proj, pointwise-2): 128 x 128.
+// With few rows (a clip or two, a streaming window) the large tiles leave most of the chip
+// idle: when one of them would give fewer than 160 workgroups even split, 128 x 128 is used
+// (then split-K on top when even those are few).
+static int dl_variant(AMode am, const GemmParams& p) {
+  if (g_force_variant) return g_force_variant;
+  int v = GEMM_DMA_128x128;
+  if (p.N > 1024 && am != A_DUAL) v = GEMM_DMA_256x256;
+  else if (p.N > 1024) v = GEMM_DMA_256x128_K32;
+  else if (p.K > 1024) v = GEMM_DMA_256x128_K64;
+  if (v != GEMM_DMA_128x128) {
+    const DlGeom* g = dl_geom(v);
+    const long t = tile_count(p, g->BM, g->BN);
+    if (t * splitk_slices(p, t, g->KB, E_STORE) < kNarrowBelow) v = GEMM_DMA_128x128;
   }
+  return v;
+}
+// Geometry {BM, BN, KB} of the chosen variant, for the split-K planning:
+static void dl_geometry(AMode am, const GemmParams& p, int& BM, int& BN, int& KB) {
+  const DlGeom* g = dl_geom(dl_variant(am, p));
+  BM = g->BM; BN = g->BN; KB = g->KB;
 }
 
 template <typename T>
 static hipError_t run_dl_shape(AMode am, Epi ep, const GemmParams& p, hipStream_t s) {
-  switch (dl_shape(am, p)) {
-    case DL_WIDE: return run_dl<T, 256, 256, 4, 2, 2, 64, 1>(am, ep, p, s);
-    case DL_DUAL: return run_dl<T, 256, 128, 4, 2, 3, 32, 2>(am, ep, p, s);
-    case DL_LONGK: return run_dl<T, 256, 128, 4, 2, 3, 64, 1>(am, ep, p, s);
-    default: return run_dl<T, 128, 128, 4, 2, 2, 64, 2>(am, ep, p, s);
+  switch (dl_variant(am, p)) {
+    case GEMM_DMA_256x256: return run_dl<T, 256, 256, 4, 2, 2, 64, 1>(am, ep, p, s);
+    case GEMM_DMA_256x128_K32: return run_dl<T, 256, 128, 4, 2, 3, 32, 2>(am, ep, p, s);
+    case GEMM_DMA_256x128_K64: return run_dl<T, 256, 128, 4, 2, 3, 64, 1>(am, ep, p, s);
+    case GEMM_DMA_128x128: return run_dl<T, 128, 128, 4, 2, 2, 64, 2>(am, ep, p, s);
+    case GEMM_DMA_256x192: return run_dl<T, 256, 192, 4, 2, 2, 64, 1>(am, ep, p, s);
+    case GEMM_DMA_256x128_W4: return run_dl<T, 256, 128, 4, 1, 3, 32, 2>(am, ep, p, s);
+    case GEMM_DMA_256x128_W4S: return run_dl<T, 256, 128, 2, 2, 3, 32, 2>(am, ep, p, s);
+    case GEMM_DMA_128x256: return run_dl<T, 128, 256, 2, 4, 2, 32, 2>(am, ep, p, s);
   }
+  return hipErrorInvalidValue;
 }
 
 static bool direct_path(DType dt, int qbits, AMode am, Epi ep, const GemmParams& p) {
@@ -958,12 +997,14 @@ int gemm_shape_id(DType dt, int qbits, AMode am, Epi ep, const GemmParams& p) {
   }
   GemmParams q = p;
   if (qbits != 0) { q.part = nullptr; q.part_cap = 0; }   // the expanded weights fill it
-  switch (dl_shape(am, q)) {
-    case DL_WIDE: return GEMM_DMA_256x256;
-    case DL_DUAL: return GEMM_DMA_256x128_K32;
-    case DL_LONGK: return GEMM_DMA_256x128_K64;
-    default: return GEMM_DMA_128x128;
-  }
+  return dl_variant(am, q);
+}
+
+int gemm_force_variant(int id) {
+  if (id != 0 && !dl_geom(id)) return -1;
+  const int old = g_force_variant;
+  g_force_variant = id;
+  return old;
 }
 
 static hipError_t launch_gemm_impl(DType dt, int qbits, AMode am, Epi ep, const GemmParams& p,
@@ -982,7 +1023,6 @@ static hipError_t launch_gemm_impl(DType dt, int qbits, AMode am, Epi ep, const 
                                    hipStream_t s) {
   if (p.M <= 0) return hipSuccess;
   if ((dt == DT_W8F16 || dt == DT_W6F16 || dt == DT_W4F16) && dequant_first(qbits, am, ep, p)) {
-    if (am == A_DUAL && p.nsplit % 128 != 0) return hipErrorInvalidValue;
     f16* wd = (f16*)p.part;
     const long n = (long)p.N * (p.K / 16);
     dim3 grid((unsigned)((n + 255) / 256));
@@ -1006,7 +1046,6 @@ static hipError_t launch_gemm_impl(DType dt, int qbits, AMode am, Epi ep, const 
     if (am == A_CONV_F32) am = A_CONV;
   }
   const bool direct = direct_path(dt, qbits, am, ep, p);
-  if (direct && am == A_DUAL && p.nsplit % 128 != 0) return hipErrorInvalidValue;
   switch (dt) {
     case DT_F32: return run_tiles<float, 0>(am, ep, p, s);
     case DT_F16: return direct ? run_dl_shape<f16>(am, ep, p, s) : run_tiles<f16, 0>(am, ep, p, s);

@@ -909,8 +909,8 @@ extern "C" int gigaam_debug_gemm_role(int32_t dtype, int32_t a_mode, int32_t epi
                                       int32_t N, int32_t K, const void* A_dev, const void* A2_dev,
                                       int32_t nsplit, const void* W_dev, const void* scale_dev,
                                       const float* bias_dev, float alpha, void* C_dev, float* part_dev,
-                                      size_t part_floats, int32_t* slices_host, int32_t* shape_host,
-                                      void* hip_stream) {
+                                      size_t part_floats, int32_t shape_request, int32_t* slices_host,
+                                      int32_t* shape_host, void* hip_stream) {
   if (dtype < GIGAAM_F32 || dtype > GIGAAM_W4F16) return fail(GIGAAM_E_INVAL, "dtype %d", dtype);
   if (a_mode != GIGAAM_GEMM_A_PLAIN && a_mode != GIGAAM_GEMM_A_DUAL)
     return fail(GIGAAM_E_INVAL, "a_mode %d", a_mode);
@@ -941,6 +941,26 @@ extern "C" int gigaam_debug_gemm_role(int32_t dtype, int32_t a_mode, int32_t epi
   p.part_cap = part_dev ? (long)std::min(part_floats, (size_t)LONG_MAX) : 0;
   const AMode am = (AMode)a_mode;
   const Epi ep = (Epi)epilogue;
+  if (shape_request != 0) {
+    if (shape_request < GIGAAM_GEMM_DMA_256x256 || shape_request > GIGAAM_GEMM_DMA_128x256)
+      return fail(GIGAAM_E_INVAL, "shape_request %d is not a direct-load variant", shape_request);
+    const int natural = gemm_shape_id((DType)dtype, qb, am, ep, p);
+    if (natural < GIGAAM_GEMM_DMA_256x256)
+      return fail(GIGAAM_E_INVAL, "this dtype / shape runs the register-staged kernel");
+    if (epilogue == GIGAAM_GEMM_E_GLU &&
+        (shape_request == GIGAAM_GEMM_DMA_256x192))
+      return fail(GIGAAM_E_INVAL, "variant %d has odd 32-column blocks per wave (no GLU)", shape_request);
+    if (a_mode == GIGAAM_GEMM_A_DUAL) {
+      const int bn = shape_request == GIGAAM_GEMM_DMA_256x256 || shape_request == GIGAAM_GEMM_DMA_128x256 ? 256
+                     : shape_request == GIGAAM_GEMM_DMA_256x192 ? 192 : 128;
+      if (nsplit % bn) return fail(GIGAAM_E_INVAL, "dual split %d not a multiple of tile width %d", nsplit, bn);
+    }
+  }
+  struct Force {                        // the override covers this call only
+    int old;
+    explicit Force(int id) : old(gemm_force_variant(id)) {}
+    ~Force() { gemm_force_variant(old); }
+  } force(shape_request);
   if (slices_host) *slices_host = gemm_split_slices((DType)dtype, qb, am, ep, p);
   if (shape_host) *shape_host = gemm_shape_id((DType)dtype, qb, am, ep, p);
   HIP_TRY(launch_gemm((DType)dtype, qb, am, ep, p, (hipStream_t)hip_stream));

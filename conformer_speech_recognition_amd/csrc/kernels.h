@@ -54,9 +54,13 @@ int gemm_split_slices(DType dt, int qbits, AMode am, Epi ep, const GemmParams& p
 // Kernel shape launch_gemm uses for these arguments (the GIGAAM_GEMM_* ids of gigaam.h)
 enum GemmShape {
   GEMM_REG_128x64 = 1, GEMM_REG_128x128 = 2, GEMM_DMA_256x256 = 3, GEMM_DMA_256x128_K32 = 4,
-  GEMM_DMA_256x128_K64 = 5, GEMM_DMA_128x128 = 6
+  GEMM_DMA_256x128_K64 = 5, GEMM_DMA_128x128 = 6, GEMM_DMA_256x192 = 7, GEMM_DMA_256x128_W4 = 8,
+  GEMM_DMA_256x128_W4S = 9, GEMM_DMA_128x256 = 10
 };
 int gemm_shape_id(DType dt, int qbits, AMode am, Epi ep, const GemmParams& p);
+// Diagnostics: force the direct-load variant of the following launches on this thread (0:
+// the encoder's choice); returns the previous setting, or -1 for an unknown id.
+int gemm_force_variant(int id);
 
 // Fused macaron FFN for few rows: x += alpha * (W2 SiLU(W1 y + b1) + b2) without the hidden
 // activations in HBM (16-bit weights, d 768 or 1024, f a multiple of 256, at most

@@ -272,21 +272,27 @@ int gigaam_debug_gemm(int32_t dtype, int32_t M, int32_t N, int32_t K, const void
  * quantised dtypes: fp16 A and C, W the packed rows with scale_dev as in
  * gigaam_debug_gemm). A_dev, A2_dev, W_dev, C_dev 16-byte aligned; bias_dev float [N] or
  * NULL; part_dev / part_floats / slices_host as in gigaam_debug_gemm (a split K sum is
- * always finished by the reduce kernel here). shape_host (may be NULL) receives the
- * kernel shape used, one of GIGAAM_GEMM_REG_* (register-staged loads, 4 waves) or
- * GIGAAM_GEMM_DMA_* (direct-to-LDS pipeline, 8 waves). K must be a multiple of 64 (32
- * for GIGAAM_F32). Errors: GIGAAM_E_INVAL, GIGAAM_E_HIP.                             */
+ * always finished by the reduce kernel here). shape_request: 0 = the kernel the encoder
+ * would choose for these arguments; otherwise one of the GIGAAM_GEMM_DMA_* variants, run
+ * instead (measurement of alternatives: fp16 / bf16 or quantised-with-expansion paths
+ * only; GLU needs an even number of 32-column blocks per wave, the dual mode a split at
+ * a multiple of the tile width). shape_host (may be NULL) receives the kernel shape
+ * used, one of GIGAAM_GEMM_REG_* (register-staged loads, 4 waves) or GIGAAM_GEMM_DMA_*
+ * (direct-to-LDS pipeline: tile rows x columns, 8 waves unless _W4*: 4 waves). K must be
+ * a multiple of 64 (32 for GIGAAM_F32). Errors: GIGAAM_E_INVAL, GIGAAM_E_HIP.        */
 enum { GIGAAM_GEMM_A_PLAIN = 0, GIGAAM_GEMM_A_DUAL = 2 };
 enum { GIGAAM_GEMM_E_STORE = 0, GIGAAM_GEMM_E_SILU = 1, GIGAAM_GEMM_E_GLU = 4,
        GIGAAM_GEMM_E_RESID = 5, GIGAAM_GEMM_E_F32 = 6 };
 enum { GIGAAM_GEMM_REG_128x64 = 1, GIGAAM_GEMM_REG_128x128 = 2, GIGAAM_GEMM_DMA_256x256 = 3,
        GIGAAM_GEMM_DMA_256x128_K32 = 4, GIGAAM_GEMM_DMA_256x128_K64 = 5,
-       GIGAAM_GEMM_DMA_128x128 = 6 };
+       GIGAAM_GEMM_DMA_128x128 = 6, GIGAAM_GEMM_DMA_256x192 = 7, GIGAAM_GEMM_DMA_256x128_W4 = 8,
+       GIGAAM_GEMM_DMA_256x128_W4S = 9, GIGAAM_GEMM_DMA_128x256 = 10 };
 int gigaam_debug_gemm_role(int32_t dtype, int32_t a_mode, int32_t epilogue, int32_t M, int32_t N,
                            int32_t K, const void* A_dev, const void* A2_dev, int32_t nsplit,
                            const void* W_dev, const void* scale_dev, const float* bias_dev,
                            float alpha, void* C_dev, float* part_dev, size_t part_floats,
-                           int32_t* slices_host, int32_t* shape_host, void* hip_stream);
+                           int32_t shape_request, int32_t* slices_host, int32_t* shape_host,
+                           void* hip_stream);
 
 /* Diagnostics: a fused variant of the macaron FFN for few rows (hidden activations kept on
  * chip), measured against the encoder's two GEMMs, which the encoder uses instead:

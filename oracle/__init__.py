@@ -267,11 +267,15 @@ def mhsa_rope(y: np.ndarray, P: dict, pre: str, n_heads: int, base: float) -> np
 # Conformer block ([ML-port] "What is inside the model": FFN, attention, conv, FFN)
 # ==================================================================================
 
-def feed_forward(x, P, pre, eps):
-    """Macaron FFN on the pre-normed input: linear2(SiLU(linear1(LN(x))))."""
-    y = layer_norm(x, P[pre + "norm.weight"], P[pre + "norm.bias"], eps)
+def ffn_body(y, P, pre):
+    """The feed-forward module after its norm: linear2(SiLU(linear1(y)))."""
     h = silu(linear(y, P[pre + "linear1.weight"], P[pre + "linear1.bias"]))
     return linear(h, P[pre + "linear2.weight"], P[pre + "linear2.bias"])
+
+
+def feed_forward(x, P, pre, eps):
+    """Macaron FFN on the pre-normed input: linear2(SiLU(linear1(LN(x))))."""
+    return ffn_body(layer_norm(x, P[pre + "norm.weight"], P[pre + "norm.bias"], eps), P, pre)
 
 
 def conv_module(x, P, pre, eps, bn_eps):

@@ -261,9 +261,9 @@ def test_debug_gemm_role_validation(gg):
     fake = 1 << 20
     F = ctypes.c_float
 
-    def call(dt=1, am=0, ep=1, M=64, N=256, K=128, A=fake, A2=None, ns=0, W=fake, C=fake, part=None):
+    def call(dt=1, am=0, ep=1, M=64, N=256, K=128, A=fake, A2=None, ns=0, W=fake, C=fake, part=None, req=0):
         return L.gigaam_debug_gemm_role(dt, am, ep, M, N, K, A, A2, ns, W, None, None, F(1.0), C, part,
-                                        0, None, None, None)
+                                        0, req, None, None, None)
     assert call(dt=9) == gg.E_INVAL
     assert call(am=1) == gg.E_INVAL                      # not a role mode
     assert call(ep=3) == gg.E_INVAL                      # not a role epilogue
@@ -278,6 +278,11 @@ def test_debug_gemm_role_validation(gg):
     assert call(A=fake + 2) == gg.E_INVAL and call(W=fake + 2) == gg.E_INVAL and call(C=fake + 4) == gg.E_INVAL
     assert call(part=fake + 4) == gg.E_INVAL
     assert call(dt=3) == gg.E_INVAL                                  # quantised weights need scales
+    assert call(req=2) == gg.E_INVAL                                 # not a direct-load variant
+    assert call(req=11) == gg.E_INVAL
+    assert call(dt=0, req=3) == gg.E_INVAL                           # fp32 runs the register path
+    assert call(ep=4, N=384, req=7) == gg.E_INVAL                    # 256x192: no GLU pairs
+    assert call(am=2, ep=0, A2=fake, ns=128, N=512, req=3) == gg.E_INVAL   # split inside a tile
 
 
 def test_noalloc_entry_validates_before_touching_the_gpu(gg):
