@@ -1,19 +1,8 @@
 // Flash-style self-attention over packed variable-length clips for gfx950.
 // softmax(q k^T / sqrt(d_k)) v per clip and head, keys beyond the clip masked
 // (key-padding mask; fused scaled-dot-product attention: "GigaAM MLX port for Mac",
-// section "Where the time goes").
-//
-// Block = 4 waves = 64 queries of one clip and one head; each wave owns 16 queries.
-// Per 64-key tile (K and V^T staged in LDS, the next tile prefetched into registers):
-//   S^T[key][query] = K . Q^T   with 16x16 MFMAs (A = K rows from LDS, B = the wave's Q
-//                               fragment kept in registers)
-//   lane l then holds 16 scores of ONE query (l % 16): keys kb*16 + 4*(l/16) + r,
-//   so the online-softmax running max / sum / rescale are lane-local (plus a 4-lane
-//   max across l/16);
-//   O^T[dim][query] += V^T . P^T with the probabilities used straight from the score
-//   registers as the B operand (the lane's k slots are exactly its keys).
-// Scores, max, sum and the output accumulator are fp32; P is rounded to T for the MFMA.
-// d_k = 48 runs the score contraction as two 16x16x32 MFMAs with the top 16 k slots zero.
+// section "Where the time goes"). Scores, max, sum and the output accumulator are fp32;
+// the probabilities are rounded to the operand type for the second product.
 #include "kernels.h"
 
 namespace gg {
@@ -22,20 +11,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int AT_KV = 64;
-
-template <typename T> struct AttnMma;
-template <> struct AttnMma<f16> {
-  static __device__ __forceinline__ f32x4 k32(u32x4 a, u32x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-  }
-};
-template <> struct AttnMma<bf16> {
-  static __device__ __forceinline__ f32x4 k32(u32x4 a, u32x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-  }
-};
 
 template <typename T> __device__ __forceinline__ u32x4 pack8f(const float* v) {
   typedef T t8 __attribute__((ext_vector_type(8)));
@@ -58,15 +33,30 @@ template <typename T> __device__ __forceinline__ u32x2 lds_read_tr(const T* p) {
 }
 
 // ---------------------------------------------------------------- fp16 / bf16 kernel
-// K and V tiles are double-buffered in LDS, both row-major (key, dim) copies of the global
-// rows: the next 64-key tile is loaded into registers while the current one is consumed,
-// and stored after it (one barrier per tile). The P.V product reads its V^T operand with
-// the transposing LDS read, so V is never transposed in registers.
+// Block = 4 waves = 128 queries (a 128-frame tile) of one clip and one head; wave w owns
+// queries 32 w .. 32 w + 31 of the tile (a wave past the clip's end only helps with the
+// K / V loads). Per 64-key tile, with 32 x 32 x 16 MFMAs:
+//   S^T[key][query] = K . Q^T  (A = 32 K rows from LDS, 16 dims per step; B = the wave's Q
+//                               fragment in registers; d_k / 16 steps, no padded dims)
+//   lane l then holds 32 scores of ONE query (l % 32): in each 32-key block the keys
+//   8 (r / 4) + 4 (l / 32) + r % 4, r < 16; lanes l and l + 32 share a query, so the
+//   running max needs one lane swap;
+//   O^T[dim][query] += V^T . P^T with 32-dim output blocks; the probabilities go straight
+//   from the score registers into the B operand (8 per lane per 16-key step: r = 8 j ..
+//   8 j + 7 of a block, i.e. keys 16 j + 4 (l / 32) + {0..3} and 16 j + 8 + 4 (l / 32) +
+//   {0..3}); the A operand (V^T) is read in exactly that key order with the transposing LDS
+//   read, so V is never transposed in registers.
+// V carries a column of ones at dim d_k, so the last output block also accumulates each
+// query's probability sum in the rounded P the MFMA uses (for d_k = 48 it sits in the
+// second 32-dim block's spare rows).
 //
-// The softmax is kept in base 2 with the scale folded into one FMA per score:
-// p = 2^(s*c - m*c), c = log2(e)/sqrt(d_k), m the running max of the raw scores.  The
-// key mask is applied only on a clip's last, partial tile; the accumulator is rescaled
-// only when some query's running max moved.
+// K and V tiles are double-buffered in LDS as row-major (key, dim) copies of the global
+// rows: the next 64-key tile is loaded into registers while the current one is consumed,
+// and stored after it (one barrier per tile). The softmax is kept in base 2 with the scale
+// folded into one FMA per score: p = 2^(s*c - m*c), c = log2(e)/sqrt(d_k), m the running
+// of the raw scores seen so far (a stale one while it is within 2^8, see below). The key mask
+// is applied only on a clip's last, partial tile.
+//
 // v_max3_f32 without the NaN-quieting canonicalisation the compiler adds around fmaxf
 __device__ __forceinline__ float max3_(float a, float b, float c) {
   float r;
@@ -86,58 +76,68 @@ __device__ __forceinline__ void attn_item(int bid, int n_tiles, int n_heads, int
   tile = w - h * n_tiles;
 }
 
-__device__ __forceinline__ float max_xor16(float v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
-                                                  false, false);
-  return max3_(__uint_as_float(r[0]), __uint_as_float(r[1]), v);
-}
 __device__ __forceinline__ float max_xor32(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
                                                   false, false);
   return max3_(__uint_as_float(r[0]), __uint_as_float(r[1]), v);
 }
 
+template <typename T> struct AttnMma32;
+template <> struct AttnMma32<f16> {
+  static __device__ __forceinline__ f32x16 run(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+};
+template <> struct AttnMma32<bf16> {
+  static __device__ __forceinline__ f32x16 run(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+};
+
 template <typename T, int DK>
-__global__ void __launch_bounds__(256) k_attn(AttnParams p) {
-  constexpr int KP = DK + 8;         // LDS row pitch (elements) of K: 16 rows -> 16 bank groups
-  // LDS row pitch of V: dims, then a column of ones and zeros up to DK + 16; 80 elements
-  // put the 8 rows one transposing read pass touches on disjoint banks
-  constexpr int VP = 80;
-  constexpr int NDB = DK / 16;       // 16-wide dim blocks of the output
-  constexpr int NDBX = NDB + 1;      // + one block whose first column is all ones: row sums
+__global__ void __launch_bounds__(256, 4) k_attn(AttnParams p) {
+  constexpr int QT = 128;            // queries per block
+  constexpr int KP = DK + 8;         // K row pitch (elements): 16 rows of a read pass on disjoint banks
+  // V row pitch: dims, the ones column, zeros; 96 elements (48 dwords) put the 4 rows of one
+  // transposing read pass, 32 dims each, on disjoint banks
+  constexpr int VP = 96;
+  constexpr int KS = DK / 16;        // 16-dim steps of the score product
+  constexpr int NDB = (DK + 1 + 31) / 32;   // 32-dim output blocks, the ones column included
   constexpr int CPR = DK / 8;        // 16-byte chunks per K / V row
   constexpr int KCH = AT_KV * CPR;   // 16-byte chunks per tile (each of K and V)
-  constexpr int KPT = (KCH + 255) / 256;       // chunks per thread
-  static_assert(DK + 16 <= VP, "V row pitch");
-  __shared__ T sK[2][AT_KV][KP];
+  constexpr int KPT = (KCH + 255) / 256;    // chunks per thread
+  static_assert(DK % 16 == 0 && NDB * 32 <= VP, "head size");
+  __shared__ __attribute__((aligned(16))) T sK[2][AT_KV][KP];
   __shared__ __attribute__((aligned(16))) T sV[2][AT_KV][VP];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, c16 = lane & 15;
+  const int hf = lane >> 5, c32 = lane & 31;
   int tile, h;
   attn_item(blockIdx.x, p.n_tiles, p.n_heads, tile, h);
   const int b = p.tileQ[tile];
   const int base = p.cuU[b], U = p.cuU[b + 1] - base;
-  const int qi = (tile - p.cuQ[b]) * 64 + wave * 16 + c16;
+  const int q0 = (tile - p.cuQ[b]) * QT + wave * 32;      // the wave's first query
+  const bool active = q0 < U;                              // wave-uniform
+  const int qi = q0 + c32;
   const int ld = 3 * p.d;
   const T* Qg = (const T*)p.qkv + (long)base * ld + h * DK;
   const T* Kg = Qg + p.d;
   const T* Vg = Qg + 2 * p.d;
   const float c = p.scale_log2;
 
-  // Q fragment (B operand of S^T): query qi, dims [8g, 8g+8) and the remainder block
+  // Q fragments (B operand of S^T): query qi, dims 16 ks + 8 hf .. + 7
   const int qrow = qi < U ? qi : U - 1;
-  const T* qp = Qg + (long)qrow * ld;
-  // dims 32.. go through a second 16x16x32 MFMA; for d_k = 48 its lanes g >= 2 (dims 48..63)
-  // are zero on both operands
-  const bool hi_ok = DK == 64 || g < 2;
-  const u32x4 qa = *(const u32x4*)(qp + 8 * g);
-  const u32x4 qb = hi_ok ? *(const u32x4*)(qp + 32 + 8 * g) : u32x4{0, 0, 0, 0};
+  const T* qp = Qg + (long)qrow * ld + 8 * hf;
+  u32x4 qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const u32x4*)(qp + 16 * ks);
 
   // this thread's tile loads: 16-byte K and V chunks (e = tid + 256 i: key e / CPR, chunk
   // e % CPR), as raw buffer loads against a per-tile resource that ends at the clip's last
   // row: rows past the clip read as zero
-  int koff[KPT], kls[KPT], vls[KPT];  // global byte offset in the tile, LDS element offsets
+  int koff[KPT], kls[KPT], vls[KPT];
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
     const int e = tid + 256 * i, key = e / CPR, ch = e - key * CPR;
@@ -167,26 +167,27 @@ __global__ void __launch_bounds__(256) k_attn(AttnParams p) {
         *(u32x4*)(&sV[buf][0][0] + vls[i]) = rv[i];
       }
   };
-  // d_k = 48: the score MFMA's upper 16 k slots read the zero pad columns [48, 56) of the
-  // K rows (set once here, never overwritten by the tile stores)
-  if (DK == 48 && tid < 2 * AT_KV)
-    *(u32x4*)&sK[tid / AT_KV][tid % AT_KV][DK] = u32x4{0, 0, 0, 0};
-  const int khi = hi_ok ? 32 + 8 * g : DK;
-
-  // columns DK.. DK+15 of both V buffers: a column of ones then zeros, so that the P.V
-  // product also accumulates each query's probability sum (in the rounded P the MFMA uses)
+  // columns DK .. VP - 1 of both V buffers: one at DK, zeros after it (never overwritten by
+  // the tile stores)
   {
-    const int vb = tid >> 7, key = (tid >> 1) & 63, half = tid & 1;
-    const uint32_t one = half == 0 ? (uint32_t)__builtin_bit_cast(uint16_t, (T)1.0f) : 0u;
-    *(u32x4*)&sV[vb][key][DK + 8 * half] = u32x4{one, 0u, 0u, 0u};
+    constexpr int XC = (VP - DK) / 8;            // 16-byte chunks per row past the dims
+    const uint32_t one = (uint32_t)__builtin_bit_cast(uint16_t, (T)1.0f);
+    for (int e = tid; e < 2 * AT_KV * XC; e += 256) {
+      const int vb = e / (AT_KV * XC), rem = e - vb * AT_KV * XC, key = rem / XC, x = rem - key * XC;
+      *(u32x4*)&sV[vb][key][DK + 8 * x] = u32x4{x == 0 ? one : 0u, 0u, 0u, 0u};
+    }
   }
-  // this lane's rows for the transposing V reads: lane 4 s + q of its 16-lane group names
-  // key 4 g + s (and 16 + 4 g + s) of a 32-key half, dims 4 q .. 4 q + 3 of a dim block
-  const int tr_key = 4 * g + (c16 >> 2), tr_dim = 4 * (c16 & 3);
+  // this lane's transposing V reads: lane 4 s + q of its 16-lane group g names key
+  // 4 (g / 2) + s (plus 8 for the second read) of a 16-key step, dims 16 (g % 2) + 4 q ..
+  // + 3 of a 32-dim block; it receives dim (lane % 32) of keys 4 hf + {0..3} (+ 8)
+  const int g16 = lane >> 4, i16 = lane & 15;
+  const int tr_key = 4 * (g16 >> 1) + (i16 >> 2), tr_dim = 16 * (g16 & 1) + 4 * (i16 & 3);
   float m_run = -INFINITY;
-  f32x4 o[NDBX];
+  f32x16 o[NDB];
 #pragma unroll
-  for (int db = 0; db < NDBX; ++db) o[db] = f32x4{0, 0, 0, 0};
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
 
   load(0);
   store(0);
@@ -198,83 +199,94 @@ __global__ void __launch_bounds__(256) k_attn(AttnParams p) {
   for (int kv0 = 0; kv0 < U; kv0 += AT_KV) {
     const bool more = kv0 + AT_KV < U;
     if (more) load(kv0 + AT_KV);
-
-    // S^T blocks: s[kb][r] = raw score(key kv0 + kb*16 + 4g + r, query qi)
-    f32x4 s[4];
+    if (active) {
+      // S^T blocks: s[kb][r] = raw score(key kv0 + 32 kb + 8 (r / 4) + 4 hf + r % 4, query qi)
+      f32x16 s[2];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const T* kr = &sK[buf][kb * 16 + c16][0];
-      f32x4 acc = f32x4{0, 0, 0, 0};
-      acc = AttnMma<T>::k32(*(const u32x4*)(kr + 8 * g), qa, acc);
-      acc = AttnMma<T>::k32(*(const u32x4*)(kr + khi), qb, acc);
-      s[kb] = acc;
-    }
-    if (!more) {                     // the clip's last tile: keys >= U get probability 0
+      for (int kb = 0; kb < 2; ++kb) {
+        const T* kr = &sK[buf][kb * 32 + c32][8 * hf];
+        f32x16 acc;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (kv0 + kb * 16 + 4 * g + r >= U) s[kb][r] = -INFINITY;
-    }
-    float mx = max3_(s[0][0], s[0][1], s[0][2]);
-    mx = max3_(mx, s[0][3], s[1][0]);
-    mx = max3_(mx, s[1][1], s[1][2]);
-    mx = max3_(mx, s[1][3], s[2][0]);
-    mx = max3_(mx, s[2][1], s[2][2]);
-    mx = max3_(mx, s[2][3], s[3][0]);
-    mx = max3_(mx, s[3][1], s[3][2]);
-    mx = max3_(mx, s[3][3], m_run);
-    const float m_new = max_xor32(max_xor16(mx));
-    if (__builtin_amdgcn_ballot_w64(m_new != m_run)) {
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
-#pragma unroll
-      for (int db = 0; db < NDBX; ++db) o[db] *= alpha;
-      m_run = m_new;
-    }
-    const float mc = m_run * c;
-    float pv[4][4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) pv[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -mc));
-
-#pragma unroll
-    for (int hk = 0; hk < 2; ++hk) {
-      float pp[8];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) { pp[r] = pv[2 * hk][r]; pp[4 + r] = pv[2 * hk + 1][r]; }
-      const u32x4 pb = pack8f<T>(pp);
-#pragma unroll
-      for (int db = 0; db < NDBX; ++db) {
-        // V^T rows db*16 + c16, keys 32 hk + 4 g + 0..3 and 32 hk + 16 + 4 g + 0..3
-        const u32x2 lo = lds_read_tr(&sV[buf][32 * hk + tr_key][db * 16 + tr_dim]);
-        const u32x2 hi = lds_read_tr(&sV[buf][32 * hk + 16 + tr_key][db * 16 + tr_dim]);
-        o[db] = AttnMma<T>::k32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb, o[db]);
+        for (int ks = 0; ks < KS; ++ks) acc = AttnMma32<T>::run(*(const u32x4*)(kr + 16 * ks), qf[ks], acc);
+        s[kb] = acc;
       }
+      if (!more) {                   // the clip's last tile: keys >= U get probability 0
+        const int lim = U - kv0 - 4 * hf;         // first masked key offset of this lane's rows
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (32 * kb + 8 * (r >> 2) + (r & 3) >= lim) s[kb][r] = -INFINITY;
+      }
+      float mx = max3_(s[0][0], s[0][1], m_run);
+#pragma unroll
+      for (int r = 2; r < 16; r += 2) mx = max3_(mx, s[0][r], s[0][r + 1]);
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) mx = max3_(mx, s[1][r], s[1][r + 1]);
+      const float m_new = max_xor32(mx);
+      // The reference point of the exponentials moves only when some query's maximum rose by
+      // more than 8 in base-2 units: until then every probability stays below 2^8, and the
+      // numerator and the sum (the ones column) share the same reference, so the result is
+      // unchanged while most tiles skip the rescale.
+      if (__builtin_amdgcn_ballot_w64((m_new - m_run) * c > 8.0f)) {
+        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+        m_run = m_new;
+      }
+      const float mc = m_run * c;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          float pp[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) pp[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * j + t], c, -mc));
+          const u32x4 pb = pack8f<T>(pp);
+          const int k0 = 32 * kb + 16 * j + tr_key;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const u32x2 lo = lds_read_tr(&sV[buf][k0][32 * db + tr_dim]);
+            const u32x2 hi = lds_read_tr(&sV[buf][k0 + 8][32 * db + tr_dim]);
+            o[db] = AttnMma32<T>::run(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb, o[db]);
+          }
+        }
     }
     if (more) store(buf ^ 1);
     __syncthreads();
     buf ^= 1;
   }
+  if (!active) return;
 
-  // the probability sum sits in dim DK of the extra block: lane c16 (g = 0), element 0
-  const float l = __shfl(o[NDB][0], c16, 64);
+  // the probability sum: dim DK of block DK / 32, i.e. row DK % 32 of that block, held by
+  // the lanes of half (DK % 32) / 4 % 2 at r = 4 ((DK % 32) / 8) + DK % 4 (DK % 32 is 16 or 0)
+  constexpr int LR = DK % 32, LDB = DK / 32;
+  constexpr int LHF = (LR >> 2) & 1, LRR = 4 * (LR >> 3) + (LR & 3);
+  const float lsum = __shfl(o[LDB][LRR], c32 + 32 * LHF, 64);
   if (qi < U) {
-    const float inv = 1.0f / l;
+    const float inv = 1.0f / lsum;
     T* op = (T*)p.out + (long)(base + qi) * p.d + h * DK;
+    typedef T t4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      typedef T t4 __attribute__((ext_vector_type(4)));
-      t4 w;
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) w[r] = (T)(o[db][r] * inv);
-      *(t4*)(op + db * 16 + 4 * g) = w;
-    }
+      for (int rg = 0; rg < 4; ++rg) {
+        const int dim = 32 * db + 8 * rg + 4 * hf;
+        if (dim < DK) {
+          t4 w;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) w[r] = (T)(o[db][4 * rg + r] * inv);
+          *(t4*)(op + dim) = w;
+        }
+      }
   }
 }
 
 // ---------------------------------------------------------------- fp32 kernel
-// Same dataflow with v_mfma_f32_16x16x4_f32 (one k element per lane group).
+// 64-frame query tiles, 16 queries per wave, v_mfma_f32_16x16x4_f32 (one k element per lane
+// group); lane l holds the scores of query l % 16 for keys 16 kb + 4 (l / 16) + r.
 template <int DK>
 __global__ void __launch_bounds__(256) k_attn_f32(AttnParams p) {
   constexpr int KP = DK + 4, VP = AT_KV + 4, NDB = DK / 16;

@@ -32,9 +32,13 @@ struct MetaArgs {          // passed by value to the meta kernel (kernarg, < 4 K
   int cuU[kMaxBatch + 1];
 };
 
+// Attention works on 128-frame query tiles (cuQ2 / tileQ2, numbered the same way).
+constexpr int kQTile2 = 128;
+
 struct MetaDev {           // device view of the meta region
   int* cuT; int* cuS; int* cuU; int* cuQ;
   int* rowT; int* rowS; int* rowU; int* tileQ;
+  int* cuQ2; int* tileQ2;
 };
 
 template <typename T> struct TypeOf;

@@ -538,7 +538,7 @@ extern "C" void gigaam_destroy(gigaam_model* m) { delete m; }
 namespace {
 
 struct Ws {
-  size_t cuT, cuS, cuU, cuQ, rowT, rowS, rowU, tileQ;
+  size_t cuT, cuS, cuU, cuQ, rowT, rowS, rowU, tileQ, cuQ2, tileQ2;
   size_t mel, h1, x, y, r, qkv, ao, hid, cos_t, sin_t, logits, fids, part, fe;
   size_t total;
 };
@@ -552,6 +552,8 @@ Ws plan(const gigaam_config& c, int B, int T_tot, int S_tot, int U_tot, int nQ, 
   w.cuT = take((B + 1) * 4); w.cuS = take((B + 1) * 4); w.cuU = take((B + 1) * 4); w.cuQ = take((B + 1) * 4);
   w.rowT = take((size_t)T_tot * 4); w.rowS = take((size_t)S_tot * 4); w.rowU = take((size_t)U_tot * 4);
   w.tileQ = take((size_t)nQ * 4);
+  w.cuQ2 = take((B + 1) * 4);
+  w.tileQ2 = take((size_t)nQ * 4);            // nQ2 <= nQ
   w.mel = take((size_t)T_tot * 64 * 4);
   w.h1 = take((size_t)S_tot * d * es);
   w.x = take((size_t)U_tot * d * 4);
@@ -635,7 +637,7 @@ int run(gigaam_model* m, const float* pcm, const int32_t* lengths, int32_t B, in
   MetaArgs meta;
   std::memset(&meta, 0, sizeof meta);
   meta.B = B;
-  int U_max = 0, nQ = 0, maxlen = 0;
+  int U_max = 0, nQ = 0, nQ2 = 0, maxlen = 0;
   std::vector<int> Ub(B);
   for (int b = 0; b < B; ++b) {
     const int L = lengths[b];
@@ -649,6 +651,7 @@ int run(gigaam_model* m, const float* pcm, const int32_t* lengths, int32_t B, in
     Ub[b] = U;
     U_max = U > U_max ? U : U_max;
     nQ += (U + kQTile - 1) / kQTile;
+    nQ2 += (U + kQTile2 - 1) / kQTile2;
     maxlen = L > maxlen ? L : maxlen;
   }
   const int T_tot = meta.cuT[B], S_tot = meta.cuS[B], U_tot = meta.cuU[B];
@@ -669,7 +672,8 @@ int run(gigaam_model* m, const float* pcm, const int32_t* lengths, int32_t B, in
 
   char* W = (char*)ws;
   MetaDev md{(int*)(W + w.cuT), (int*)(W + w.cuS), (int*)(W + w.cuU), (int*)(W + w.cuQ),
-             (int*)(W + w.rowT), (int*)(W + w.rowS), (int*)(W + w.rowU), (int*)(W + w.tileQ)};
+             (int*)(W + w.rowT), (int*)(W + w.rowS), (int*)(W + w.rowU), (int*)(W + w.tileQ),
+             (int*)(W + w.cuQ2), (int*)(W + w.tileQ2)};
   float* mel = (float*)(W + w.mel);
   char* h1 = W + w.h1;
   float* x = (float*)(W + w.x);
@@ -749,7 +753,9 @@ int run(gigaam_model* m, const float* pcm, const int32_t* lengths, int32_t B, in
            launch_layernorm(dt, mode, q, s));
     return GIGAAM_OK;
   };
-  AttnParams ap{qkv, ao, d, H, nQ, md.cuU, md.cuQ, md.tileQ, (float)(1.4426950408889634 / std::sqrt((double)dk))};
+  const bool f32 = dt == DT_F32;              // the fp32 kernel works on 64-frame tiles
+  AttnParams ap{qkv, ao, d, H, f32 ? nQ : nQ2, md.cuU, f32 ? md.cuQ : md.cuQ2, f32 ? md.tileQ : md.tileQ2,
+                (float)(1.4426950408889634 / std::sqrt((double)dk))};
   DwParams dp;
   dp.in = hid; dp.out = hid2; dp.d = d; dp.n_tiles = nQ; dp.cuU = md.cuU; dp.cuQ = md.cuQ;
   dp.tileQ = md.tileQ; dp.eps = c.bn_eps;
@@ -1000,25 +1006,28 @@ extern "C" int gigaam_debug_attention(int32_t dtype, int32_t d_model, int32_t n_
   MetaArgs meta;
   std::memset(&meta, 0, sizeof meta);
   meta.B = batch;
-  int nQ = 0;
+  int nQ = 0, nQ2 = 0;
   for (int b = 0; b < batch; ++b) {
     if (frames_host[b] < 1) return fail(GIGAAM_E_INVAL, "frames[%d] = %d", b, frames_host[b]);
     meta.cuU[b + 1] = meta.cuU[b] + frames_host[b];
     nQ += (frames_host[b] + kQTile - 1) / kQTile;
+    nQ2 += (frames_host[b] + kQTile2 - 1) / kQTile2;
   }
   const int U_tot = meta.cuU[batch];
   std::memcpy(meta.cuT, meta.cuU, sizeof meta.cuU);
   std::memcpy(meta.cuS, meta.cuU, sizeof meta.cuU);
-  const size_t need = 16 * (size_t)(batch + 1) + 16 * (size_t)U_tot + 4096;
+  const size_t need = 20 * (size_t)(batch + 1) + 20 * (size_t)U_tot + 4096;
   if (workspace_bytes < need) return fail(GIGAAM_E_WORKSPACE, "workspace %zu < %zu", workspace_bytes, need);
   int* w = (int*)workspace;
-  MetaDev md{w, w + (batch + 1), w + 2 * (batch + 1), w + 3 * (batch + 1), w + 4 * (batch + 1),
-             w + 4 * (batch + 1) + U_tot, w + 4 * (batch + 1) + 2 * U_tot,
-             w + 4 * (batch + 1) + 3 * U_tot};
+  const int c1 = batch + 1;                    // five clip tables, then five row/tile tables
+  int* rows = w + 5 * c1;
+  MetaDev md{w, w + c1, w + 2 * c1, w + 3 * c1, rows, rows + U_tot, rows + 2 * U_tot,
+             rows + 3 * U_tot, w + 4 * c1, rows + 4 * U_tot};
   hipStream_t s = (hipStream_t)hip_stream;
   HIP_TRY(launch_meta(meta, md, U_tot, U_tot, U_tot, s));
-  AttnParams ap{qkv_dev, out_dev, d_model, n_heads, nQ, md.cuU, md.cuQ, md.tileQ,
-                (float)(1.4426950408889634 / std::sqrt((double)dk))};
+  const bool f32 = dtype == GIGAAM_F32;
+  AttnParams ap{qkv_dev, out_dev, d_model, n_heads, f32 ? nQ : nQ2, md.cuU, f32 ? md.cuQ : md.cuQ2,
+                f32 ? md.tileQ : md.tileQ2, (float)(1.4426950408889634 / std::sqrt((double)dk))};
   HIP_TRY(launch_attention((DType)dtype, dk, ap, s));
   return GIGAAM_OK;
 }

@@ -114,6 +114,8 @@ hipError_t launch_rope_table(float* cos_t, float* sin_t, int n_pos, int dk, floa
 struct AttnParams {
   const void* qkv;                 // T [rows][3d]: q | k | v
   void* out;                       // T [rows][d]
+  // query tiles: 128 frames for the 16-bit kernel (MetaDev cuQ2 / tileQ2), 64 frames for
+  // the fp32 kernel (cuQ / tileQ)
   int d, n_heads, n_tiles;
   const int* cuU; const int* cuQ; const int* tileQ;
   float scale_log2;                // log2(e) / sqrt(d_k)

@@ -1,5 +1,6 @@
 // Batch geometry on the device: clip offsets and row -> clip maps of the packed
-// mel (T), first-conv (S) and encoder (U) row spaces, plus the 64-frame q-tiles.
+// mel (T), first-conv (S) and encoder (U) row spaces, plus the 64-frame tiles (depthwise
+// conv) and 128-frame query tiles (attention) of every clip.
 // Variable-length clips are packed back to back so every per-frame kernel touches valid
 // frames only (batched chunks with masks: "GigaAM MLX port for Mac", section "What is
 // inside the model").
@@ -19,20 +20,25 @@ __device__ __forceinline__ int find_clip(const int* cu, int B, int r) {
 __global__ void __launch_bounds__(256) k_meta(MetaArgs a, MetaDev m, int T_tot, int S_tot,
                                               int U_tot) {
   __shared__ int cuQ[kMaxBatch + 1];
+  __shared__ int cuQ2[kMaxBatch + 1];
   if (threadIdx.x == 0) {
-    int q = 0;
+    int q = 0, q2 = 0;
     for (int b = 0; b < a.B; ++b) {
       cuQ[b] = q;
+      cuQ2[b] = q2;
       q += (a.cuU[b + 1] - a.cuU[b] + kQTile - 1) / kQTile;
+      q2 += (a.cuU[b + 1] - a.cuU[b] + kQTile2 - 1) / kQTile2;
     }
     cuQ[a.B] = q;
+    cuQ2[a.B] = q2;
   }
   __syncthreads();
-  const int nQ = cuQ[a.B];
+  const int nQ = cuQ[a.B], nQ2 = cuQ2[a.B];
   const int gid = blockIdx.x * blockDim.x + threadIdx.x;
   if (blockIdx.x == 0) {
     for (int b = threadIdx.x; b <= a.B; b += blockDim.x) {
       m.cuT[b] = a.cuT[b]; m.cuS[b] = a.cuS[b]; m.cuU[b] = a.cuU[b]; m.cuQ[b] = cuQ[b];
+      m.cuQ2[b] = cuQ2[b];
     }
   }
   const int stride = gridDim.x * blockDim.x;
@@ -40,6 +46,7 @@ __global__ void __launch_bounds__(256) k_meta(MetaArgs a, MetaDev m, int T_tot, 
   for (int r = gid; r < S_tot; r += stride) m.rowS[r] = find_clip(a.cuS, a.B, r);
   for (int r = gid; r < U_tot; r += stride) m.rowU[r] = find_clip(a.cuU, a.B, r);
   for (int r = gid; r < nQ; r += stride) m.tileQ[r] = find_clip(cuQ, a.B, r);
+  for (int r = gid; r < nQ2; r += stride) m.tileQ2[r] = find_clip(cuQ2, a.B, r);
 }
 
 hipError_t launch_meta(const MetaArgs& a, const MetaDev& m, int T_tot, int S_tot, int U_tot,
