@@ -32,21 +32,18 @@ PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "w8f16": 2516.6, "w6f16": 2516.6, 
                "f32": 157.3}   # dense MFMA (the quantised dtypes multiply in fp16)
 PEAK_HBM_GBS = 8000.0
 
-# HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE on this benchmark (batch32,
-# fp16), scaled by the same counters' reading of a plain 512 MiB copy (FETCH_SIZE x 2.0,
-# WRITE_SIZE x 1.0); reported only while the GEMM source is the one measured.
 # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch) on this
 # bench, scaled by what the counters read for a plain copy of known size; valid only while the
 # kernel's source is the one the counters were taken on (sha256 prefix)
-GEMM_SRC = ("conformer_speech_recognition_amd/csrc/gemm.hip", "cbcedd65d7437a0d")
-ATTN_SRC = ("conformer_speech_recognition_amd/csrc/attention.hip", "95db4798160df9cc")
-TRAFFIC_KIB = {("batch32", "gemm.ffn_up"): (GEMM_SRC, 41513, 49242),
-               ("batch32", "gemm.ffn_down"): (GEMM_SRC, 83896, 24621),
-               ("batch32", "gemm.qkv"): (GEMM_SRC, 43072, 36932),
-               ("batch32", "gemm.pw1_glu"): (GEMM_SRC, 21270, 12310),
+GEMM_SRC = ("conformer_speech_recognition_amd/csrc/gemm.hip", "105ada521bf71138")
+ATTN_SRC = ("conformer_speech_recognition_amd/csrc/attention.hip", "96ea1ed4a935c859")
+TRAFFIC_KIB = {("batch32", "gemm.ffn_up"): (GEMM_SRC, 41514, 49242),
+               ("batch32", "gemm.ffn_down"): (GEMM_SRC, 83897, 24621),
+               ("batch32", "gemm.qkv"): (GEMM_SRC, 43130, 36932),
+               ("batch32", "gemm.pw1_glu"): (GEMM_SRC, 21265, 12310),
                ("batch32", "gemm.out_proj"): (GEMM_SRC, 25743, 24621),
                ("batch32", "gemm.pw2"): (GEMM_SRC, 25743, 24621),
-               ("batch32", "attention"): (ATTN_SRC, 34458, 12921)}
+               ("batch32", "attention"): (ATTN_SRC, 27917, 14536)}
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 
 
@@ -467,6 +464,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the vendor-library GEMM and copy peak measurements (profiled runs)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="end with one plain 256 MiB device copy: the known-size reference for "
+                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
     ap.add_argument("--rnnt", action="store_true",
                     help="also time greedy RNNT decoding (character head, 34 classes) of every "
                          "encoded batch and report it beside the encoder line")
@@ -596,6 +596,24 @@ def main():
         line["gemm_variants"] = gemm_variants_leg(cfg, line["config"]["encoder_frames"])
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(a.workload, a.cpu_budget)
+    if a.calib_copy:
+        src = torch.ones(1 << 26, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        line["calib_copy_bytes"] = 1 << 28
+        del src, dst
+        # the same check for direct-to-LDS loads: one 256 x 128 tile of the pipelined fp16 GEMM
+        # with K = 65536 reads A (32 MiB) and W (16 MiB) exactly once
+        A = torch.ones(256, 65536, device="cuda", dtype=torch.half)
+        Wt = torch.ones(128, 65536, device="cuda", dtype=torch.half)
+        C = torch.empty(256, 128, device="cuda")
+        torch.cuda.synchronize()
+        line["calib_dma_shape"] = gg.debug_gemm_role("f16", "plain", "f32", A, Wt, C, split=False)[2]
+        torch.cuda.synchronize()
+        line["calib_dma_read_bytes"] = (256 + 128) * 65536 * 2
+        del A, Wt, C
     print(json.dumps(line), flush=True)
 
 
