@@ -39,6 +39,7 @@ struct MetaDev {           // device view of the meta region
   int* cuT; int* cuS; int* cuU; int* cuQ;
   int* rowT; int* rowS; int* rowU; int* tileQ;
   int* cuQ2; int* tileQ2;
+  int* tileG;              // 4 ints per 64-frame tile: first row, clip length, first frame, clip
 };
 
 template <typename T> struct TypeOf;

@@ -538,7 +538,7 @@ extern "C" void gigaam_destroy(gigaam_model* m) { delete m; }
 namespace {
 
 struct Ws {
-  size_t cuT, cuS, cuU, cuQ, rowT, rowS, rowU, tileQ, cuQ2, tileQ2;
+  size_t cuT, cuS, cuU, cuQ, rowT, rowS, rowU, tileQ, cuQ2, tileQ2, tileG;
   size_t mel, h1, x, y, r, qkv, ao, hid, cos_t, sin_t, logits, fids, part, fe;
   size_t total;
 };
@@ -554,6 +554,7 @@ Ws plan(const gigaam_config& c, int B, int T_tot, int S_tot, int U_tot, int nQ, 
   w.tileQ = take((size_t)nQ * 4);
   w.cuQ2 = take((B + 1) * 4);
   w.tileQ2 = take((size_t)nQ * 4);            // nQ2 <= nQ
+  w.tileG = take((size_t)nQ * 16);
   w.mel = take((size_t)T_tot * 64 * 4);
   w.h1 = take((size_t)S_tot * d * es);
   w.x = take((size_t)U_tot * d * 4);
@@ -673,7 +674,7 @@ int run(gigaam_model* m, const float* pcm, const int32_t* lengths, int32_t B, in
   char* W = (char*)ws;
   MetaDev md{(int*)(W + w.cuT), (int*)(W + w.cuS), (int*)(W + w.cuU), (int*)(W + w.cuQ),
              (int*)(W + w.rowT), (int*)(W + w.rowS), (int*)(W + w.rowU), (int*)(W + w.tileQ),
-             (int*)(W + w.cuQ2), (int*)(W + w.tileQ2)};
+             (int*)(W + w.cuQ2), (int*)(W + w.tileQ2), (int*)(W + w.tileG)};
   float* mel = (float*)(W + w.mel);
   char* h1 = W + w.h1;
   float* x = (float*)(W + w.x);
@@ -758,7 +759,7 @@ int run(gigaam_model* m, const float* pcm, const int32_t* lengths, int32_t B, in
                 (float)(1.4426950408889634 / std::sqrt((double)dk))};
   DwParams dp;
   dp.in = hid; dp.out = hid2; dp.d = d; dp.n_tiles = nQ; dp.cuU = md.cuU; dp.cuQ = md.cuQ;
-  dp.tileQ = md.tileQ; dp.eps = c.bn_eps;
+  dp.tileQ = md.tileQ; dp.tileG = md.tileG; dp.eps = c.bn_eps;
 
   if ((rc = LN(LN_PLAIN, L.layers[0].ff1_g, L.layers[0].ff1_b, nullptr, nullptr, y, nullptr))) return rc;
   for (int li = 0; li < c.n_layers; ++li) {
@@ -1022,7 +1023,7 @@ extern "C" int gigaam_debug_attention(int32_t dtype, int32_t d_model, int32_t n_
   const int c1 = batch + 1;                    // five clip tables, then five row/tile tables
   int* rows = w + 5 * c1;
   MetaDev md{w, w + c1, w + 2 * c1, w + 3 * c1, rows, rows + U_tot, rows + 2 * U_tot,
-             rows + 3 * U_tot, w + 4 * c1, rows + 4 * U_tot};
+             rows + 3 * U_tot, w + 4 * c1, rows + 4 * U_tot, nullptr};
   hipStream_t s = (hipStream_t)hip_stream;
   HIP_TRY(launch_meta(meta, md, U_tot, U_tot, U_tot, s));
   const bool f32 = dtype == GIGAAM_F32;

@@ -129,6 +129,7 @@ struct DwParams {
   const float* bn_g; const float* bn_b; const float* bn_m; const float* bn_v;
   int d, n_tiles;
   const int* cuU; const int* cuQ; const int* tileQ;
+  const int* tileG;                // per 64-frame tile: first row, clip length, first frame, clip
   float eps;
 };
 hipError_t launch_dwconv(DType dt, int kernel, const DwParams& p, hipStream_t s);

@@ -1,6 +1,7 @@
 // Batch geometry on the device: clip offsets and row -> clip maps of the packed
 // mel (T), first-conv (S) and encoder (U) row spaces, plus the 64-frame tiles (depthwise
-// conv) and 128-frame query tiles (attention) of every clip.
+// conv, with each tile's clip geometry in one 16-byte record) and 128-frame query tiles
+// (attention) of every clip.
 // Variable-length clips are packed back to back so every per-frame kernel touches valid
 // frames only (batched chunks with masks: "GigaAM MLX port for Mac", section "What is
 // inside the model").
@@ -45,7 +46,14 @@ __global__ void __launch_bounds__(256) k_meta(MetaArgs a, MetaDev m, int T_tot, 
   for (int r = gid; r < T_tot; r += stride) m.rowT[r] = find_clip(a.cuT, a.B, r);
   for (int r = gid; r < S_tot; r += stride) m.rowS[r] = find_clip(a.cuS, a.B, r);
   for (int r = gid; r < U_tot; r += stride) m.rowU[r] = find_clip(a.cuU, a.B, r);
-  for (int r = gid; r < nQ; r += stride) m.tileQ[r] = find_clip(cuQ, a.B, r);
+  for (int r = gid; r < nQ; r += stride) {
+    const int b = find_clip(cuQ, a.B, r);
+    m.tileQ[r] = b;
+    if (m.tileG) {
+      const int4 g = {a.cuU[b], a.cuU[b + 1] - a.cuU[b], (r - cuQ[b]) * kQTile, b};
+      *(int4*)(m.tileG + 4 * r) = g;
+    }
+  }
   for (int r = gid; r < nQ2; r += stride) m.tileQ2[r] = find_clip(cuQ2, a.B, r);
 }
 
