@@ -137,13 +137,35 @@ __global__ void __launch_bounds__(256, 4) k_attn(AttnParams p) {
   // this thread's tile loads: 16-byte K and V chunks (e = tid + 256 i: key e / CPR, chunk
   // e % CPR), as raw buffer loads against a per-tile resource that ends at the clip's last
   // row: rows past the clip read as zero
-  int koff[KPT], kls[KPT], vls[KPT];
+  // Chunk e of a tile goes to LDS so that every 16 lanes of one store hit disjoint banks:
+  //  K (row pitch 28 dwords): 16 consecutive keys, one chunk column;
+  //  V (row pitch 48 dwords): 4 consecutive keys x 4 consecutive chunks (the last
+  //    chunks of each row, fewer than 4, take 8 keys x 2 chunks).
+  int koff[KPT], voff[KPT], kls[KPT], vls[KPT];
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
-    const int e = tid + 256 * i, key = e / CPR, ch = e - key * CPR;
-    koff[i] = (key * ld + ch * 8) * (int)sizeof(T);
-    kls[i] = key * KP + ch * 8;
-    vls[i] = key * VP + ch * 8;
+    const int e = tid + 256 * i;
+    {
+      const int blk = e / (16 * CPR), r = e - blk * 16 * CPR;
+      const int key = 16 * blk + (r & 15), ch = r >> 4;
+      koff[i] = (key * ld + ch * 8) * (int)sizeof(T);
+      kls[i] = key * KP + ch * 8;
+    }
+    {
+      constexpr int C4 = CPR / 4 * 4;               // chunks placed 4 at a time
+      int key, ch;
+      if (e < AT_KV * C4) {
+        const int g = e >> 4, l = e & 15, cg = g / (AT_KV / 4), kg = g - cg * (AT_KV / 4);
+        key = 4 * kg + (l >> 2);
+        ch = 4 * cg + (l & 3);
+      } else {
+        const int r = e - AT_KV * C4, w = CPR - C4;
+        key = r / w;
+        ch = C4 + r % w;
+      }
+      voff[i] = (key * ld + ch * 8) * (int)sizeof(T);
+      vls[i] = key * VP + ch * 8;
+    }
   }
   u32x4 rk[KPT], rv[KPT];
   auto load = [&](int kv0) {
@@ -156,7 +178,7 @@ __global__ void __launch_bounds__(256, 4) k_attn(AttnParams p) {
     for (int i = 0; i < KPT; ++i)
       if (KCH % 256 == 0 || tid + 256 * i < KCH) {
         rk[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rK, koff[i], 0, 0));
-        rv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rV, koff[i], 0, 0));
+        rv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rV, voff[i], 0, 0));
       }
   };
   auto store = [&](int buf) {

@@ -32,7 +32,8 @@ struct MetaArgs {          // passed by value to the meta kernel (kernarg, < 4 K
   int cuU[kMaxBatch + 1];
 };
 
-// Attention works on 128-frame query tiles (cuQ2 / tileQ2, numbered the same way).
+// Attention works on 128-frame query tiles (cuQ2 / tileQ2; numbered clip by clip, longest
+// clip first).
 constexpr int kQTile2 = 128;
 
 struct MetaDev {           // device view of the meta region

@@ -1,7 +1,7 @@
 // Batch geometry on the device: clip offsets and row -> clip maps of the packed
 // mel (T), first-conv (S) and encoder (U) row spaces, plus the 64-frame tiles (depthwise
 // conv, with each tile's clip geometry in one 16-byte record) and 128-frame query tiles
-// (attention) of every clip.
+// (attention, numbered longest clip first) of every clip.
 // Variable-length clips are packed back to back so every per-frame kernel touches valid
 // frames only (batched chunks with masks: "GigaAM MLX port for Mac", section "What is
 // inside the model").
@@ -21,16 +21,36 @@ __device__ __forceinline__ int find_clip(const int* cu, int B, int r) {
 __global__ void __launch_bounds__(256) k_meta(MetaArgs a, MetaDev m, int T_tot, int S_tot,
                                               int U_tot) {
   __shared__ int cuQ[kMaxBatch + 1];
-  __shared__ int cuQ2[kMaxBatch + 1];
+  __shared__ int cuQ2[kMaxBatch + 1];     // indexed by clip
+  __shared__ int cuQ2s[kMaxBatch + 1];    // indexed by rank
+  __shared__ int order[kMaxBatch];        // clips by length, longest first (ties: index)
+  // The 128-frame query tiles are numbered clip by clip in that order, so the attention
+  // grid (dispatched in tile order) starts the longest clips' work first and ends on the
+  // shortest: the last, partly filled round of workgroups is the cheapest.
+  for (int b = threadIdx.x; b < a.B; b += blockDim.x) {
+    const int Ub = a.cuU[b + 1] - a.cuU[b];
+    int r = 0;
+    for (int k = 0; k < a.B; ++k) {
+      const int Uk = a.cuU[k + 1] - a.cuU[k];
+      r += (Uk > Ub) || (Uk == Ub && k < b);
+    }
+    order[r] = b;
+  }
+  __syncthreads();
   if (threadIdx.x == 0) {
     int q = 0, q2 = 0;
     for (int b = 0; b < a.B; ++b) {
       cuQ[b] = q;
-      cuQ2[b] = q2;
       q += (a.cuU[b + 1] - a.cuU[b] + kQTile - 1) / kQTile;
-      q2 += (a.cuU[b + 1] - a.cuU[b] + kQTile2 - 1) / kQTile2;
     }
     cuQ[a.B] = q;
+    for (int i = 0; i < a.B; ++i) {
+      const int b = order[i];
+      cuQ2s[i] = q2;
+      cuQ2[b] = q2;
+      q2 += (a.cuU[b + 1] - a.cuU[b] + kQTile2 - 1) / kQTile2;
+    }
+    cuQ2s[a.B] = q2;
     cuQ2[a.B] = q2;
   }
   __syncthreads();
@@ -54,7 +74,7 @@ __global__ void __launch_bounds__(256) k_meta(MetaArgs a, MetaDev m, int T_tot, 
       *(int4*)(m.tileG + 4 * r) = g;
     }
   }
-  for (int r = gid; r < nQ2; r += stride) m.tileQ2[r] = find_clip(cuQ2, a.B, r);
+  for (int r = gid; r < nQ2; r += stride) m.tileQ2[r] = order[find_clip(cuQ2s, a.B, r)];
 }
 
 hipError_t launch_meta(const MetaArgs& a, const MetaDev& m, int T_tot, int S_tot, int U_tot,
