@@ -196,9 +196,24 @@ def rnnt_leg(model, pcm_d, lens, cfg, steps, warmup):
         e1.synchronize()
         both_ms.append(e0.elapsed_time(e1))
     n = out["n_tokens"].cpu().numpy()
+    G = head.cluster_size(len(U))
+    # the same decode with one workgroup per clip, for comparison
+    head.set_max_cluster(1)
+    one_ms = []
+    for _ in range(max(1, steps // 2)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        out1 = head.decode(enc["enc_out"], U)
+        e1.record(st)
+        e1.synchronize()
+        one_ms.append(e0.elapsed_time(e1))
+    same = bool(torch.equal(out1["n_tokens"], out["n_tokens"]))
     audio_s = float(np.sum(lens)) / 16000.0
     return {"classes": 34, "dtype": rcfg["dtype"], "max_symbols": rcfg["max_symbols"],
+            "workgroups_per_clip": G,
             "decode_ms_p50": round(float(np.median(dec_ms)), 4),
+            "decode_ms_p50_one_workgroup_per_clip": round(float(np.median(one_ms)), 4),
+            "same_token_counts": same,
             "encode_plus_decode_ms_p50": round(float(np.median(both_ms)), 4),
             "encode_plus_decode_audio_s_per_s": round(audio_s / (float(np.median(both_ms)) * 1e-3), 1),
             "symbols_per_frame": round(float(n.sum()) / float(sum(U)), 3)}

@@ -121,6 +121,8 @@ _SIGNATURES = {
     "gigaam_rnnt_destroy": (None, [_P]),
     "gigaam_rnnt_workspace_bytes": (ctypes.c_int, [_P, _I, _I, ctypes.POINTER(_SZ)]),
     "gigaam_rnnt_decode": (ctypes.c_int, [_P, _P, _I, _IP, _I, _P, _SZ, _P, _P, _P, _I, _P]),
+    "gigaam_rnnt_cluster_size": (ctypes.c_int, [_P, _I, _IP]),
+    "gigaam_rnnt_set_max_cluster": (ctypes.c_int, [_P, _I]),
     "gigaam_stream_init": (ctypes.c_int, [ctypes.POINTER(StreamState), _I, _I]),
     "gigaam_stream_plan_push": (ctypes.c_int, [ctypes.POINTER(StreamState), _I, ctypes.POINTER(StreamPlan)]),
     "gigaam_stream_push": (ctypes.c_int, [ctypes.POINTER(StreamState), _P, _P, _I, _P]),
@@ -550,6 +552,16 @@ class RnntHead:
             self.close()
         except Exception:
             pass
+
+    def cluster_size(self, batch: int) -> int:
+        """Workgroups per clip the decoder would use for ``batch`` clips (1: one per clip)."""
+        g = ctypes.c_int32()
+        _check(lib().gigaam_rnnt_cluster_size(self._h, int(batch), ctypes.byref(g)))
+        return int(g.value)
+
+    def set_max_cluster(self, members: int):
+        """Cap the workgroups per clip (1: one workgroup per clip)."""
+        _check(lib().gigaam_rnnt_set_max_cluster(self._h, int(members)))
 
     def decode(self, enc, n_frames, stream=None) -> dict:
         """enc: float32 CUDA tensor [B, U_max, d]; n_frames: frames per clip (host).

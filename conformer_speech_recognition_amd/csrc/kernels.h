@@ -160,4 +160,23 @@ struct RnntParams {
 size_t rnnt_lds_bytes(DType dt, int P, int J, int Cp, bool wo_lds);
 hipError_t launch_rnnt_decode(DType dt, const RnntParams& p, int batch, hipStream_t s);
 
+// Clustered decoding (G cooperative workgroups per clip exchanging partial logits and h
+// slices through sequence-tagged 64-bit words).
+struct RnntCluster {
+  unsigned long long* xl;          // [batch][2][G][Cp] partial logits, then
+  unsigned long long* xh;          // [batch][2][P] h slices, then
+  unsigned long long* xc;          // [batch][G] each member's XCD (contiguous, xbytes in all)
+  int xbytes;
+  int batch;
+  int G;                           // members per clip (P % G == J % G == 0)
+  int wo_lds;                      // the member's W_out columns are copied to LDS
+  int spin_limit;                  // polls before a member gives up (its clip: n_tokens < 0)
+};
+long rnnt_cl_grid(int batch, int G);
+size_t rnnt_cl_lds_bytes(DType dt, int P, int J, int Cp, int G, bool wo_lds);
+// largest usable G <= max_g for this batch on the current device (1: none)
+int rnnt_cluster_size(DType dt, int P, int J, int Cp, int batch, int max_g);
+hipError_t launch_rnnt_cluster(DType dt, const RnntParams& p, const RnntCluster& q, int batch,
+                               hipStream_t s);
+
 }  // namespace gg

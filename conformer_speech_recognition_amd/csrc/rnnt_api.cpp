@@ -1,8 +1,10 @@
 // Host side of the RNNT head's C ABI (include/gigaam.h): configuration checks, the
 // canonical weight list, repacking, workspace planning and the launch sequence
-// (two GEMMs, then the per-clip greedy decoding kernel) on the caller's stream.
+// (two GEMMs, then the greedy decoding kernel: a cooperative cluster of workgroups per clip
+// when the batch leaves enough CUs, else one workgroup per clip) on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -64,6 +66,7 @@ struct gigaam_rnnt {
   gigaam_rnnt_config cfg;
   const char* w;
   RnntLayout L;
+  int max_cluster;
 };
 
 extern "C" int gigaam_rnnt_check_config(const gigaam_rnnt_config* c) {
@@ -173,6 +176,7 @@ extern "C" int gigaam_rnnt_create(const gigaam_rnnt_config* cfg, const void* pac
   h->cfg = *cfg;
   h->w = (const char*)packed_dev;
   h->L = L;
+  h->max_cluster = 64;
   *out = h;
   return GIGAAM_OK;
 }
@@ -180,17 +184,46 @@ extern "C" int gigaam_rnnt_create(const gigaam_rnnt_config* cfg, const void* pac
 extern "C" void gigaam_rnnt_destroy(gigaam_rnnt* head) { delete head; }
 
 namespace {
-struct RnntWs { size_t fenc, gemb, total; };
+// cluster members per clip the workspace is sized for: the clustered grid (clips in groups
+// of 8) within two workgroups on each of 256 CUs, G <= 64 (the launch itself checks the
+// occupancy of the device it runs on)
+int rnnt_gmax(int batch) {
+  int g = 1;
+  while (g < 64 && rnnt_cl_grid(batch, 2 * g) <= 512) g *= 2;
+  return g;
+}
+struct RnntWs { size_t fenc, gemb, xch, total; int gmax; };
 RnntWs rnnt_ws(const gigaam_rnnt_config& c, int batch, int stride) {
   RnntWs w;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = al256(off + bytes); return o; };
+  const int Cp = (c.n_classes + 7) / 8 * 8;
+  w.gmax = rnnt_gmax(batch);
   w.fenc = take((size_t)batch * stride * c.joint_hidden * 4);
   w.gemb = take((size_t)c.n_classes * 4 * c.pred_hidden * 4);
+  // the clustered decoder's exchange words: partial logits, then h slices, two slots each
+  w.xch = take(w.gmax > 1 ? ((size_t)batch * 2 * ((size_t)w.gmax * Cp + c.pred_hidden) + (size_t)batch * w.gmax) * 8
+                          : 0);
   w.total = off;
   return w;
 }
 }  // namespace
+
+extern "C" int gigaam_rnnt_set_max_cluster(gigaam_rnnt* head, int32_t max_members) {
+  if (!head) return fail(GIGAAM_E_INVAL, "head is NULL");
+  if (max_members < 1 || max_members > 64) return fail(GIGAAM_E_INVAL, "max_members %d outside [1, 64]", max_members);
+  head->max_cluster = max_members;
+  return GIGAAM_OK;
+}
+
+extern "C" int gigaam_rnnt_cluster_size(const gigaam_rnnt* head, int32_t batch, int32_t* members) {
+  if (!head || !members) return fail(GIGAAM_E_INVAL, "NULL pointer");
+  if (batch < 1 || batch > GIGAAM_MAX_BATCH) return fail(GIGAAM_E_INVAL, "batch %d", batch);
+  const gigaam_rnnt_config& c = head->cfg;
+  *members = rnnt_cluster_size((DType)c.dtype, c.pred_hidden, c.joint_hidden, head->L.Cp, batch,
+                               std::min(head->max_cluster, rnnt_gmax(batch)));
+  return GIGAAM_OK;
+}
 
 extern "C" int gigaam_rnnt_workspace_bytes(const gigaam_rnnt* head, int32_t batch, int32_t enc_stride,
                                            size_t* bytes) {
@@ -255,6 +288,20 @@ extern "C" int gigaam_rnnt_decode(gigaam_rnnt* head, const float* enc_dev, int32
   rp.wo_lds = rnnt_lds_bytes(dt, P, J, L.Cp, true) <= 96 * 1024;
   rp.tokens = tokens_dev; rp.tframes = token_frames_dev; rp.ntok = n_tokens_dev;
   for (int b = 0; b < batch; ++b) rp.frames[b] = frames_host[b];
-  HIP_TRY(launch_rnnt_decode(dt, rp, batch, s));
+  const int G = rnnt_cluster_size(dt, P, J, L.Cp, batch, std::min(head->max_cluster, w.gmax));
+  if (G >= 2) {
+    RnntCluster q;
+    q.xl = (unsigned long long*)(ws + w.xch);
+    q.xh = q.xl + (size_t)batch * 2 * G * L.Cp;
+    q.xc = q.xh + (size_t)batch * 2 * P;
+    q.xbytes = (int)(((size_t)batch * 2 * ((size_t)G * L.Cp + P) + (size_t)batch * G) * 8);
+    q.batch = batch;
+    q.G = G;
+    q.wo_lds = rnnt_cl_lds_bytes(dt, P, J, L.Cp, G, true) <= 160 * 1024;
+    q.spin_limit = 1 << 16;
+    HIP_TRY(launch_rnnt_cluster(dt, rp, q, batch, s));
+  } else {
+    HIP_TRY(launch_rnnt_decode(dt, rp, batch, s));
+  }
   return GIGAAM_OK;
 }

@@ -382,14 +382,28 @@ int gigaam_rnnt_workspace_bytes(const gigaam_rnnt* head, int32_t batch, int32_t 
  *   frames_host      int32 [batch], each in [1, enc_stride].
  *   tokens_dev       int32 [batch][max_tokens]: emitted symbols in order, -1 after them.
  *   token_frames_dev int32 [batch][max_tokens]: frame of each symbol, -1 after; or NULL.
- *   n_tokens_dev     int32 [batch].
+ *   n_tokens_dev     int32 [batch]; negative marks a clip whose cluster gave up (below).
  *   max_tokens       >= enc_stride * max_symbols (the most a clip can emit).
- * One workgroup per clip runs the whole sequential loop on the GPU (the stream is not
- * synchronised). Errors: GIGAAM_E_INVAL, GIGAAM_E_WORKSPACE, GIGAAM_E_HIP.            */
+ * The whole sequential loop runs on the GPU (the stream is not synchronised). When the
+ * batch leaves enough compute units ("GigaAM v3 MLX" card, section "Long-form stage
+ * breakdown": the decoding loop is the sequential bottleneck), each clip gets a cluster of
+ * G cooperatively launched workgroups (G a power of two, batch * G within the CUs, P and J
+ * multiples of G), each holding 1/G of W_hh, W_pred and W_out in LDS; the members exchange
+ * partial logits per decision and h slices per emission through the workspace. A member
+ * that waits for a partner beyond a fixed bound (tens of milliseconds; a partner that was
+ * never scheduled) ends its clip with a negative n_tokens instead of hanging. Otherwise one
+ * workgroup per clip. Both give the oracle's decisions within rounding (the sums are
+ * taken in a different order). Errors: GIGAAM_E_INVAL, GIGAAM_E_WORKSPACE, GIGAAM_E_HIP. */
 int gigaam_rnnt_decode(gigaam_rnnt* head, const float* enc_dev, int32_t enc_stride,
                        const int32_t* frames_host, int32_t batch, void* workspace,
                        size_t workspace_bytes, int32_t* tokens_dev, int32_t* token_frames_dev,
                        int32_t* n_tokens_dev, int32_t max_tokens, void* hip_stream);
+
+/* The cluster size gigaam_rnnt_decode would use for `batch` clips on the current device
+ * (1: one workgroup per clip), and a cap on it for this handle (max_members in [1, 64];
+ * 1 forces one workgroup per clip; the default cap is 64). Errors: GIGAAM_E_INVAL.      */
+int gigaam_rnnt_cluster_size(const gigaam_rnnt* head, int32_t batch, int32_t* members);
+int gigaam_rnnt_set_max_cluster(gigaam_rnnt* head, int32_t max_members);
 
 /* ---------------------------------------------------------------------------------
  * Pseudo-streaming ("GigaAM on MLX ...", section "Streaming: honestly, it's

@@ -54,23 +54,30 @@ def _structure(out, frames, max_symbols):
     return tok, fr, n
 
 
+@pytest.mark.parametrize("members", ["cluster", "single"])
 @pytest.mark.parametrize("dtype,C", [("f32", 34), ("f16", 34), ("bf16", 34), ("f16", 1025)])
-def test_rnnt_head_matches_oracle(dtype, C):
+def test_rnnt_head_matches_oracle(dtype, C, members):
+    """Both decoders: a cluster of cooperating workgroups per clip (the default for a batch
+    that leaves enough CUs) and one workgroup per clip (the cap set to 1)."""
     import torch
     import conformer_speech_recognition_amd as gg
     cfg = synth.rnnt_config(768, C, dtype)
     w = synth.make_rnnt_weights(cfg, 21)
     P = {k: np.asarray(v, np.float64) for k, v in w.items()}
     enc = synth.make_encoder_like(np.random.default_rng(22), FRAMES, 768)
-    say(f"[rnnt] head {dtype} C={C}: decode {len(FRAMES)} clips")
     head = gg.RnntHead(cfg, w)
+    if members == "single":
+        head.set_max_cluster(1)
+    G = head.cluster_size(len(FRAMES))
+    say(f"[rnnt] head {dtype} C={C}: decode {len(FRAMES)} clips, {G} workgroups per clip")
+    assert G == 1 if members == "single" else G >= 2
     out = head.decode(torch.from_numpy(enc).cuda(), FRAMES)
     torch.cuda.synchronize()
     tok, fr, n = _structure(out, FRAMES, cfg["max_symbols"])
     ex = tot = 0
     for b, u in enumerate(FRAMES):
         e, t = _check_clip(P, enc[b, :u].astype(np.float64), tok[b], fr[b], n[b],
-                           cfg["max_symbols"], dtype, f"{dtype} C={C} clip {b}")
+                           cfg["max_symbols"], dtype, f"{dtype} C={C} G={G} clip {b}")
         ex += e
         tot += t
     assert ex / tot >= 0.995

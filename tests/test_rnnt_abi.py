@@ -110,3 +110,37 @@ def test_rnnt_decode_argument_errors_before_any_launch(gg):
     assert dec(tokens=None) == gg.E_INVAL
     L.gigaam_rnnt_destroy(h)
     assert L.gigaam_rnnt_create(ctypes.byref(c), fake + 8, ctypes.byref(h)) == gg.E_INVAL
+
+
+def test_rnnt_cluster_controls_validate_and_size_the_workspace(gg):
+    """The cap on the decoding cluster is range-checked; the workspace grows with the
+    exchange words of the clustered decoder (two slots of partial logits and h slices per
+    clip, one XCD word per member), sized for up to two workgroups per CU."""
+    L = gg.lib()
+    cfg = synth.rnnt_config(768, 34, "f16")
+    c = gg.make_rnnt_config(cfg)
+    h = ctypes.c_void_p()
+    assert L.gigaam_rnnt_create(ctypes.byref(c), 1 << 20, ctypes.byref(h)) == 0
+    assert L.gigaam_rnnt_set_max_cluster(h, 0) == gg.E_INVAL
+    assert L.gigaam_rnnt_set_max_cluster(h, 65) == gg.E_INVAL
+    assert L.gigaam_rnnt_set_max_cluster(None, 4) == gg.E_INVAL
+    assert L.gigaam_rnnt_set_max_cluster(h, 1) == 0
+    g = ctypes.c_int32()
+    assert L.gigaam_rnnt_cluster_size(h, 0, ctypes.byref(g)) == gg.E_INVAL
+    assert L.gigaam_rnnt_cluster_size(h, 4, None) == gg.E_INVAL
+
+    def ws(batch, stride):
+        nb = ctypes.c_size_t()
+        assert L.gigaam_rnnt_workspace_bytes(h, batch, stride, ctypes.byref(nb)) == 0
+        return nb.value
+
+    def al(x):
+        return (x + 255) // 256 * 256
+    P, J, C = cfg["pred_hidden"], cfg["joint_hidden"], cfg["n_classes"]
+    Cp = (C + 7) // 8 * 8
+    # clusters: clips in groups of 8 (one per XCD), (groups * 8) * G <= 2 x 256 CUs, G <= 64
+    for batch, stride, gmax in ((32, 100, 16), (6, 40, 64), (1, 10, 64), (9, 10, 32), (256, 20, 2)):
+        base = al(batch * stride * J * 4) + al(C * 4 * P * 4)
+        xch = al((batch * 2 * (gmax * Cp + P) + batch * gmax) * 8) if gmax > 1 else 0
+        assert ws(batch, stride) == base + xch, (batch, gmax)
+    L.gigaam_rnnt_destroy(h)
