@@ -84,31 +84,51 @@ __global__ void __launch_bounds__(256) k_frontend(const float* __restrict__ pcm,
   float (*zr)[20][ZP] = (float (*)[20][ZP])region;
   float (*zi)[20][ZP] = (float (*)[20][ZP])(region + ZSZ);
   float (*P)[FE_K + 3] = (float (*)[FE_K + 3])region;
+  __shared__ long foff[FE_FT];                   // each frame's first sample in pcm (-1: none)
   const int tid = threadIdx.x;
   const int f0 = blockIdx.x * FE_FT;
+  const int f1 = tid / 20, n21 = tid - f1 * 20;  // stage-1 thread (frame, n2)
+  const int mm = tid & (FE_M - 1);               // this thread's mel filter (every pass)
 
+  // Everything that does not depend on the samples is loaded first and independently of
+  // them: the frames' clip geometry (one dependent pair of loads per frame, not per
+  // sample), the twiddles, this stage-1 thread's 16 window values and this thread's mel
+  // filter's nonzero range (its weights are loaded during stage 2).
+  if (tid < FE_FT) {
+    const int g = f0 + tid;
+    long off = -1;
+    if (g < T_tot) {
+      const int b = m.rowT[g];
+      off = (long)b * stride + 160L * (g - m.cuT[b]);
+    }
+    foff[tid] = off;
+  }
   for (int i = tid; i < FE_N; i += 256) {
     tc[i] = tw[i];
     ts[i] = tw[FE_N + i];
   }
-  for (int e = tid; e < FE_FT * FE_N; e += 256) {
-    const int f = e / FE_N, n = e - f * FE_N, g = f0 + f;
-    float v = 0.f;
-    if (g < T_tot) {
-      const int b = m.rowT[g];
-      const int t = g - m.cuT[b];
-      v = pcm[(long)b * stride + 160 * t + n] * window[n];
+  float win[16];
+#pragma unroll
+  for (int n1 = 0; n1 < 16; ++n1) win[n1] = tid < FE_FT * 20 ? window[20 * n1 + n21] : 0.f;
+  const int lo = melr[2 * mm], hi = melr[2 * mm + 1];
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < (FE_FT * FE_N + 255) / 256; ++r) {   // independent loads, all in flight
+    const int e = tid + 256 * r;
+    if (e < FE_FT * FE_N) {
+      const int f = e / FE_N, n = e - f * FE_N;
+      const long off = foff[f];
+      xw[f][n] = off >= 0 ? pcm[off + n] : 0.f;
     }
-    xw[f][n] = v;
   }
   __syncthreads();
 
-  // stage 1: thread (f, n2) -> 16-point DFT over n1, then the W320^(n2 k1) twiddle
-  const int f1 = tid / 20, n21 = tid - f1 * 20;
+  // stage 1: thread (f, n2) -> 16-point DFT over n1 of the windowed frame, then the
+  // W320^(n2 k1) twiddle
   float x[16];
   if (tid < FE_FT * 20) {
 #pragma unroll
-    for (int n1 = 0; n1 < 16; ++n1) x[n1] = xw[f1][20 * n1 + n21];
+    for (int n1 = 0; n1 < 16; ++n1) x[n1] = xw[f1][20 * n1 + n21] * win[n1];
   }
   __syncthreads();                               // the frames are in registers: reuse
   if (tid < FE_FT * 20) {
@@ -138,6 +158,12 @@ __global__ void __launch_bounds__(256) k_frontend(const float* __restrict__ pcm,
     for (int n2 = 0; n2 < 20; ++n2) { ar[n2] = zr[f2][n2][k12]; ai[n2] = zi[f2][n2][k12]; }
   }
   __syncthreads();                               // stage-1 outputs in registers: reuse
+  // this thread's mel filter weights (the HTK filters span at most 13 bins), in flight
+  // during stage 2
+  constexpr int MW = 16;
+  float wts[MW];
+#pragma unroll
+  for (int j = 0; j < MW; ++j) wts[j] = lo + j <= hi ? fb[(lo + j) * FE_M + mm] : 0.f;
   if (tid < FE_FT * 16) {
     const int f = f2, k1 = k12;
 #pragma unroll
@@ -158,13 +184,15 @@ __global__ void __launch_bounds__(256) k_frontend(const float* __restrict__ pcm,
   }
   __syncthreads();
 
-  // mel projection + log clip: thread (f, m)
+  // mel projection + log clip: thread (f, m), the filter's weights already in registers
+  // (a wider filter continues from the table), summed in ascending bin order
   for (int e = tid; e < FE_FT * FE_M; e += 256) {
-    const int f = e >> 6, mm = e & 63;
-    const int lo = melr[2 * mm], hi = melr[2 * mm + 1];
+    const int f = e >> 6;
     float acc = 0.f;
-#pragma unroll 4
-    for (int k = lo; k <= hi; ++k) acc = fmaf(fb[k * FE_M + mm], P[f][k], acc);
+#pragma unroll
+    for (int j = 0; j < MW; ++j)
+      if (lo + j <= hi) acc = fmaf(wts[j], P[f][lo + j], acc);
+    for (int k = lo + MW; k <= hi; ++k) acc = fmaf(fb[k * FE_M + mm], P[f][k], acc);
     const int g = f0 + f;
     if (g < T_tot) mel[(long)g * FE_M + mm] = logf(fminf(fmaxf(acc, 1e-9f), 1e9f));
   }
