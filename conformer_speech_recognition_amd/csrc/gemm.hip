@@ -428,6 +428,9 @@ constexpr int chunk_rows(int BM, int fit) {
   return c;
 }
 
+// 16 zero bytes: the source of every load of a subsampling-conv tap that falls outside its clip
+__device__ __align__(16) uint32_t g_zero16[4] = {0u, 0u, 0u, 0u};
+
 template <typename T, int BM, int BN, int WGM, int WGN, int S, int KB, int AM, int EP, int OCC = 1>
 __global__ void __launch_bounds__(64 * WGM * WGN, OCC) k_gemm_p(GemmParams p) {
   constexpr int NW = WGM * WGN, NT = 64 * NW;
@@ -444,6 +447,8 @@ __global__ void __launch_bounds__(64 * WGM * WGN, OCC) k_gemm_p(GemmParams p) {
   // the prologue leaves up to S - 1 load groups in flight (the vmcnt field is 6 bits)
   static_assert(LPW * (S - 1) <= 63 && S >= 2, "vmcnt range");
   static_assert(EP != E_GLU || NI % 2 == 0, "GLU needs value/gate block pairs");
+  static_assert(AM == A_PLAIN || AM == A_DUAL || AM == A_CONV, "A mode");
+  constexpr bool CONV = AM == A_CONV;
   __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -457,6 +462,13 @@ __global__ void __launch_bounds__(64 * WGM * WGN, OCC) k_gemm_p(GemmParams p) {
   const long koff = (long)blockIdx.y * p.K;            // split-K slice
   if (gridDim.y > 1) p.C = (float*)p.C + blockIdx.y * (long)p.M * p.ldc;
 
+  // The implicit subsampling conv (kernel 5, stride 2, padding 2, clips packed by rows):
+  // the A row of output frame s of clip b is source rows r0 .. r0 + 4 (r0 = the clip's
+  // first source row + 2s - 2) laid end to end, which is contiguous memory, so it streams
+  // like a plain row. A k-tile lies inside one tap (cin is a multiple of KB); a tap outside
+  // the clip loads the zero chunk instead. Bit 5i + j of tapok: load i's row has tap j
+  // inside its clip (all bits set for weight rows).
+  unsigned long long tapok = 0;
   const char* src[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
@@ -464,12 +476,36 @@ __global__ void __launch_bounds__(64 * WGM * WGN, OCC) k_gemm_p(GemmParams p) {
     const int lc = (lane % CPR) ^ ((R >> SWS) & (CPR - 1));
     if (R < BM) {
       const int gm = m0 + R < p.M ? m0 + R : p.M - 1;
-      src[i] = Ab + ((long)gm * p.lda + koff + lc * 8) * sizeof(T);
+      if constexpr (CONV) {
+        const int b = p.rowclip[gm];
+        const int lo = p.cu_in[b], hi = p.cu_in[b + 1];
+        const long r0 = (long)lo + 2 * (gm - p.cu_out[b]) - 2;
+#pragma unroll
+        for (int j = 0; j < 5; ++j)
+          if (r0 + j >= lo && r0 + j < hi) tapok |= 1ull << (5 * i + j);
+        src[i] = Ab + (r0 * p.cin + koff + lc * 8) * (long)sizeof(T);
+      } else {
+        src[i] = Ab + ((long)gm * p.lda + koff + lc * 8) * sizeof(T);
+      }
     } else {
       const int gn = n0 + R - BM < p.N ? n0 + R - BM : p.N - 1;
       src[i] = (const char*)p.W + ((long)gn * p.ldw + koff + lc * 8) * sizeof(T);
+      tapok |= 31ull << (5 * i);
     }
   }
+  // tap of k-tile g: (koff / KB + g) / (cin / KB), by a multiply (exact while the k-tile
+  // index times cin / KB stays below 2^20)
+  const uint32_t kt_tap = CONV ? (uint32_t)(p.cin / KB) : 1u;
+  const uint32_t tap_mul = (1u << 20) / kt_tap + 1u;
+  const uint32_t kt0 = (uint32_t)(koff / KB);
+  auto asrc = [&](int i, int g) -> const char* {
+    const char* a = src[i] + (long)g * RB;
+    if constexpr (CONV) {
+      const uint32_t j = ((kt0 + (uint32_t)g) * tap_mul) >> 20;
+      if (!((tapok >> (5 * i + j)) & 1ull)) a = (const char*)g_zero16;
+    }
+    return a;
+  };
   const uint32_t sbase = lds_u32(smem) + wave * LPW * 1024;
 
   f32x16 acc[NI][MI];
@@ -491,7 +527,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, OCC) k_gemm_p(GemmParams p) {
   };
 
   // epilogue geometry: the output is staged through LDS in chunks of CH rows
-  constexpr bool F32OUT = (EP == E_RESID || EP == E_F32);
+  constexpr bool F32OUT = (EP == E_RESID || EP == E_F32 || EP == E_RELU_F32);
   constexpr int OES = F32OUT ? 4 : (int)sizeof(T);
   constexpr int BNO = (EP == E_GLU) ? BN / 2 : BN;
   constexpr int PITCH = BNO * OES + 16;
@@ -528,7 +564,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, OCC) k_gemm_p(GemmParams p) {
   for (int g = 0; g < S; ++g)
     if (g < KT)
 #pragma unroll
-      for (int i = 0; i < LPW; ++i) dma16(sbase + g * STAGE + i * 1024, src[i] + g * RB);
+      for (int i = 0; i < LPW; ++i) dma16(sbase + g * STAGE + i * 1024, asrc(i, g));
   wait_groups<LPW, S - 1>((KT < S ? KT : S) - 1);
   __syncthreads();
 #pragma unroll
@@ -566,7 +602,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, OCC) k_gemm_p(GemmParams p) {
           if (more) {
 #pragma unroll
             for (int i = 0; i < LPW; ++i)          // loads spread evenly over the slots
-              if (i * NM / LPW == j) dma16(sbase + st * STAGE + i * 1024, src[i] + (kt + S) * RB);
+              if (i * NM / LPW == j) dma16(sbase + st * STAGE + i * 1024, asrc(i, kt + S));
           }
           // the next k-tile's first reads take the last slots (all slots when NR > NM)
           if (next && j >= R0) rd(sn, 0, 0, j - R0);
@@ -627,7 +663,8 @@ __global__ void __launch_bounds__(64 * WGM * WGN, OCC) k_gemm_p(GemmParams p) {
 #pragma unroll
               for (int j = 0; j < 4; ++j) {
                 const float x = acc[ni][mi][4 * g + j] + bv[ni][g][j];
-                v[j] = (EP == E_SILU) ? siluf_(x) : (EP == E_RESID) ? p.alpha * x : x;
+                v[j] = (EP == E_SILU) ? siluf_(x) : (EP == E_RESID) ? p.alpha * x
+                       : (EP == E_RELU_F32) ? fmaxf(x, 0.f) : x;
               }
               const int cs = wn * WTN + ni * 32 + 8 * g + h4;
               if constexpr (F32OUT) *(f32x4*)(srow + cs * 4) = v;
@@ -814,6 +851,7 @@ static hipError_t run_dl(AMode am, Epi ep, const GemmParams& p, hipStream_t s) {
   constexpr bool GLU_OK = ((BN / WGN) / 32) % 2 == 0;     // value / gate block pairs per wave
   if (ep == E_GLU && !GLU_OK) return hipErrorInvalidValue;
   if (am == A_DUAL && p.nsplit % BN != 0) return hipErrorInvalidValue;
+  if (am == A_CONV && (p.cin % KB != 0 || p.K != 5 * p.cin)) return hipErrorInvalidValue;
   const long tiles = (long)((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   const int ks = splitk_slices(p, tiles, KB, ep);
   dim3 blk(64 * WGM * WGN);
@@ -827,6 +865,8 @@ static hipError_t run_dl(AMode am, Epi ep, const GemmParams& p, hipStream_t s) {
     dim3 grid((unsigned)tiles, ks);
     if (am == A_DUAL)
       hipLaunchKernelGGL((k_gemm_p<T, BM, BN, WGM, WGN, S, KB, A_DUAL, E_F32, OCC>), grid, blk, 0, s, q);
+    else if (am == A_CONV)
+      hipLaunchKernelGGL((k_gemm_p<T, BM, BN, WGM, WGN, S, KB, A_CONV, E_F32, OCC>), grid, blk, 0, s, q);
     else
       hipLaunchKernelGGL((k_gemm_p<T, BM, BN, WGM, WGN, S, KB, A_PLAIN, E_F32, OCC>), grid, blk, 0, s, q);
     const hipError_t e = hipGetLastError();
@@ -841,7 +881,7 @@ static hipError_t run_dl(AMode am, Epi ep, const GemmParams& p, hipStream_t s) {
     return hipGetLastError();                                                                      \
   }
   GG_DL(A_PLAIN, E_STORE) GG_DL(A_PLAIN, E_SILU) GG_DL(A_PLAIN, E_RESID) GG_DL(A_PLAIN, E_F32)
-  GG_DL(A_DUAL, E_STORE)
+  GG_DL(A_DUAL, E_STORE) GG_DL(A_CONV, E_RELU_F32)
   if constexpr (GLU_OK) { GG_DL(A_PLAIN, E_GLU) }
 #undef GG_DL
   return hipErrorInvalidValue;
@@ -933,9 +973,11 @@ static hipError_t run_dl_shape(AMode am, Epi ep, const GemmParams& p, hipStream_
 }
 
 static bool direct_path(DType dt, int qbits, AMode am, Epi ep, const GemmParams& p) {
-  return dt != DT_F32 && qbits == 0 && (am == A_PLAIN || am == A_DUAL) && p.K % 64 == 0 &&
-         (ep == E_STORE || ep == E_SILU || ep == E_RESID || ep == E_GLU || ep == E_F32) &&
-         (am == A_PLAIN || ep == E_STORE);
+  if (dt == DT_F32 || qbits != 0 || p.K % 64 != 0) return false;
+  if (am == A_CONV) return ep == E_RELU_F32 && p.cin % 64 == 0 && p.K == 5 * p.cin;
+  if (am == A_DUAL) return ep == E_STORE;
+  return am == A_PLAIN &&
+         (ep == E_STORE || ep == E_SILU || ep == E_RESID || ep == E_GLU || ep == E_F32);
 }
 
 
