@@ -61,6 +61,15 @@ __device__ __forceinline__ float sigmoidf_(float x) {
 }
 __device__ __forceinline__ float siluf_(float x) { return x * sigmoidf_(x); }
 
+// Orders LDS accesses across the lanes of one wave (each wave owns its LDS slice): a
+// wavefront-scope release/acquire pair around a wave barrier, which, unlike a workgroup
+// barrier's fence, waits for no outstanding global access.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Lane exchanges for butterfly reductions, without the LDS crossbar that a shuffle
 // (ds_bpermute) goes through.
 //  * lanes 32 / 16 apart: v_permlane32_swap / v_permlane16_swap on two copies of a value

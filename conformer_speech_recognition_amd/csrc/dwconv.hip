@@ -72,14 +72,6 @@ __global__ void __launch_bounds__(256) k_dw32(DwParams p) {
   }
 }
 
-// Orders LDS accesses across the lanes of one wave (each wave owns its LDS slice): a
-// wavefront-scope release/acquire pair around a wave barrier, which, unlike a workgroup
-// barrier's fence, waits for no outstanding global access.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // storage-type pairs as the dot-product instructions take them
 template <typename T> struct Pair;

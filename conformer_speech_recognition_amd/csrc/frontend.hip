@@ -4,23 +4,28 @@
 // power 2.0; "GigaAM v3 RNNT - MLX" card, "Notes for other runtimes": the window and
 // filterbank are stored model buffers and the features are log(clip(x, 1e-9, 1e9)).
 //
-// One block turns FE_FT frames into FE_FT x 64 log-mel values entirely on chip. The
-// 320-point DFT of each windowed frame is factored as 320 = 16 x 20 (Cooley-Tukey with
-// n = 20 n1 + n2, k = k1 + 16 k2):
-//   Y[n2][k1] = sum_{n1<16} x[20 n1 + n2] W16^(n1 k1)           (16-point DFTs)
-//   Z[n2][k1] = Y[n2][k1] W320^(n2 k1)                           (twiddle)
-//   X[k1 + 16 k2] = sum_{n2<20} Z[n2][k1] W20^(n2 k2)            (20-point DFTs)
-// evaluated in fp32 with twiddles rounded from fp64, for bins k <= 160 only; then
-// power, mel projection and log-clip. The small DFTs keep their twiddles in registers.
-// A one-block prologue kernel builds, once per launch, the twiddle table and each mel
-// filter's range of nonzero weights; the projection sums over that range only, in the
-// same ascending order as the full sum, so the result is the same (the skipped terms
-// are exact zeros).
+// One wave turns two frames at a time into 2 x 64 log-mel values, 32 lanes per frame,
+// with no workgroup barrier in its loop. The 320-point DFT of the real windowed frame x
+// comes from one 160-point complex DFT of z[n] = x[2n] + i x[2n+1] (even samples as the
+// real part, odd as the imaginary part), factored as 160 = 5 x 32 (Cooley-Tukey with
+// n = 32 n1 + n2, k = k1 + 5 k2):
+//   Y[n2][k1] = sum_{n1<5} z[32 n1 + n2] W5^(n1 k1)          lane n2, in registers
+//   Y[n2][k1] *= W160^(n2 k1)                                 twiddle
+//   Z[k1 + 5 k2] = sum_{n2<32} Y[n2][k1] W32^(n2 k2)          radix-2 across the 32 lanes
+// The radix-2 steps are decimation in frequency over lane spans 16, 8, 4, 2, 1 (lane
+// exchanges), which leaves Z[k1 + 5 k2] in lane bitreverse(k2). Through the wave's LDS
+// slice, the even / odd halves are separated,
+//   E[k] = (Z[k] + conj Z[160 - k]) / 2,  O[k] = (Z[k] - conj Z[160 - k]) / 2i,
+//   X[k] = E[k] + W320^k O[k]  (k < 160),  X[160] = E[0] - O[0],
+// then power |X[k]|^2 for k <= 160, the mel projection and the log-clip. Everything is
+// fp32 with twiddles rounded from fp64. A one-block prologue kernel builds, once per
+// launch, the twiddle table and each mel filter's range of nonzero weights; the
+// projection sums over that range only, in the same ascending order as the full sum, so
+// the result is the same (the skipped terms are exact zeros).
 #include "kernels.h"
 
 namespace gg {
 
-constexpr int FE_FT = 12;     // frames per block
 constexpr int FE_N = 320;     // FFT size = window length
 constexpr int FE_K = 161;     // power bins 0..160
 constexpr int FE_M = 64;      // mel bins
@@ -66,135 +71,157 @@ __global__ void __launch_bounds__(FE_N) k_frontend_prep(const float* __restrict_
   }
 }
 
-__global__ void __launch_bounds__(256) k_frontend(const float* __restrict__ pcm, int stride,
-                                                  const float* __restrict__ window,
-                                                  const float* __restrict__ fb,
-                                                  const float* __restrict__ tw,
-                                                  const int* __restrict__ melr, MetaDev m,
-                                                  int T_tot, float* __restrict__ mel) {
-  // one LDS region holds, in turn, the windowed frames, the stage-1 outputs and the power
-  // spectra (each stage reads its input into registers before the next is written), so
-  // four blocks fit on a CU
-  constexpr int ZP = 17;                          // row pitch of the stage-1 outputs
-  constexpr int ZSZ = FE_FT * 20 * ZP;
-  static_assert(FE_FT * FE_N <= 2 * ZSZ && FE_FT * (FE_K + 3) <= 2 * ZSZ, "LDS reuse");
-  __shared__ float region[2 * ZSZ];
-  __shared__ float tc[FE_N], ts[FE_N];           // W320^j = tc[j] - i ts[j]
-  float (*xw)[FE_N] = (float (*)[FE_N])region;
-  float (*zr)[20][ZP] = (float (*)[20][ZP])region;
-  float (*zi)[20][ZP] = (float (*)[20][ZP])(region + ZSZ);
-  float (*P)[FE_K + 3] = (float (*)[FE_K + 3])region;
-  __shared__ long foff[FE_FT];                   // each frame's first sample in pcm (-1: none)
-  const int tid = threadIdx.x;
-  const int f0 = blockIdx.x * FE_FT;
-  const int f1 = tid / 20, n21 = tid - f1 * 20;  // stage-1 thread (frame, n2)
-  const int mm = tid & (FE_M - 1);               // this thread's mel filter (every pass)
+constexpr int FE_WAVES = 4;   // waves per block, each with its own LDS slice
 
-  // Everything that does not depend on the samples is loaded first and independently of
-  // them: the frames' clip geometry (one dependent pair of loads per frame, not per
-  // sample), the twiddles, this stage-1 thread's 16 window values and this thread's mel
-  // filter's nonzero range (its weights are loaded during stage 2).
-  if (tid < FE_FT) {
-    const int g = f0 + tid;
-    long off = -1;
-    if (g < T_tot) {
-      const int b = m.rowT[g];
-      off = (long)b * stride + 160L * (g - m.cuT[b]);
-    }
-    foff[tid] = off;
-  }
-  for (int i = tid; i < FE_N; i += 256) {
+__device__ __forceinline__ float2 cmul(float2 a, float c, float sn) {   // a (c - i sn)
+  return make_float2(fmaf(a.x, c, a.y * sn), fmaf(a.y, c, -a.x * sn));
+}
+
+__global__ void __launch_bounds__(64 * FE_WAVES) k_frontend(const float* __restrict__ pcm, int stride,
+                                                          const float* __restrict__ window,
+                                                          const float* __restrict__ fb,
+                                                          const float* __restrict__ tw,
+                                                          const int* __restrict__ melr, MetaDev m,
+                                                          int T_tot, float* __restrict__ mel) {
+  __shared__ float tc[FE_N], ts[FE_N];                  // W320^t = tc[t] - i ts[t]
+  __shared__ float2 zs[FE_WAVES][2][160];               // Z of the wave's two frames
+  __shared__ float ps[FE_WAVES][2][FE_K + 3];           // their power spectra
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int h = lane >> 5, j = lane & 31;               // frame of the pair, n2 / output lane
+
+  for (int i = threadIdx.x; i < FE_N; i += 64 * FE_WAVES) {
     tc[i] = tw[i];
     ts[i] = tw[FE_N + i];
   }
-  float win[16];
+  // per-lane constants, loaded once: this lane's 10 window values (samples 2j + 64 n1 and
+  // the next), its two mel filters (j and j + 32: range and up to 16 weights each)
+  float wv[5][2];
 #pragma unroll
-  for (int n1 = 0; n1 < 16; ++n1) win[n1] = tid < FE_FT * 20 ? window[20 * n1 + n21] : 0.f;
-  const int lo = melr[2 * mm], hi = melr[2 * mm + 1];
-  __syncthreads();
-#pragma unroll
-  for (int r = 0; r < (FE_FT * FE_N + 255) / 256; ++r) {   // independent loads, all in flight
-    const int e = tid + 256 * r;
-    if (e < FE_FT * FE_N) {
-      const int f = e / FE_N, n = e - f * FE_N;
-      const long off = foff[f];
-      xw[f][n] = off >= 0 ? pcm[off + n] : 0.f;
-    }
+  for (int n1 = 0; n1 < 5; ++n1) {
+    wv[n1][0] = window[2 * j + 64 * n1];
+    wv[n1][1] = window[2 * j + 64 * n1 + 1];
   }
-  __syncthreads();
-
-  // stage 1: thread (f, n2) -> 16-point DFT over n1 of the windowed frame, then the
-  // W320^(n2 k1) twiddle
-  float x[16];
-  if (tid < FE_FT * 20) {
-#pragma unroll
-    for (int n1 = 0; n1 < 16; ++n1) x[n1] = xw[f1][20 * n1 + n21] * win[n1];
-  }
-  __syncthreads();                               // the frames are in registers: reuse
-  if (tid < FE_FT * 20) {
-    const int f = f1, n2 = n21;
-#pragma unroll
-    for (int k1 = 0; k1 < 16; ++k1) {
-      float yr = 0.f, yi = 0.f;
-#pragma unroll
-      for (int n1 = 0; n1 < 16; ++n1) {
-        const int j = 20 * ((n1 * k1) & 15);      // W16^(n1 k1) = W320^(20 (n1 k1 mod 16))
-        yr = fmaf(x[n1], tc[j], yr);
-        yi = fmaf(-x[n1], ts[j], yi);
-      }
-      const int j = (n2 * k1) % FE_N;
-      const float c = tc[j], sn = ts[j];           // (yr + i yi)(c - i sn)
-      zr[f][n2][k1] = yr * c + yi * sn;
-      zi[f][n2][k1] = yi * c - yr * sn;
-    }
-  }
-  __syncthreads();
-
-  // stage 2: thread (f, k1) -> 20-point DFT over n2 for k2 = 0..10, power of bins <= 160
-  const int f2 = tid >> 4, k12 = tid & 15;
-  float ar[20], ai[20];
-  if (tid < FE_FT * 16) {
-#pragma unroll
-    for (int n2 = 0; n2 < 20; ++n2) { ar[n2] = zr[f2][n2][k12]; ai[n2] = zi[f2][n2][k12]; }
-  }
-  __syncthreads();                               // stage-1 outputs in registers: reuse
-  // this thread's mel filter weights (the HTK filters span at most 13 bins), in flight
-  // during stage 2
   constexpr int MW = 16;
-  float wts[MW];
+  int lo[2], hi[2];
+  float wts[2][MW];
 #pragma unroll
-  for (int j = 0; j < MW; ++j) wts[j] = lo + j <= hi ? fb[(lo + j) * FE_M + mm] : 0.f;
-  if (tid < FE_FT * 16) {
-    const int f = f2, k1 = k12;
+  for (int q = 0; q < 2; ++q) {
+    const int mm = j + 32 * q;
+    lo[q] = melr[2 * mm];
+    hi[q] = melr[2 * mm + 1];
 #pragma unroll
-    for (int k2 = 0; k2 <= 10; ++k2) {
-      const int k = k1 + 16 * k2;
-      if (k < FE_K) {
-        float xr = 0.f, xi = 0.f;
+    for (int t = 0; t < MW; ++t) wts[q][t] = lo[q] + t <= hi[q] ? fb[(lo[q] + t) * FE_M + mm] : 0.f;
+  }
+  __syncthreads();                                      // the twiddle table, once
+  // W5^q = W320^(64 q) for q = 1, 2 (the only two the 5-point DFT needs, with conjugates)
+  const float c1 = tc[64], s1 = ts[64], c2 = tc[128], s2 = ts[128];
+  // stage-1 twiddles W160^(j k1) = W320^(2 j k1), k1 = 1..4
+  float t1c[4], t1s[4];
 #pragma unroll
-        for (int n2 = 0; n2 < 20; ++n2) {
-          const int j = 16 * ((n2 * k2) % 20);    // W20^(n2 k2) = W320^(16 (n2 k2 mod 20))
-          const float c = tc[j], sn = ts[j];
-          xr = fmaf(ar[n2], c, fmaf(ai[n2], sn, xr));
-          xi = fmaf(ai[n2], c, fmaf(-ar[n2], sn, xi));
+  for (int k1 = 1; k1 < 5; ++k1) { t1c[k1 - 1] = tc[2 * j * k1]; t1s[k1 - 1] = ts[2 * j * k1]; }
+  // radix-2 steps over spans 16, 8, 4, 2: the lower lane of a pair keeps x + partner, the
+  // upper one (partner - x) W_{2s}^(j mod s) = (partner - x) W320^((j mod s) 160 / s)
+  float bs[4], bc[4], bn[4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    const int sp = 16 >> st;
+    const bool up = (j & sp) != 0;
+    const int t = up ? (j & (sp - 1)) * (160 / sp) : 0;
+    bs[st] = up ? -1.f : 1.f;
+    bc[st] = tc[t];
+    bn[st] = ts[t];
+  }
+  const int br = (int)(__builtin_bitreverse32((uint32_t)j) >> 27);   // k2 held after the steps
+
+  const int n_pairs = (T_tot + 1) >> 1;
+  for (int pr = blockIdx.x * FE_WAVES + wave; pr < n_pairs; pr += gridDim.x * FE_WAVES) {
+    const int g = 2 * pr + h;                           // this half-wave's frame
+    float2 z[5];
+    if (g < T_tot) {
+      const int b = m.rowT[g];
+      const float* x = pcm + (long)b * stride + 160L * (g - m.cuT[b]) + 2 * j;
+#pragma unroll
+      for (int n1 = 0; n1 < 5; ++n1)
+        z[n1] = make_float2(x[64 * n1] * wv[n1][0], x[64 * n1 + 1] * wv[n1][1]);
+    } else {
+#pragma unroll
+      for (int n1 = 0; n1 < 5; ++n1) z[n1] = make_float2(0.f, 0.f);
+    }
+    // 5-point DFT over n1: y[k] and y[5 - k] share R = sum z[n1] cos, I = sum z[n1] sin
+    float2 y[5];
+    y[0] = make_float2(z[0].x + z[1].x + z[2].x + z[3].x + z[4].x,
+                       z[0].y + z[1].y + z[2].y + z[3].y + z[4].y);
+    {
+      // k = 1: cos / sin of 2 pi n1 / 5 for n1 = 1..4 are (c1, s1), (c2, s2), (c2, -s2), (c1, -s1)
+      const float Rx = fmaf(c1, z[1].x + z[4].x, c2 * (z[2].x + z[3].x));
+      const float Ry = fmaf(c1, z[1].y + z[4].y, c2 * (z[2].y + z[3].y));
+      const float Ix = fmaf(s1, z[1].x - z[4].x, s2 * (z[2].x - z[3].x));
+      const float Iy = fmaf(s1, z[1].y - z[4].y, s2 * (z[2].y - z[3].y));
+      y[1] = make_float2(z[0].x + Rx + Iy, z[0].y + Ry - Ix);     // z0 + R - i I
+      y[4] = make_float2(z[0].x + Rx - Iy, z[0].y + Ry + Ix);     // z0 + R + i I
+    }
+    {
+      // k = 2: angles 4 pi n1 / 5 -> (c2, s2), (c1, -s1), (c1, s1), (c2, -s2)
+      const float Rx = fmaf(c2, z[1].x + z[4].x, c1 * (z[2].x + z[3].x));
+      const float Ry = fmaf(c2, z[1].y + z[4].y, c1 * (z[2].y + z[3].y));
+      const float Ix = fmaf(s2, z[1].x - z[4].x, -s1 * (z[2].x - z[3].x));
+      const float Iy = fmaf(s2, z[1].y - z[4].y, -s1 * (z[2].y - z[3].y));
+      y[2] = make_float2(z[0].x + Rx + Iy, z[0].y + Ry - Ix);
+      y[3] = make_float2(z[0].x + Rx - Iy, z[0].y + Ry + Ix);
+    }
+#pragma unroll
+    for (int k1 = 1; k1 < 5; ++k1) y[k1] = cmul(y[k1], t1c[k1 - 1], t1s[k1 - 1]);
+    // radix-2 steps across the frame's 32 lanes
+#pragma unroll
+    for (int st = 0; st < 5; ++st) {
+      const int sp = 16 >> st;
+#pragma unroll
+      for (int k1 = 0; k1 < 5; ++k1) {
+        const float px = __shfl_xor(y[k1].x, sp, 64), py = __shfl_xor(y[k1].y, sp, 64);
+        if (st < 4) {
+          const float2 d = make_float2(fmaf(bs[st], y[k1].x, px), fmaf(bs[st], y[k1].y, py));
+          y[k1] = cmul(d, bc[st], bn[st]);
+        } else {
+          const float sg = (j & 1) ? -1.f : 1.f;
+          y[k1] = make_float2(fmaf(sg, y[k1].x, px), fmaf(sg, y[k1].y, py));
         }
-        P[f][k] = xr * xr + xi * xi;
       }
     }
-  }
-  __syncthreads();
-
-  // mel projection + log clip: thread (f, m), the filter's weights already in registers
-  // (a wider filter continues from the table), summed in ascending bin order
-  for (int e = tid; e < FE_FT * FE_M; e += 256) {
-    const int f = e >> 6;
-    float acc = 0.f;
 #pragma unroll
-    for (int j = 0; j < MW; ++j)
-      if (lo + j <= hi) acc = fmaf(wts[j], P[f][lo + j], acc);
-    for (int k = lo + MW; k <= hi; ++k) acc = fmaf(fb[k * FE_M + mm], P[f][k], acc);
-    const int g = f0 + f;
-    if (g < T_tot) mel[(long)g * FE_M + mm] = logf(fminf(fmaxf(acc, 1e-9f), 1e9f));
+    for (int k1 = 0; k1 < 5; ++k1) zs[wave][h][k1 + 5 * br] = y[k1];
+    wave_lds_sync();
+    // even / odd separation and power, bins k = j + 32 q; k = 160 from Z[0] (lane 0)
+#pragma unroll
+    for (int q = 0; q < 5; ++q) {
+      const int k = j + 32 * q;
+      const float2 a = zs[wave][h][k];
+      float p;
+      if (k == 0) {
+        const float x0 = a.x + a.y, x160 = a.x - a.y;
+        p = x0 * x0;
+        ps[wave][h][160] = x160 * x160;
+      } else {
+        const float2 c = zs[wave][h][160 - k];
+        const float Er = 0.5f * (a.x + c.x), Ei = 0.5f * (a.y - c.y);
+        const float2 o = cmul(make_float2(0.5f * (a.y + c.y), -0.5f * (a.x - c.x)), tc[k], ts[k]);
+        const float Xr = Er + o.x, Xi = Ei + o.y;
+        p = fmaf(Xr, Xr, Xi * Xi);
+      }
+      ps[wave][h][k] = p;
+    }
+    wave_lds_sync();
+    // mel projection (ascending bins of each filter's range) and log clip
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      float acc = 0.f;
+#pragma unroll
+      for (int t = 0; t < MW; ++t)
+        if (lo[q] + t <= hi[q]) acc = fmaf(wts[q][t], ps[wave][h][lo[q] + t], acc);
+      for (int k = lo[q] + MW; k <= hi[q]; ++k) acc = fmaf(fb[k * FE_M + j + 32 * q], ps[wave][h][k], acc);
+      if (g < T_tot) mel[(long)g * FE_M + j + 32 * q] = logf(fminf(fmaxf(acc, 1e-9f), 1e9f));
+    }
+    wave_lds_sync();                                    // spectra read before the next pair
   }
 }
 
@@ -203,8 +230,11 @@ hipError_t launch_frontend(const float* pcm, int stride, const float* window, co
                            hipStream_t s) {
   if (T_tot <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_frontend_prep, dim3(1), dim3(FE_N), 0, s, fb, tw, melr);
-  hipLaunchKernelGGL(k_frontend, dim3((T_tot + FE_FT - 1) / FE_FT), dim3(256), 0, s, pcm, stride,
-                     window, fb, tw, melr, m, T_tot, mel);
+  // waves walk frame pairs: one pass over all pairs with four 4-wave blocks per CU
+  const int pairs = (T_tot + 1) / 2;
+  const int blocks = std::min((pairs + FE_WAVES - 1) / FE_WAVES, 1024);
+  hipLaunchKernelGGL(k_frontend, dim3(blocks), dim3(64 * FE_WAVES), 0, s, pcm, stride, window, fb,
+                     tw, melr, m, T_tot, mel);
   return hipGetLastError();
 }
 
