@@ -82,7 +82,8 @@ __global__ void __launch_bounds__(64 * FE_WAVES) k_frontend(const float* __restr
                                                           const float* __restrict__ fb,
                                                           const float* __restrict__ tw,
                                                           const int* __restrict__ melr, MetaDev m,
-                                                          int T_tot, float* __restrict__ mel) {
+                                                          int T_tot, float* __restrict__ mel,
+                                                          void* __restrict__ mel_t, int mel_dt) {
   __shared__ float tc[FE_N], ts[FE_N];                  // W320^t = tc[t] - i ts[t]
   __shared__ float2 zs[FE_WAVES][2][160];               // Z of the wave's two frames
   __shared__ float ps[FE_WAVES][2][FE_K + 3];           // their power spectra
@@ -219,22 +220,30 @@ __global__ void __launch_bounds__(64 * FE_WAVES) k_frontend(const float* __restr
       for (int t = 0; t < MW; ++t)
         if (lo[q] + t <= hi[q]) acc = fmaf(wts[q][t], ps[wave][h][lo[q] + t], acc);
       for (int k = lo[q] + MW; k <= hi[q]; ++k) acc = fmaf(fb[k * FE_M + j + 32 * q], ps[wave][h][k], acc);
-      if (g < T_tot) mel[(long)g * FE_M + j + 32 * q] = logf(fminf(fmaxf(acc, 1e-9f), 1e9f));
+      if (g < T_tot) {
+        const long o = (long)g * FE_M + j + 32 * q;
+        const float v = logf(fminf(fmaxf(acc, 1e-9f), 1e9f));
+        mel[o] = v;
+        if (mel_dt == DT_F16) ((f16*)mel_t)[o] = (f16)v;          // round to nearest even
+        else if (mel_dt == DT_BF16) ((bf16*)mel_t)[o] = (bf16)v;
+      }
     }
     wave_lds_sync();                                    // spectra read before the next pair
   }
 }
 
 hipError_t launch_frontend(const float* pcm, int stride, const float* window, const float* fb,
-                           const MetaDev& m, int T_tot, float* mel, float* tw, int* melr,
-                           hipStream_t s) {
+                           const MetaDev& m, int T_tot, float* mel, void* mel_t, DType mel_dt,
+                           float* tw, int* melr, hipStream_t s) {
+  if (mel_dt != DT_F32 && mel_dt != DT_F16 && mel_dt != DT_BF16) return hipErrorInvalidValue;
+  if (mel_dt != DT_F32 && !mel_t) return hipErrorInvalidValue;
   if (T_tot <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_frontend_prep, dim3(1), dim3(FE_N), 0, s, fb, tw, melr);
   // waves walk frame pairs: one pass over all pairs with four 4-wave blocks per CU
   const int pairs = (T_tot + 1) / 2;
   const int blocks = std::min((pairs + FE_WAVES - 1) / FE_WAVES, 1024);
   hipLaunchKernelGGL(k_frontend, dim3(blocks), dim3(64 * FE_WAVES), 0, s, pcm, stride, window, fb,
-                     tw, melr, m, T_tot, mel);
+                     tw, melr, m, T_tot, mel, mel_t, (int)mel_dt);
   return hipGetLastError();
 }
 

@@ -664,7 +664,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, OCC) k_gemm_p(GemmParams p) {
               for (int j = 0; j < 4; ++j) {
                 const float x = acc[ni][mi][4 * g + j] + bv[ni][g][j];
                 v[j] = (EP == E_SILU) ? siluf_(x) : (EP == E_RESID) ? p.alpha * x
-                       : (EP == E_RELU_F32) ? fmaxf(x, 0.f) : x;
+                       : (EP == E_RELU_F32 || EP == E_RELU) ? fmaxf(x, 0.f) : x;
               }
               const int cs = wn * WTN + ni * 32 + 8 * g + h4;
               if constexpr (F32OUT) *(f32x4*)(srow + cs * 4) = v;
@@ -881,7 +881,7 @@ static hipError_t run_dl(AMode am, Epi ep, const GemmParams& p, hipStream_t s) {
     return hipGetLastError();                                                                      \
   }
   GG_DL(A_PLAIN, E_STORE) GG_DL(A_PLAIN, E_SILU) GG_DL(A_PLAIN, E_RESID) GG_DL(A_PLAIN, E_F32)
-  GG_DL(A_DUAL, E_STORE) GG_DL(A_CONV, E_RELU_F32)
+  GG_DL(A_DUAL, E_STORE) GG_DL(A_CONV, E_RELU_F32) GG_DL(A_CONV, E_RELU)
   if constexpr (GLU_OK) { GG_DL(A_PLAIN, E_GLU) }
 #undef GG_DL
   return hipErrorInvalidValue;
@@ -974,7 +974,7 @@ static hipError_t run_dl_shape(AMode am, Epi ep, const GemmParams& p, hipStream_
 
 static bool direct_path(DType dt, int qbits, AMode am, Epi ep, const GemmParams& p) {
   if (dt == DT_F32 || qbits != 0 || p.K % 64 != 0) return false;
-  if (am == A_CONV) return ep == E_RELU_F32 && p.cin % 64 == 0 && p.K == 5 * p.cin;
+  if (am == A_CONV) return (ep == E_RELU_F32 || ep == E_RELU) && p.cin % 64 == 0 && p.K == 5 * p.cin;
   if (am == A_DUAL) return ep == E_STORE;
   return am == A_PLAIN &&
          (ep == E_STORE || ep == E_SILU || ep == E_RESID || ep == E_GLU || ep == E_F32);

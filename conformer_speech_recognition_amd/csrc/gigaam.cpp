@@ -539,7 +539,7 @@ namespace {
 
 struct Ws {
   size_t cuT, cuS, cuU, cuQ, rowT, rowS, rowU, tileQ, cuQ2, tileQ2, tileG;
-  size_t mel, h1, x, y, r, qkv, ao, hid, cos_t, sin_t, logits, fids, part, fe;
+  size_t mel, melh, h1, x, y, r, qkv, ao, hid, cos_t, sin_t, logits, fids, part, fe;
   size_t total;
 };
 
@@ -556,6 +556,7 @@ Ws plan(const gigaam_config& c, int B, int T_tot, int S_tot, int U_tot, int nQ, 
   w.tileQ2 = take((size_t)nQ * 4);            // nQ2 <= nQ
   w.tileG = take((size_t)nQ * 16);
   w.mel = take((size_t)T_tot * 64 * 4);
+  w.melh = take(es == 2 ? (size_t)T_tot * 64 * 2 : 0);     // 16-bit copy: the conv1 operand
   w.h1 = take((size_t)S_tot * d * es);
   w.x = take((size_t)U_tot * d * 4);
   w.y = take((size_t)U_tot * d * es);
@@ -723,14 +724,21 @@ int run(gigaam_model* m, const float* pcm, const int32_t* lengths, int32_t B, in
   // ---- geometry to the device
   LAUNCH("meta", launch_meta(meta, md, T_tot, S_tot, U_tot, s));
   // ---- frontend (log-mel)
+  // activations of the 16-bit models are bf16 for the bf16 dtype, fp16 otherwise
+  const DType act = dt == DT_F32 ? DT_F32 : dt == DT_BF16 ? DT_BF16 : DT_F16;
   LAUNCH("frontend", launch_frontend(pcm, stride, m->window, m->fb, md, T_tot, mel,
+                                     act == DT_F32 ? nullptr : (void*)(W + w.melh), act,
                                      (float*)(W + w.fe), (int*)(W + w.fe + 640 * 4), s));
   if (stage == GIGAAM_STAGE_MEL) return copy_out(mel, (size_t)T_tot * 64);
   // ---- subsampling: two implicit-GEMM Conv1d k5 s2 p2 + ReLU
   {
-    GemmParams g1 = gemm(S_tot, d, 5 * 64, mel, 0, P + L.conv1_w, nullptr, (const float*)(P + L.conv1_b), h1, d);
+    // 16-bit models read the mel copy in their own type (the same rounding the fp32
+    // source gets while staging), which the pipelined kernel streams
+    const bool mel16 = act != DT_F32;
+    GemmParams g1 = gemm(S_tot, d, 5 * 64, mel16 ? (const void*)(W + w.melh) : (const void*)mel, 0,
+                         P + L.conv1_w, nullptr, (const float*)(P + L.conv1_b), h1, d);
     g1.rowclip = md.rowS; g1.cu_in = md.cuT; g1.cu_out = md.cuS; g1.cin = 64;
-    if ((rc = G("gemm.conv1", A_CONV_F32, E_RELU, false, g1))) return rc;
+    if ((rc = G("gemm.conv1", mel16 ? A_CONV : A_CONV_F32, E_RELU, false, g1))) return rc;
     GemmParams g2 = gemm(U_tot, d, 5 * d, h1, 0, P + L.conv2_w, nullptr, (const float*)(P + L.conv2_b), x, d);
     g2.rowclip = md.rowU; g2.cu_in = md.cuS; g2.cu_out = md.cuU; g2.cin = d;
     if ((rc = G("gemm.conv2", A_CONV, E_RELU_F32, false, g2))) return rc;

@@ -84,10 +84,12 @@ hipError_t launch_meta(const MetaArgs& a, const MetaDev& m, int T_tot, int S_tot
 hipError_t launch_copy_f32(float* dst, const float* src, long n, hipStream_t s);
 
 // ---- frontend -----------------------------------------------------------------------
-// tw: 640 floats and melr: 128 ints of scratch for the per-launch tables
+// tw: 640 floats and melr: 128 ints of scratch for the per-launch tables; mel_t (or
+// nullptr): a second copy of the log-mel rows rounded to mel_dt (DT_F16 or DT_BF16), the
+// operand of the first subsampling conv on 16-bit models
 hipError_t launch_frontend(const float* pcm, int stride, const float* window, const float* fb,
-                           const MetaDev& m, int T_tot, float* mel, float* tw, int* melr,
-                           hipStream_t s);
+                           const MetaDev& m, int T_tot, float* mel, void* mel_t, DType mel_dt,
+                           float* tw, int* melr, hipStream_t s);
 hipError_t launch_default_frontend(float* window, float* fb, hipStream_t s);
 
 // ---- norms / rotary -----------------------------------------------------------------
