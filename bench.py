@@ -35,15 +35,17 @@ PEAK_HBM_GBS = 8000.0
 # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch) on this
 # bench, scaled by what the counters read for a plain copy of known size; valid only while the
 # kernel's source is the one the counters were taken on (sha256 prefix)
-GEMM_SRC = ("conformer_speech_recognition_amd/csrc/gemm.hip", "105ada521bf71138")
+GEMM_SRC = ("conformer_speech_recognition_amd/csrc/gemm.hip", "7350c3016b1823de")
 ATTN_SRC = ("conformer_speech_recognition_amd/csrc/attention.hip", "d57238f4d5cf971f")
-TRAFFIC_KIB = {("batch32", "gemm.ffn_up"): (GEMM_SRC, 41514, 49242),
-               ("batch32", "gemm.ffn_down"): (GEMM_SRC, 83897, 24621),
-               ("batch32", "gemm.qkv"): (GEMM_SRC, 43130, 36932),
-               ("batch32", "gemm.pw1_glu"): (GEMM_SRC, 21265, 12310),
+TRAFFIC_KIB = {("batch32", "gemm.ffn_up"): (GEMM_SRC, 41511, 49242),
+               ("batch32", "gemm.ffn_down"): (GEMM_SRC, 83898, 24621),
+               ("batch32", "gemm.qkv"): (GEMM_SRC, 43963, 36932),
+               ("batch32", "gemm.pw1_glu"): (GEMM_SRC, 21270, 12310),
                ("batch32", "gemm.out_proj"): (GEMM_SRC, 25743, 24621),
                ("batch32", "gemm.pw2"): (GEMM_SRC, 25743, 24621),
-               ("batch32", "attention"): (ATTN_SRC, 28733, 14387)}
+               ("batch32", "gemm.conv2"): (GEMM_SRC, 89304, 24621),
+               ("batch32", "gemm.conv1"): (GEMM_SRC, 4534, 24597),
+               ("batch32", "attention"): (ATTN_SRC, 28768, 14400)}
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 
 
@@ -106,7 +108,8 @@ def role_bytes(cfg, lens):
     U = sum(x[2] for x in fr)
     B, Umax = len(lens), max(x[2] for x in fr)
     return {
-        "frontend": int(sum(int(n) for n in lens)) * 4 + T * 64 * 4,
+        # samples in, fp32 log-mel rows out, plus their 16-bit copy on 16-bit models
+        "frontend": int(sum(int(n) for n in lens)) * 4 + T * 64 * (4 + (es if es == 2 else 0)),
         "layernorm": U * d * (4 + es),
         "layernorm_rope": U * d * (4 + 2 * es),
         "layernorm_two": U * d * (8 + es),
