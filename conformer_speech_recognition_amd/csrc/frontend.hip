@@ -22,6 +22,8 @@
 // launch, the twiddle table and each mel filter's range of nonzero weights; the
 // projection sums over that range only, in the same ascending order as the full sum, so
 // the result is the same (the skipped terms are exact zeros).
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace gg {
@@ -73,6 +75,27 @@ __global__ void __launch_bounds__(FE_N) k_frontend_prep(const float* __restrict_
 
 constexpr int FE_WAVES = 4;   // waves per block, each with its own LDS slice
 
+// the value of lane ^ SP (SP = 16, 8, 4, 2, 1: inside the lane's 32-lane half) on vector
+// lane operations instead of the LDS crossbar a shuffle takes: a row swap for 16 (whichever
+// of the two results is not the lane's own value; equal values make either one right), a row
+// rotation by 8, a half-row mirror then a quad reversal for 4, quad permutations for 2 and 1
+template <int SP> __device__ __forceinline__ float lane_xor(float v) {
+  if constexpr (SP == 16) {
+    uint32_t a, b;
+    pair_x16(fbits(v), a, b);
+    return ffrom(a == fbits(v) ? b : a);
+  } else if constexpr (SP == 8) {
+    return dpp_f<kDppRor8>(v);
+  } else if constexpr (SP == 4) {
+    return dpp_f<0x1B>(dpp_f<0x141>(v));
+  } else if constexpr (SP == 2) {
+    return dpp_f<kDppXor2>(v);
+  } else {
+    static_assert(SP == 1, "span");
+    return dpp_f<kDppXor1>(v);
+  }
+}
+
 __device__ __forceinline__ float2 cmul(float2 a, float c, float sn) {   // a (c - i sn)
   return make_float2(fmaf(a.x, c, a.y * sn), fmaf(a.y, c, -a.x * sn));
 }
@@ -85,7 +108,7 @@ __global__ void __launch_bounds__(64 * FE_WAVES) k_frontend(const float* __restr
                                                           int T_tot, float* __restrict__ mel,
                                                           void* __restrict__ mel_t, int mel_dt) {
   __shared__ float tc[FE_N], ts[FE_N];                  // W320^t = tc[t] - i ts[t]
-  __shared__ float2 zs[FE_WAVES][2][160];               // Z of the wave's two frames
+  __shared__ float2 zs[FE_WAVES][2][164];               // Z of the wave's two frames (padded)
   __shared__ float ps[FE_WAVES][2][FE_K + 3];           // their power spectra
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -174,13 +197,12 @@ __global__ void __launch_bounds__(64 * FE_WAVES) k_frontend(const float* __restr
 #pragma unroll
     for (int k1 = 1; k1 < 5; ++k1) y[k1] = cmul(y[k1], t1c[k1 - 1], t1s[k1 - 1]);
     // radix-2 steps across the frame's 32 lanes
-#pragma unroll
-    for (int st = 0; st < 5; ++st) {
-      const int sp = 16 >> st;
+    auto step = [&](auto spc, int st) {
+      constexpr int SP = decltype(spc)::value;
 #pragma unroll
       for (int k1 = 0; k1 < 5; ++k1) {
-        const float px = __shfl_xor(y[k1].x, sp, 64), py = __shfl_xor(y[k1].y, sp, 64);
-        if (st < 4) {
+        const float px = lane_xor<SP>(y[k1].x), py = lane_xor<SP>(y[k1].y);
+        if constexpr (SP > 1) {
           const float2 d = make_float2(fmaf(bs[st], y[k1].x, px), fmaf(bs[st], y[k1].y, py));
           y[k1] = cmul(d, bc[st], bn[st]);
         } else {
@@ -188,7 +210,12 @@ __global__ void __launch_bounds__(64 * FE_WAVES) k_frontend(const float* __restr
           y[k1] = make_float2(fmaf(sg, y[k1].x, px), fmaf(sg, y[k1].y, py));
         }
       }
-    }
+    };
+    step(std::integral_constant<int, 16>{}, 0);
+    step(std::integral_constant<int, 8>{}, 1);
+    step(std::integral_constant<int, 4>{}, 2);
+    step(std::integral_constant<int, 2>{}, 3);
+    step(std::integral_constant<int, 1>{}, 4);
 #pragma unroll
     for (int k1 = 0; k1 < 5; ++k1) zs[wave][h][k1 + 5 * br] = y[k1];
     wave_lds_sync();
