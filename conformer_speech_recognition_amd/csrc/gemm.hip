@@ -483,6 +483,8 @@ __global__ void __launch_bounds__(64 * WGM * WGN, OCC) k_gemm_p(GemmParams p) {
 #pragma unroll
         for (int j = 0; j < 5; ++j)
           if (r0 + j >= lo && r0 + j < hi) tapok |= 1ull << (5 * i + j);
+        // (r0 is two rows before the clip for its first frame: such a row's taps 0 and 1
+        // take the zero chunk, so this address is only dereferenced from tap 2 on)
         src[i] = Ab + (r0 * p.cin + koff + lc * 8) * (long)sizeof(T);
       } else {
         src[i] = Ab + ((long)gm * p.lda + koff + lc * 8) * sizeof(T);
