@@ -41,6 +41,7 @@ struct MetaDev {           // device view of the meta region
   int* rowT; int* rowS; int* rowU; int* tileQ;
   int* cuQ2; int* tileQ2;
   int* tileG;              // 4 ints per 64-frame tile: first row, clip length, first frame, clip
+  int* posU;               // position of each encoder row inside its clip, or nullptr
 };
 
 template <typename T> struct TypeOf;

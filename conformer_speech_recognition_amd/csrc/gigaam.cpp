@@ -538,7 +538,7 @@ extern "C" void gigaam_destroy(gigaam_model* m) { delete m; }
 namespace {
 
 struct Ws {
-  size_t cuT, cuS, cuU, cuQ, rowT, rowS, rowU, tileQ, cuQ2, tileQ2, tileG;
+  size_t cuT, cuS, cuU, cuQ, rowT, rowS, rowU, posU, tileQ, cuQ2, tileQ2, tileG;
   size_t mel, melh, h1, x, y, r, qkv, ao, hid, cos_t, sin_t, logits, fids, part, fe;
   size_t total;
 };
@@ -551,6 +551,7 @@ Ws plan(const gigaam_config& c, int B, int T_tot, int S_tot, int U_tot, int nQ, 
   const size_t hidw = (size_t)c.d_ff > 2 * d ? (size_t)c.d_ff : 2 * d;
   w.cuT = take((B + 1) * 4); w.cuS = take((B + 1) * 4); w.cuU = take((B + 1) * 4); w.cuQ = take((B + 1) * 4);
   w.rowT = take((size_t)T_tot * 4); w.rowS = take((size_t)S_tot * 4); w.rowU = take((size_t)U_tot * 4);
+  w.posU = take((size_t)U_tot * 4);
   w.tileQ = take((size_t)nQ * 4);
   w.cuQ2 = take((B + 1) * 4);
   w.tileQ2 = take((size_t)nQ * 4);            // nQ2 <= nQ
@@ -675,7 +676,7 @@ int run(gigaam_model* m, const float* pcm, const int32_t* lengths, int32_t B, in
   char* W = (char*)ws;
   MetaDev md{(int*)(W + w.cuT), (int*)(W + w.cuS), (int*)(W + w.cuU), (int*)(W + w.cuQ),
              (int*)(W + w.rowT), (int*)(W + w.rowS), (int*)(W + w.rowU), (int*)(W + w.tileQ),
-             (int*)(W + w.cuQ2), (int*)(W + w.tileQ2), (int*)(W + w.tileG)};
+             (int*)(W + w.cuQ2), (int*)(W + w.tileQ2), (int*)(W + w.tileG), (int*)(W + w.posU)};
   float* mel = (float*)(W + w.mel);
   char* h1 = W + w.h1;
   float* x = (float*)(W + w.x);
@@ -750,7 +751,7 @@ int run(gigaam_model* m, const float* pcm, const int32_t* lengths, int32_t B, in
   LnParams ln;
   std::memset(&ln, 0, sizeof ln);
   ln.rows = U_tot; ln.d = d; ln.x = x; ln.eps = c.ln_eps;
-  ln.cos_t = cos_t; ln.sin_t = sin_t; ln.rowclip = md.rowU; ln.cu = md.cuU;
+  ln.cos_t = cos_t; ln.sin_t = sin_t; ln.rowpos = md.posU;
   // ks / rb / ra: a preceding residual GEMM's deferred split-K slices, its bias and scale
   auto LN = [&](LnMode mode, size_t g1, size_t b1, const float* g2, const float* b2, void* yo,
                 void* ro, int ks = 0, const float* rb = nullptr, float ra = 1.f) -> int {

@@ -102,10 +102,11 @@ struct LnParams {
   void* y;                         // T out
   void* r;                         // LN_ROPE: rotated copy (T)
   const float* cos_t; const float* sin_t;  // [U_max][d_k/2]
-  const int* rowclip; const int* cu;       // encoder-space clip map (for positions)
+  const int* rowpos;                       // LN_ROPE: position of each row inside its clip
   float eps;
   // a residual GEMM's deferred split-K sum, added to x first: x += ralpha * (sum of the rks
-  // slices of rpart [rks][rows][d] in slice order + rbias); rks = 0: none
+  // slices of rpart [rks][rows][d] in slice order + rbias); rks = 0: none, else 1..4 with
+  // rpart and rbias both given
   const float* rpart; const float* rbias; int rks; float ralpha;
 };
 hipError_t launch_layernorm(DType dt, LnMode mode, const LnParams& p, hipStream_t s);

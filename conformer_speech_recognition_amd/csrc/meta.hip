@@ -65,7 +65,11 @@ __global__ void __launch_bounds__(256) k_meta(MetaArgs a, MetaDev m, int T_tot, 
   const int stride = gridDim.x * blockDim.x;
   for (int r = gid; r < T_tot; r += stride) m.rowT[r] = find_clip(a.cuT, a.B, r);
   for (int r = gid; r < S_tot; r += stride) m.rowS[r] = find_clip(a.cuS, a.B, r);
-  for (int r = gid; r < U_tot; r += stride) m.rowU[r] = find_clip(a.cuU, a.B, r);
+  for (int r = gid; r < U_tot; r += stride) {
+    const int b = find_clip(a.cuU, a.B, r);
+    m.rowU[r] = b;
+    if (m.posU) m.posU[r] = r - a.cuU[b];
+  }
   for (int r = gid; r < nQ; r += stride) {
     const int b = find_clip(cuQ, a.B, r);
     m.tileQ[r] = b;

@@ -29,9 +29,23 @@ template <> __device__ __forceinline__ void store4<bf16>(bf16* dst, float a, flo
   *(bf16x4*)dst = bf16x4{(bf16)a, (bf16)b, (bf16)c, (bf16)d};
 }
 
+// gamma and beta of this lane's features, loaded with the row (the deferred-residual
+// variants store x before normalising, and loads written after those stores waited for them)
+template <int NI> struct LnAffine { f32x4 g[NI], b[NI]; };
+template <int NI>
+__device__ __forceinline__ LnAffine<NI> ln_affine(const float* g, const float* b, int lane) {
+  LnAffine<NI> a;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    a.g[i] = *(const f32x4*)(g + 256 * i + 4 * lane);
+    a.b[i] = *(const f32x4*)(b + 256 * i + 4 * lane);
+  }
+  return a;
+}
+
 // v[4 i + q] = feature 256 i + 4 lane + q
 template <int NI>
-__device__ __forceinline__ void ln_row(float (&v)[4 * NI], const float* g, const float* b, int lane,
+__device__ __forceinline__ void ln_row(float (&v)[4 * NI], const LnAffine<NI>& ab, int lane,
                                        float eps) {
   constexpr int D = NI * 256;
   float s = 0.f;
@@ -46,22 +60,20 @@ __device__ __forceinline__ void ln_row(float (&v)[4 * NI], const float* g, const
   }
   const float rstd = 1.0f / sqrtf(wave_sum(ss) * (1.0f / D) + eps);
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const f32x4 gg4 = *(const f32x4*)(g + 256 * i + 4 * lane);
-    const f32x4 bb4 = *(const f32x4*)(b + 256 * i + 4 * lane);
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) v[4 * i + q] = v[4 * i + q] * rstd * gg4[q] + bb4[q];
-  }
+    for (int q = 0; q < 4; ++q) v[4 * i + q] = v[4 * i + q] * rstd * ab.g[i][q] + ab.b[i][q];
 }
 
 // normalise one row held in v (the row's loads already issued) and write its outputs
 template <typename T, int NI, int MODE>
 __device__ __forceinline__ void ln_finish(const LnParams& p, float (&v)[4 * NI], int row, int lane,
-                                          float* sr, float cv, float sv) {
+                                          float* sr, float cv, float sv, const LnAffine<NI>& a1,
+                                          const LnAffine<NI>& a2) {
   constexpr int D = NI * 256;
   constexpr int DK = D / 16, HALF = DK / 2;      // 16 heads
   float* xr = p.x + (long)row * D + 4 * lane;
-  ln_row<NI>(v, p.g1, p.b1, lane, p.eps);
+  ln_row<NI>(v, a1, lane, p.eps);
   T* yr = (T*)p.y + (long)row * D + 4 * lane;
   if constexpr (MODE == LN_TWO) {
 #pragma unroll
@@ -74,7 +86,7 @@ __device__ __forceinline__ void ln_finish(const LnParams& p, float (&v)[4 * NI],
           store4<T>(yr + 256 * i, v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
       return;
     }
-    ln_row<NI>(v, p.g2, p.b2, lane, p.eps);
+    ln_row<NI>(v, a2, lane, p.eps);
   }
 #pragma unroll
   for (int i = 0; i < NI; ++i) store4<T>(yr + 256 * i, v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
@@ -115,9 +127,12 @@ __device__ __forceinline__ void ln_finish(const LnParams& p, float (&v)[4 * NI],
 }
 
 // One wave per RPW consecutive rows: every row's loads (and, for RoPE, its cos / sin
-// entries, a chain of three dependent loads) are issued before the first row's statistics,
-// so a wave keeps RPW rows of reads in flight and the grid fits the chip in one round.
-template <typename T, int NI, int MODE, int RPW, bool RES>
+// entries, two dependent loads: the frame's position, then the table) are issued before the
+// first row's statistics, so a wave keeps RPW rows of reads in flight and the grid fits the
+// chip in one round. RKS > 0: the preceding residual GEMM left its K sum in RKS slices,
+// which are added here (all slice reads issued together: a loop over a run-time slice count
+// made the compiler wait for each one, one round trip to memory per slice and feature group).
+template <typename T, int NI, int MODE, int RPW, int RKS>
 __global__ void __launch_bounds__(256) k_ln(LnParams p) {
   constexpr int D = NI * 256;
   constexpr int DK = D / 16, HALF = DK / 2;
@@ -138,25 +153,45 @@ __global__ void __launch_bounds__(256) k_ln(LnParams p) {
       for (int j = 0; j < 4; ++j) v[r][4 * i + j] = q[j];
     }
   }
-  if constexpr (RES) {
-    // the preceding residual GEMM's split K sum: x += ralpha * (slices in order + bias), the
-    // reduce step of that GEMM done here, and x written back unless the LayerNorm overwrites it
+  const LnAffine<NI> a1 = ln_affine<NI>(p.g1, p.b1, lane);
+  // (pointers selected, not the loads: a load under a branch is waited for at its join)
+  const LnAffine<NI> a2 = MODE == LN_TWO ? ln_affine<NI>(p.g2 ? p.g2 : p.g1, p.g2 ? p.b2 : p.b1, lane) : a1;
+  if constexpr (RKS > 0) {
+    // x += ralpha * (slices in order + bias): the reduce step of that GEMM done here, and x
+    // written back unless the LayerNorm overwrites it
     const long slice = (long)p.rows * D;
+    f32x4 part[RPW][NI][RKS];
+    f32x4 rb[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) rb[i] = *(const f32x4*)(p.rbias + 256 * i + 4 * lane);
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
-      if (row0 + r >= p.rows) continue;
-      const long off = (long)(row0 + r) * D + 4 * lane;
+      const int row = row0 + r < p.rows ? row0 + r : p.rows - 1;
+      const long off = (long)row * D + 4 * lane;
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int k = 0; k < RKS; ++k) part[r][i][k] = *(const f32x4*)(p.rpart + off + 256 * i + k * slice);
+    }
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        f32x4 a = *(const f32x4*)(p.rpart + off + 256 * i);
-        for (int k = 1; k < p.rks; ++k) a += *(const f32x4*)(p.rpart + off + 256 * i + k * slice);
-        const f32x4 b = p.rbias ? *(const f32x4*)(p.rbias + 256 * i + 4 * lane) : f32x4{0.f, 0.f, 0.f, 0.f};
-        const f32x4 sum = a + b;
+        f32x4 a = part[r][i][0];
+#pragma unroll
+        for (int k = 1; k < RKS; ++k) a += part[r][i][k];
+        const f32x4 sum = a + rb[i];
 #pragma unroll
         for (int j = 0; j < 4; ++j) v[r][4 * i + j] = v[r][4 * i + j] + p.ralpha * sum[j];
-        if constexpr (MODE != LN_TWO)
-          *(f32x4*)(p.x + off + 256 * i) =
-              f32x4{v[r][4 * i], v[r][4 * i + 1], v[r][4 * i + 2], v[r][4 * i + 3]};
+      }
+    if constexpr (MODE != LN_TWO) {
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        if (row0 + r >= p.rows) continue;
+        const long off = (long)(row0 + r) * D + 4 * lane;
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+          *(f32x4*)(p.x + off + 256 * i) = f32x4{v[r][4 * i], v[r][4 * i + 1], v[r][4 * i + 2], v[r][4 * i + 3]};
       }
     }
   }
@@ -166,7 +201,7 @@ __global__ void __launch_bounds__(256) k_ln(LnParams p) {
     sv[r] = 0.f;
     if constexpr (MODE == LN_ROPE) {
       const int row = row0 + r < p.rows ? row0 + r : p.rows - 1;
-      const int t = row - p.cu[p.rowclip[row]];
+      const int t = p.rowpos[row];
       if (lane < HALF) {
         cv[r] = p.cos_t[(long)t * HALF + lane];
         sv[r] = p.sin_t[(long)t * HALF + lane];
@@ -175,28 +210,36 @@ __global__ void __launch_bounds__(256) k_ln(LnParams p) {
   }
 #pragma unroll
   for (int r = 0; r < RPW; ++r)
-    if (row0 + r < p.rows) ln_finish<T, NI, MODE>(p, v[r], row0 + r, lane, srow[wv], cv[r], sv[r]);
+    if (row0 + r < p.rows) ln_finish<T, NI, MODE>(p, v[r], row0 + r, lane, srow[wv], cv[r], sv[r], a1, a2);
 }
 
 // rows per wave, by timing inside the encode: two for the two-norm variant (14.8 vs 16.7 us
-// at 8207 rows of 768), one for the others (two made the RoPE variant slower, 13.6 -> 14.9)
+// at 8207 rows of 768), one for the others (two made the RoPE variant slower, 13.6 -> 14.9,
+// and the plain one 8.8 -> 10.0)
 template <typename T, int NI, int MODE, int RPW>
-static void ln_launch(const LnParams& p, hipStream_t s) {
+static hipError_t ln_launch(const LnParams& p, hipStream_t s) {
   dim3 grid((p.rows + 4 * RPW - 1) / (4 * RPW));
-  // the deferred-residual variant is its own instantiation: its stores to x would otherwise
-  // keep the plain kernel's parameter loads from being hoisted
-  if (p.rks > 0) hipLaunchKernelGGL((k_ln<T, NI, MODE, RPW, true>), grid, dim3(256), 0, s, p);
-  else hipLaunchKernelGGL((k_ln<T, NI, MODE, RPW, false>), grid, dim3(256), 0, s, p);
+  // each deferred-residual slice count is its own instantiation: its stores to x would
+  // otherwise keep the plain kernel's parameter loads from being hoisted
+  switch (p.rks) {
+    case 0: hipLaunchKernelGGL((k_ln<T, NI, MODE, RPW, 0>), grid, dim3(256), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((k_ln<T, NI, MODE, RPW, 1>), grid, dim3(256), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((k_ln<T, NI, MODE, RPW, 2>), grid, dim3(256), 0, s, p); break;
+    case 3: hipLaunchKernelGGL((k_ln<T, NI, MODE, RPW, 3>), grid, dim3(256), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((k_ln<T, NI, MODE, RPW, 4>), grid, dim3(256), 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 template <typename T, int NI>
 static hipError_t ln_modes(LnMode mode, const LnParams& p, hipStream_t s) {
   switch (mode) {
-    case LN_PLAIN: ln_launch<T, NI, LN_PLAIN, 1>(p, s); break;
-    case LN_ROPE: ln_launch<T, NI, LN_ROPE, 1>(p, s); break;
-    case LN_TWO: ln_launch<T, NI, LN_TWO, 2>(p, s); break;
+    case LN_PLAIN: return ln_launch<T, NI, LN_PLAIN, 1>(p, s);
+    case LN_ROPE: return ln_launch<T, NI, LN_ROPE, 1>(p, s);
+    case LN_TWO: return ln_launch<T, NI, LN_TWO, 2>(p, s);
   }
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 template <typename T>
@@ -210,6 +253,7 @@ static hipError_t ln_widths(LnMode mode, const LnParams& p, hipStream_t s) {
 
 hipError_t launch_layernorm(DType dt, LnMode mode, const LnParams& p, hipStream_t s) {
   if (p.rows <= 0) return hipSuccess;
+  if (p.rks > 0 && (!p.rpart || !p.rbias)) return hipErrorInvalidValue;
   switch (dt) {
     case DT_F32: return ln_widths<float>(mode, p, s);
     case DT_F16:
