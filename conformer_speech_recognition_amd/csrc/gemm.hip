@@ -735,10 +735,13 @@ static hipError_t run_epi(AMode am, Epi ep, const GemmParams& p, hipStream_t s, 
   return hipErrorInvalidValue;
 }
 
-// Split-K: out = epilogue(sum over slices of the fp32 partials + bias), the slices summed
-// in order 0, 1, ... (deterministic). Thread = 4 consecutive output columns of one row;
-// GLU reads the value columns and their gates 32 columns later (64-column groups).
-template <typename T, int EP>
+// Split-K: out = epilogue(sum over the KS slices of the fp32 partials + bias), the slices
+// summed in order 0, 1, ... (deterministic). Thread = 4 consecutive output columns of one
+// row; GLU reads the value columns and their gates 32 columns later (64-column groups). The
+// slice count is a template argument so that every slice's load is issued before the first
+// add (a loop over a run-time count waited for each load in turn); KS = 0 takes `slices` at
+// run time (the fused FFN's f / 256 slices).
+template <typename T, int EP, int KS>
 __global__ void __launch_bounds__(256) k_splitk_reduce(const float* __restrict__ part, int slices,
                                                        GemmParams p) {
   const int No = (EP == E_GLU) ? p.N / 2 : p.N;
@@ -748,11 +751,21 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(const float* __restrict__
   const int row = (int)(q / qpr), co = (int)(q % qpr) * 4;
   const long slice = (long)p.M * p.N;
   auto sum4 = [&](int col) {
-    f32x4 v = p.bias ? *(const f32x4*)(p.bias + col) : f32x4{0.f, 0.f, 0.f, 0.f};
     const float* src = part + (long)row * p.N + col;
-    f32x4 a = *(const f32x4*)src;
-    for (int k = 1; k < slices; ++k) a += *(const f32x4*)(src + k * slice);
-    return a + v;
+    if constexpr (KS == 0) {
+      const f32x4 v = p.bias ? *(const f32x4*)(p.bias + col) : f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 a = *(const f32x4*)src;
+      for (int k = 1; k < slices; ++k) a += *(const f32x4*)(src + k * slice);
+      return a + v;
+    } else {
+      f32x4 a[KS];
+#pragma unroll
+      for (int k = 0; k < KS; ++k) a[k] = *(const f32x4*)(src + k * slice);
+      const f32x4 v = p.bias ? *(const f32x4*)(p.bias + col) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 1; k < KS; ++k) a[0] += a[k];
+      return a[0] + v;
+    }
   };
   if constexpr (EP == E_GLU) {
     const int c = (co / 32) * 64 + co % 32;              // value column; its gate is c + 32
@@ -806,10 +819,13 @@ static hipError_t run_splitk_reduce(Epi ep, int ks, const GemmParams& p, hipStre
   const int No = (ep == E_GLU) ? p.N / 2 : p.N;
   const long n = (long)p.M * (No / 4);
   dim3 grid((unsigned)((n + 255) / 256));
-#define GG_R(EPv)                                                                      \
-  if (ep == EPv) {                                                                     \
-    hipLaunchKernelGGL((k_splitk_reduce<T, EPv>), grid, dim3(256), 0, s, p.part, ks, p); \
-    return hipGetLastError();                                                          \
+#define GG_R(EPv)                                                                                  \
+  if (ep == EPv) {                                                                                 \
+    if (ks == 2) hipLaunchKernelGGL((k_splitk_reduce<T, EPv, 2>), grid, dim3(256), 0, s, p.part, ks, p); \
+    else if (ks == 4) hipLaunchKernelGGL((k_splitk_reduce<T, EPv, 4>), grid, dim3(256), 0, s, p.part, ks, p); \
+    else if (ks == 8) hipLaunchKernelGGL((k_splitk_reduce<T, EPv, 8>), grid, dim3(256), 0, s, p.part, ks, p); \
+    else hipLaunchKernelGGL((k_splitk_reduce<T, EPv, 0>), grid, dim3(256), 0, s, p.part, ks, p);          \
+    return hipGetLastError();                                                                      \
   }
   GG_R(E_STORE) GG_R(E_SILU) GG_R(E_RESID) GG_R(E_GLU) GG_R(E_F32) GG_R(E_RELU) GG_R(E_RELU_F32)
 #undef GG_R
