@@ -795,6 +795,23 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(const float* __restrict__
   }
 }
 
+// Split-K for an fp32 output of any width (the CTC head: 34, 129 or 257 classes): one thread
+// per output, the KS slices summed in order, then the bias.
+template <int KS>
+__global__ void __launch_bounds__(256) k_splitk_reduce_f32(const float* __restrict__ part, GemmParams p) {
+  const long q = (long)blockIdx.x * 256 + threadIdx.x;
+  if (q >= (long)p.M * p.N) return;
+  const int row = (int)(q / p.N), col = (int)(q % p.N);
+  const long slice = (long)p.M * p.N;
+  float a[KS];
+#pragma unroll
+  for (int k = 0; k < KS; ++k) a[k] = part[q + k * slice];
+  const float b = p.bias ? p.bias[col] : 0.f;
+#pragma unroll
+  for (int k = 1; k < KS; ++k) a[0] += a[k];
+  ((float*)p.C)[(long)row * p.ldc + col] = a[0] + b;
+}
+
 // Residual GEMMs whose split-K sum the next kernel adds (the LayerNorm that reads x):
 // launch_gemm's caller passes where to report the slices; the reduce launch is skipped. Only
 // up to kDeferMaxSlices: the LayerNorm has one wave per row, and adding 8 slices there was
@@ -805,7 +822,10 @@ constexpr int kDeferMaxSlices = 4;
 // Slices for a launch of `tiles` workgroups over K (k-tile KB): only when the tiles fill
 // less than half the chip, at most 8 slices of at least two k-tiles, tiles * slices <= 256.
 static int splitk_slices(const GemmParams& p, long tiles, int KB, Epi ep) {
-  if (!p.part || tiles >= 128 || p.N % 4 != 0 || (ep == E_GLU && p.N % 64 != 0) || p.ldc % 4 != 0)
+  // (fp32 outputs of any width have a reduce of their own)
+  const bool any_width = ep == E_F32;
+  if (!p.part || tiles >= 128 || (!any_width && (p.N % 4 != 0 || p.ldc % 4 != 0)) ||
+      (ep == E_GLU && p.N % 64 != 0))
     return 1;
   int ks = 1;
   while (ks < 8 && tiles * ks * 2 <= 256 && p.K % (ks * 2 * KB) == 0 && p.K / (ks * 2) >= 2 * KB &&
@@ -816,6 +836,14 @@ static int splitk_slices(const GemmParams& p, long tiles, int KB, Epi ep) {
 
 template <typename T>
 static hipError_t run_splitk_reduce(Epi ep, int ks, const GemmParams& p, hipStream_t s) {
+  if (ep == E_F32 && (p.N % 4 != 0 || p.ldc % 4 != 0)) {
+    dim3 grid((unsigned)(((long)p.M * p.N + 255) / 256));
+    if (ks == 2) hipLaunchKernelGGL((k_splitk_reduce_f32<2>), grid, dim3(256), 0, s, p.part, p);
+    else if (ks == 4) hipLaunchKernelGGL((k_splitk_reduce_f32<4>), grid, dim3(256), 0, s, p.part, p);
+    else if (ks == 8) hipLaunchKernelGGL((k_splitk_reduce_f32<8>), grid, dim3(256), 0, s, p.part, p);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
   const int No = (ep == E_GLU) ? p.N / 2 : p.N;
   const long n = (long)p.M * (No / 4);
   dim3 grid((unsigned)((n + 255) / 256));
@@ -827,7 +855,11 @@ static hipError_t run_splitk_reduce(Epi ep, int ks, const GemmParams& p, hipStre
     else hipLaunchKernelGGL((k_splitk_reduce<T, EPv, 0>), grid, dim3(256), 0, s, p.part, ks, p);          \
     return hipGetLastError();                                                                      \
   }
-  GG_R(E_STORE) GG_R(E_SILU) GG_R(E_RESID) GG_R(E_GLU) GG_R(E_F32) GG_R(E_RELU) GG_R(E_RELU_F32)
+  if constexpr (sizeof(T) == 4) {
+    GG_R(E_F32)                        // the fp32 CTC head of the 16-bit models
+  } else {
+    GG_R(E_STORE) GG_R(E_SILU) GG_R(E_RESID) GG_R(E_GLU) GG_R(E_F32) GG_R(E_RELU) GG_R(E_RELU_F32)
+  }
 #undef GG_R
   return hipErrorInvalidValue;
 }
@@ -848,7 +880,8 @@ static hipError_t run_tiles(AMode am, Epi ep, const GemmParams& p, hipStream_t s
     if (BN == 64) return run_epi<T, 128, 64, 4, 1, QB>(am, e, q, s, k);
     return run_epi<T, 128, 128, 2, 2, QB>(am, e, q, s, k);
   };
-  if constexpr (sizeof(T) == 2) {
+  // 16-bit models (which bring a workspace); their fp32 CTC head too (fp32 models have none)
+  if (sizeof(T) == 2 || ep == E_F32) {
     const int ks = splitk_slices(p, tiles, 64, ep);
     if (ks > 1) {
       GemmParams q = p;
@@ -1033,7 +1066,7 @@ static bool dequant_first(int qbits, AMode am, Epi ep, const GemmParams& p) {
 }
 
 int gemm_split_slices(DType dt, int qbits, AMode am, Epi ep, const GemmParams& p) {
-  if (dt == DT_F32) return 1;
+  if (dt == DT_F32 && ep != E_F32) return 1;          // fp32 splits only an fp32-output product
   if (qbits != 0 && dequant_first(qbits, am, ep, p)) return 1;
   if (!direct_path(dt, qbits, am, ep, p)) {           // the register-staged kernel
     int BM, BN;

@@ -115,3 +115,23 @@ def test_dequantised_pipeline_matches_float64(dtype, M, N, K):
           f"vs register-staged {np.abs(C - C1).max():.3e}", flush=True)
     assert ks == 1
     assert err <= bound and np.abs(C1 - ref).max() <= bound
+
+
+@pytest.mark.parametrize("M,N,K", [(500, 34, 768), (77, 257, 768), (1, 129, 1024)])
+def test_fp32_head_split_matches_float64(M, N, K):
+    """The fp32 CTC head of the 16-bit models at few rows: its K sum is split too, and an
+    output width that is no multiple of 4 (34, 129, 257 classes) is reduced one output per
+    thread; same bound as the unsplit kernel, which agrees with it."""
+    import conformer_speech_recognition_amd as gg
+    print(f"[gemm head split] M={M} N={N} K={K}", flush=True)
+    A, W, S, bias, a, w, b = _operands("f32", M, N, K, seed=M * 7 + N + K)
+    C, ks = gg.debug_gemm("f32", A, W, bias=bias, scale=S, split=True)
+    C = C.cpu().numpy().astype(np.float64)
+    C1 = gg.debug_gemm("f32", A, W, bias=bias, scale=S).cpu().numpy().astype(np.float64)
+    ref = a @ w.T + b
+    bound = 1e-6 * K * np.abs(a).max() * np.abs(w).max() + 1e-5
+    err = np.abs(C - ref).max()
+    print(f"[gemm head split] {M}x{N}x{K}: {ks} slices, max|d| = {err:.3e} (bound {bound:.2e}), "
+          f"vs unsplit {np.abs(C - C1).max():.3e}", flush=True)
+    assert ks > 1
+    assert err <= bound and np.abs(C1 - ref).max() <= bound
