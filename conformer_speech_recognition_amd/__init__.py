@@ -416,7 +416,8 @@ GEMM_A = {"plain": 0, "dual": 2}
 GEMM_E = {"store": 0, "silu": 1, "glu": 4, "resid": 5, "f32": 6}
 GEMM_SHAPES = {1: "reg_128x64", 2: "reg_128x128", 3: "dma_256x256", 4: "dma_256x128_k32",
                5: "dma_256x128_k64", 6: "dma_128x128", 7: "dma_256x192", 8: "dma_256x128_w4",
-               9: "dma_256x128_w4s", 10: "dma_128x256"}
+               9: "dma_256x128_w4s", 10: "dma_128x256",
+               11: "dma_128x128_s3"}
 GEMM_SHAPE_IDS = {v: k for k, v in GEMM_SHAPES.items()}
 
 

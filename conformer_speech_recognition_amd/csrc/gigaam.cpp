@@ -958,7 +958,7 @@ extern "C" int gigaam_debug_gemm_role(int32_t dtype, int32_t a_mode, int32_t epi
   const AMode am = (AMode)a_mode;
   const Epi ep = (Epi)epilogue;
   if (shape_request != 0) {
-    if (shape_request < GIGAAM_GEMM_DMA_256x256 || shape_request > GIGAAM_GEMM_DMA_128x256)
+    if (shape_request < GIGAAM_GEMM_DMA_256x256 || shape_request > GIGAAM_GEMM_DMA_128x128_S3)
       return fail(GIGAAM_E_INVAL, "shape_request %d is not a direct-load variant", shape_request);
     const int natural = gemm_shape_id((DType)dtype, qb, am, ep, p);
     if (natural < GIGAAM_GEMM_DMA_256x256)

@@ -55,7 +55,8 @@ int gemm_split_slices(DType dt, int qbits, AMode am, Epi ep, const GemmParams& p
 enum GemmShape {
   GEMM_REG_128x64 = 1, GEMM_REG_128x128 = 2, GEMM_DMA_256x256 = 3, GEMM_DMA_256x128_K32 = 4,
   GEMM_DMA_256x128_K64 = 5, GEMM_DMA_128x128 = 6, GEMM_DMA_256x192 = 7, GEMM_DMA_256x128_W4 = 8,
-  GEMM_DMA_256x128_W4S = 9, GEMM_DMA_128x256 = 10
+  GEMM_DMA_256x128_W4S = 9, GEMM_DMA_128x256 = 10,
+  GEMM_DMA_128x128_S3 = 11
 };
 int gemm_shape_id(DType dt, int qbits, AMode am, Epi ep, const GemmParams& p);
 // Diagnostics: force the direct-load variant of the following launches on this thread (0:

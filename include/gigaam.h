@@ -278,7 +278,8 @@ int gigaam_debug_gemm(int32_t dtype, int32_t M, int32_t N, int32_t K, const void
  * only; GLU needs an even number of 32-column blocks per wave, the dual mode a split at
  * a multiple of the tile width). shape_host (may be NULL) receives the kernel shape
  * used, one of GIGAAM_GEMM_REG_* (register-staged loads, 4 waves) or GIGAAM_GEMM_DMA_*
- * (direct-to-LDS pipeline: tile rows x columns, 8 waves unless _W4*: 4 waves). K must be
+ * (direct-to-LDS pipeline: tile rows x columns, 8 waves unless _W4*: 4 waves; _S3: three
+ * k-tile stages, one workgroup per CU, taken when the tiles are few). K must be
  * a multiple of 64 (32 for GIGAAM_F32). Errors: GIGAAM_E_INVAL, GIGAAM_E_HIP.        */
 enum { GIGAAM_GEMM_A_PLAIN = 0, GIGAAM_GEMM_A_DUAL = 2 };
 enum { GIGAAM_GEMM_E_STORE = 0, GIGAAM_GEMM_E_SILU = 1, GIGAAM_GEMM_E_GLU = 4,
@@ -286,7 +287,8 @@ enum { GIGAAM_GEMM_E_STORE = 0, GIGAAM_GEMM_E_SILU = 1, GIGAAM_GEMM_E_GLU = 4,
 enum { GIGAAM_GEMM_REG_128x64 = 1, GIGAAM_GEMM_REG_128x128 = 2, GIGAAM_GEMM_DMA_256x256 = 3,
        GIGAAM_GEMM_DMA_256x128_K32 = 4, GIGAAM_GEMM_DMA_256x128_K64 = 5,
        GIGAAM_GEMM_DMA_128x128 = 6, GIGAAM_GEMM_DMA_256x192 = 7, GIGAAM_GEMM_DMA_256x128_W4 = 8,
-       GIGAAM_GEMM_DMA_256x128_W4S = 9, GIGAAM_GEMM_DMA_128x256 = 10 };
+       GIGAAM_GEMM_DMA_256x128_W4S = 9, GIGAAM_GEMM_DMA_128x256 = 10,
+       GIGAAM_GEMM_DMA_128x128_S3 = 11 };
 int gigaam_debug_gemm_role(int32_t dtype, int32_t a_mode, int32_t epilogue, int32_t M, int32_t N,
                            int32_t K, const void* A_dev, const void* A2_dev, int32_t nsplit,
                            const void* W_dev, const void* scale_dev, const float* bias_dev,

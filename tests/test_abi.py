@@ -279,7 +279,7 @@ def test_debug_gemm_role_validation(gg):
     assert call(part=fake + 4) == gg.E_INVAL
     assert call(dt=3) == gg.E_INVAL                                  # quantised weights need scales
     assert call(req=2) == gg.E_INVAL                                 # not a direct-load variant
-    assert call(req=11) == gg.E_INVAL
+    assert call(req=12) == gg.E_INVAL
     assert call(dt=0, req=3) == gg.E_INVAL                           # fp32 runs the register path
     assert call(ep=4, N=384, req=7) == gg.E_INVAL                    # 256x192: no GLU pairs
     assert call(am=2, ep=0, A2=fake, ns=128, N=512, req=3) == gg.E_INVAL   # split inside a tile
