@@ -6,7 +6,11 @@
 
 namespace gg {
 
+// a row of up to 64 * kLsmRegs classes is held in registers
+constexpr int kLsmRegs = 8;
+
 // One wave per padded output row (b, t). Rows t >= U_b are zero / -1.
+
 __global__ void __launch_bounds__(256) k_logsoftmax_argmax(const float* __restrict__ logits,
                                                            int C, int B, int U_max,
                                                            const int* __restrict__ cuU,
@@ -26,16 +30,41 @@ __global__ void __launch_bounds__(256) k_logsoftmax_argmax(const float* __restri
   const float* z = logits + (long)(cuU[b] + t) * C;
   float best = -INFINITY;
   int bi = 0x7fffffff;
-  for (int c = lane; c < C; c += 64) {
-    const float v = z[c];
-    if (v > best) { best = v; bi = c; }        // ascending c: first max wins per lane
+  if (C <= 64 * kLsmRegs) {
+    // the row in registers, all its loads issued together (columns past C clamped, unused)
+    float zv[kLsmRegs];
+#pragma unroll
+    for (int j = 0; j < kLsmRegs; ++j) {
+      const int c = lane + 64 * j;
+      zv[j] = z[c < C ? c : C - 1];
+    }
+#pragma unroll
+    for (int j = 0; j < kLsmRegs; ++j) {
+      const int c = lane + 64 * j;
+      if (c < C && zv[j] > best) { best = zv[j]; bi = c; }   // ascending c: first max wins per lane
+    }
+    wave_argmax(best, bi);
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < kLsmRegs; ++j)
+      if (lane + 64 * j < C) s += expf(zv[j] - best);
+    s = wave_sum(s);
+    const float lse = best + logf(s);
+#pragma unroll
+    for (int j = 0; j < kLsmRegs; ++j)
+      if (lane + 64 * j < C) out[lane + 64 * j] = zv[j] - lse;
+  } else {
+    for (int c = lane; c < C; c += 64) {
+      const float v = z[c];
+      if (v > best) { best = v; bi = c; }
+    }
+    wave_argmax(best, bi);
+    float s = 0.f;
+    for (int c = lane; c < C; c += 64) s += expf(z[c] - best);
+    s = wave_sum(s);
+    const float lse = best + logf(s);
+    for (int c = lane; c < C; c += 64) out[c] = z[c] - lse;
   }
-  wave_argmax(best, bi);
-  float s = 0.f;
-  for (int c = lane; c < C; c += 64) s += expf(z[c] - best);
-  s = wave_sum(s);
-  const float lse = best + logf(s);
-  for (int c = lane; c < C; c += 64) out[c] = z[c] - lse;
   if (lane == 0) frame_ids[row] = bi;
 }
 
