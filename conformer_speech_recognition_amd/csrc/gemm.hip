@@ -819,16 +819,23 @@ __global__ void __launch_bounds__(256) k_splitk_reduce_f32(const float* __restri
 static thread_local int* g_defer_ks = nullptr;
 constexpr int kDeferMaxSlices = 4;
 
-// Slices for a launch of `tiles` workgroups over K (k-tile KB): only when the tiles fill
-// less than half the chip, at most 8 slices of at least two k-tiles, tiles * slices <= 256.
+// Slices for a launch of `tiles` workgroups over K (k-tile KB), tiles * slices <= 256, slices
+// of at least two k-tiles: at most 8, or kDeferMaxSlices when the next LayerNorm takes them;
+// only when the tiles fill less than half the chip, or less than a quarter when K <= 1024
+// and a reduce launch would follow (measured on 20 s clips: 1 clip 8.37k -> 9.34k audio-s/s,
+// 2 clips 15.4k -> 16.7k, 4 and more unchanged; the quarter rule alone lost 3% at 4 clips,
+// where the out-projection's 96 tiles gain from a split the LayerNorm finishes).
 static int splitk_slices(const GemmParams& p, long tiles, int KB, Epi ep) {
   // (fp32 outputs of any width have a reduce of their own)
   const bool any_width = ep == E_F32;
-  if (!p.part || tiles >= 128 || (!any_width && (p.N % 4 != 0 || p.ldc % 4 != 0)) ||
+  const bool deferred = ep == E_RESID && g_defer_ks;
+  const long below = (deferred || p.K > 1024) ? 128 : 64;
+  if (!p.part || tiles >= below || (!any_width && (p.N % 4 != 0 || p.ldc % 4 != 0)) ||
       (ep == E_GLU && p.N % 64 != 0))
     return 1;
   int ks = 1;
-  while (ks < 8 && tiles * ks * 2 <= 256 && p.K % (ks * 2 * KB) == 0 && p.K / (ks * 2) >= 2 * KB &&
+  const int kmax = deferred ? kDeferMaxSlices : 8;
+  while (ks < kmax && tiles * ks * 2 <= 256 && p.K % (ks * 2 * KB) == 0 && p.K / (ks * 2) >= 2 * KB &&
          (long)p.M * p.N * ks * 2 <= p.part_cap)
     ks *= 2;
   return ks;
