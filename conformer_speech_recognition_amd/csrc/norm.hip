@@ -213,9 +213,9 @@ __global__ void __launch_bounds__(256) k_ln(LnParams p) {
     if (row0 + r < p.rows) ln_finish<T, NI, MODE>(p, v[r], row0 + r, lane, srow[wv], cv[r], sv[r], a1, a2);
 }
 
-// rows per wave, by timing inside the encode: two for the two-norm variant (14.8 vs 16.7 us
-// at 8207 rows of 768), one for the others (two made the RoPE variant slower, 13.6 -> 14.9,
-// and the plain one 8.8 -> 10.0)
+// rows per wave, by timing inside the encode: one (two made the RoPE variant slower, 11.3 ->
+// 12.4 us at 8207 rows of 768, and the plain one 8.8 -> 10.0; the two-norm variant, faster with
+// two rows while its parameter loads waited for its first row, is now 13.7 -> 13.5 us with one)
 template <typename T, int NI, int MODE, int RPW>
 static hipError_t ln_launch(const LnParams& p, hipStream_t s) {
   dim3 grid((p.rows + 4 * RPW - 1) / (4 * RPW));
@@ -237,7 +237,7 @@ static hipError_t ln_modes(LnMode mode, const LnParams& p, hipStream_t s) {
   switch (mode) {
     case LN_PLAIN: return ln_launch<T, NI, LN_PLAIN, 1>(p, s);
     case LN_ROPE: return ln_launch<T, NI, LN_ROPE, 1>(p, s);
-    case LN_TWO: return ln_launch<T, NI, LN_TWO, 2>(p, s);
+    case LN_TWO: return ln_launch<T, NI, LN_TWO, 1>(p, s);
   }
   return hipErrorInvalidValue;
 }
