@@ -96,9 +96,14 @@ template <> struct AttnMma32<bf16> {
   }
 };
 
-template <typename T, int DK>
-__global__ void __launch_bounds__(256, 4) k_attn(AttnParams p) {
-  constexpr int QT = 128;            // queries per block
+// KS2 = 2 (batches with fewer items than CUs): a block takes a 64-frame query tile; waves 0
+// and 1 own its two 32-query groups over the even 64-key tiles, waves 2 and 3 the same
+// queries over the odd ones, and the pairs' partial results (reference max, unnormalised
+// output with its probability-sum row) are merged at the end; twice the blocks, each
+// walking half the keys per wave.
+template <typename T, int DK, int KS2 = 1>
+__global__ void __launch_bounds__(256, KS2 == 1 ? 4 : 2) k_attn(AttnParams p) {
+  constexpr int QT = 128 / KS2;      // queries per block
   constexpr int KP = DK + 8;         // K row pitch (elements): 16 rows of a read pass on disjoint banks
   // V row pitch: dims, the ones column, zeros; 96 elements (48 dwords) put the 4 rows of one
   // transposing read pass, 32 dims each, on disjoint banks
@@ -109,16 +114,19 @@ __global__ void __launch_bounds__(256, 4) k_attn(AttnParams p) {
   constexpr int KCH = AT_KV * CPR;   // 16-byte chunks per tile (each of K and V)
   constexpr int KPT = (KCH + 255) / 256;    // chunks per thread
   static_assert(DK % 16 == 0 && NDB * 32 <= VP, "head size");
-  __shared__ __attribute__((aligned(16))) T sK[2][AT_KV][KP];
-  __shared__ __attribute__((aligned(16))) T sV[2][AT_KV][VP];
+  __shared__ __attribute__((aligned(16))) T sK[2][KS2][AT_KV][KP];
+  __shared__ __attribute__((aligned(16))) T sV[2][KS2][AT_KV][VP];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hf = lane >> 5, c32 = lane & 31;
+  const int qg = KS2 == 1 ? wave : (wave & 1);             // the wave's 32-query group
+  const int kg = KS2 == 1 ? 0 : (wave >> 1);                // its share of the key tiles
+  const int* cuQ = KS2 == 1 ? p.cuQ : p.cuQ64;
   int tile, h;
-  attn_item(blockIdx.x, p.n_tiles, p.n_heads, tile, h);
-  const int b = p.tileQ[tile];
+  attn_item(blockIdx.x, KS2 == 1 ? p.n_tiles : p.n_tiles64, p.n_heads, tile, h);
+  const int b = (KS2 == 1 ? p.tileQ : p.tileQ64)[tile];
   const int base = p.cuU[b], U = p.cuU[b + 1] - base;
-  const int q0 = (tile - p.cuQ[b]) * QT + wave * 32;      // the wave's first query
+  const int q0 = (tile - cuQ[b]) * QT + qg * 32;           // the wave's first query
   const bool active = q0 < U;                              // wave-uniform
   const int qi = q0 + c32;
   const int ld = 3 * p.d;
@@ -167,36 +175,45 @@ __global__ void __launch_bounds__(256, 4) k_attn(AttnParams p) {
       vls[i] = key * VP + ch * 8;
     }
   }
-  u32x4 rk[KPT], rv[KPT];
+  u32x4 rk[KS2][KPT], rv[KS2][KPT];
+  // key tiles kv0 + 64 j, j < KS2 (a tile past the clip reads as zeros: empty resource)
   auto load = [&](int kv0) {
-    const int bytes = (U - kv0) * ld * (int)sizeof(T);
-    const __amdgpu_buffer_rsrc_t rK =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(Kg + (long)kv0 * ld), 0, bytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rV =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(Vg + (long)kv0 * ld), 0, bytes, 0x00020000);
 #pragma unroll
-    for (int i = 0; i < KPT; ++i)
-      if (KCH % 256 == 0 || tid + 256 * i < KCH) {
-        rk[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rK, koff[i], 0, 0));
-        rv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rV, voff[i], 0, 0));
-      }
+    for (int j = 0; j < KS2; ++j) {
+      const int kvj = kv0 + AT_KV * j;
+      const bool in = j == 0 || kvj < U;       // the first tile is always inside the clip
+      const int bytes = in ? (U - kvj) * ld * (int)sizeof(T) : 0;
+      const int kvc = in ? kvj : 0;
+      const __amdgpu_buffer_rsrc_t rK =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(Kg + (long)kvc * ld), 0, bytes, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rV =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(Vg + (long)kvc * ld), 0, bytes, 0x00020000);
+#pragma unroll
+      for (int i = 0; i < KPT; ++i)
+        if (KCH % 256 == 0 || tid + 256 * i < KCH) {
+          rk[j][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rK, koff[i], 0, 0));
+          rv[j][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rV, voff[i], 0, 0));
+        }
+    }
   };
   auto store = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < KPT; ++i)
-      if (KCH % 256 == 0 || tid + 256 * i < KCH) {
-        *(u32x4*)(&sK[buf][0][0] + kls[i]) = rk[i];
-        *(u32x4*)(&sV[buf][0][0] + vls[i]) = rv[i];
-      }
+    for (int j = 0; j < KS2; ++j)
+#pragma unroll
+      for (int i = 0; i < KPT; ++i)
+        if (KCH % 256 == 0 || tid + 256 * i < KCH) {
+          *(u32x4*)(&sK[buf][j][0][0] + kls[i]) = rk[j][i];
+          *(u32x4*)(&sV[buf][j][0][0] + vls[i]) = rv[j][i];
+        }
   };
   // columns DK .. VP - 1 of both V buffers: one at DK, zeros after it (never overwritten by
   // the tile stores)
   {
     constexpr int XC = (VP - DK) / 8;            // 16-byte chunks per row past the dims
     const uint32_t one = (uint32_t)__builtin_bit_cast(uint16_t, (T)1.0f);
-    for (int e = tid; e < 2 * AT_KV * XC; e += 256) {
+    for (int e = tid; e < 2 * KS2 * AT_KV * XC; e += 256) {
       const int vb = e / (AT_KV * XC), rem = e - vb * AT_KV * XC, key = rem / XC, x = rem - key * XC;
-      *(u32x4*)&sV[vb][key][DK + 8 * x] = u32x4{x == 0 ? one : 0u, 0u, 0u, 0u};
+      *(u32x4*)&sV[vb / KS2][vb % KS2][key][DK + 8 * x] = u32x4{x == 0 ? one : 0u, 0u, 0u, 0u};
     }
   }
   // this lane's transposing V reads: lane 4 s + q of its 16-lane group g names key
@@ -218,15 +235,16 @@ __global__ void __launch_bounds__(256, 4) k_attn(AttnParams p) {
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   __syncthreads();
   int buf = 0;
-  for (int kv0 = 0; kv0 < U; kv0 += AT_KV) {
-    const bool more = kv0 + AT_KV < U;
-    if (more) load(kv0 + AT_KV);
-    if (active) {
-      // S^T blocks: s[kb][r] = raw score(key kv0 + 32 kb + 8 (r / 4) + 4 hf + r % 4, query qi)
+  for (int kv0 = 0; kv0 < U; kv0 += AT_KV * KS2) {
+    const bool more = kv0 + AT_KV * KS2 < U;
+    if (more) load(kv0 + AT_KV * KS2);
+    const int kvw = kv0 + AT_KV * kg;                       // this wave's key tile
+    if (active && (KS2 == 1 || kvw < U)) {
+      // S^T blocks: s[kb][r] = raw score(key kvw + 32 kb + 8 (r / 4) + 4 hf + r % 4, query qi)
       f32x16 s[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const T* kr = &sK[buf][kb * 32 + c32][8 * hf];
+        const T* kr = &sK[buf][kg][kb * 32 + c32][8 * hf];
         f32x16 acc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[r] = 0.f;
@@ -234,8 +252,8 @@ __global__ void __launch_bounds__(256, 4) k_attn(AttnParams p) {
         for (int ks = 0; ks < KS; ++ks) acc = AttnMma32<T>::run(*(const u32x4*)(kr + 16 * ks), qf[ks], acc);
         s[kb] = acc;
       }
-      if (!more) {                   // the clip's last tile: keys >= U get probability 0
-        const int lim = U - kv0 - 4 * hf;         // first masked key offset of this lane's rows
+      if (KS2 == 1 ? !more : kvw + AT_KV > U) {   // the clip's last tile: keys >= U get probability 0
+        const int lim = U - kvw - 4 * hf;         // first masked key offset of this lane's rows
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -270,8 +288,8 @@ __global__ void __launch_bounds__(256, 4) k_attn(AttnParams p) {
           const int k0 = 32 * kb + 16 * j + tr_key;
 #pragma unroll
           for (int db = 0; db < NDB; ++db) {
-            const u32x2 lo = lds_read_tr(&sV[buf][k0][32 * db + tr_dim]);
-            const u32x2 hi = lds_read_tr(&sV[buf][k0 + 8][32 * db + tr_dim]);
+            const u32x2 lo = lds_read_tr(&sV[buf][kg][k0][32 * db + tr_dim]);
+            const u32x2 hi = lds_read_tr(&sV[buf][kg][k0 + 8][32 * db + tr_dim]);
             o[db] = AttnMma32<T>::run(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb, o[db]);
           }
         }
@@ -279,6 +297,30 @@ __global__ void __launch_bounds__(256, 4) k_attn(AttnParams p) {
     if (more) store(buf ^ 1);
     __syncthreads();
     buf ^= 1;
+  }
+  if constexpr (KS2 == 2) {
+    // merge the odd-tile waves' results into the even-tile waves' (every wave is past its
+    // last LDS read: the loop ended on a barrier): per lane its query's reference max and
+    // output rows, scaled to the larger of the two maxima
+    constexpr int XW = 1 + NDB * 16;
+    float* xo = (float*)&sK[0][0][0][0] + (qg * 64 + lane) * XW;
+    if (kg == 1) {
+      xo[0] = m_run;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xo[1 + 16 * db + r] = o[db][r];
+    }
+    __syncthreads();
+    if (kg == 1 || !active) return;
+    const float mb = xo[0];
+    const float mm = fmaxf(m_run, mb);
+    const float fa = __builtin_amdgcn_exp2f((m_run - mm) * c);
+    const float fb = mb == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mb - mm) * c);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * fa + xo[1 + 16 * db + r] * fb;
   }
   if (!active) return;
 
@@ -399,20 +441,35 @@ __global__ void __launch_bounds__(256) k_attn_f32(AttnParams p) {
   }
 }
 
+constexpr long kAttnSplitBelow = 256;
+
 hipError_t launch_attention(DType dt, int dk, const AttnParams& p, hipStream_t s) {
   if (p.n_tiles <= 0) return hipSuccess;
   dim3 grid(p.n_tiles * p.n_heads), blk(256);
+  // fewer 128-query items than CUs (a clip or two): 64-query items with the keys split
+  // between two wave pairs (one 20 s clip: 64 -> 128 workgroups)
+  const bool split = dt != DT_F32 && p.n_tiles64 > 0 && p.cuQ64 && p.tileQ64 &&
+                     (long)p.n_tiles * p.n_heads < kAttnSplitBelow;
+  dim3 grid2(split ? p.n_tiles64 * p.n_heads : 1);
 #define GG_A(T, D) hipLaunchKernelGGL((k_attn<T, D>), grid, blk, 0, s, p)
+#define GG_A2(T, D) hipLaunchKernelGGL((k_attn<T, D, 2>), grid2, blk, 0, s, p)
   if (dt == DT_F32) {
     if (dk == 48) hipLaunchKernelGGL(k_attn_f32<48>, grid, blk, 0, s, p);
     else if (dk == 64) hipLaunchKernelGGL(k_attn_f32<64>, grid, blk, 0, s, p);
     else return hipErrorInvalidValue;
+  } else if (split) {
+    if (dt == DT_BF16) {
+      if (dk == 48) GG_A2(bf16, 48); else if (dk == 64) GG_A2(bf16, 64); else return hipErrorInvalidValue;
+    } else {
+      if (dk == 48) GG_A2(f16, 48); else if (dk == 64) GG_A2(f16, 64); else return hipErrorInvalidValue;
+    }
   } else if (dt == DT_BF16) {
     if (dk == 48) GG_A(bf16, 48); else if (dk == 64) GG_A(bf16, 64); else return hipErrorInvalidValue;
   } else {
     if (dk == 48) GG_A(f16, 48); else if (dk == 64) GG_A(f16, 64); else return hipErrorInvalidValue;
   }
 #undef GG_A
+#undef GG_A2
   return hipGetLastError();
 }
 

@@ -765,7 +765,7 @@ int run(gigaam_model* m, const float* pcm, const int32_t* lengths, int32_t B, in
   };
   const bool f32 = dt == DT_F32;              // the fp32 kernel works on 64-frame tiles
   AttnParams ap{qkv, ao, d, H, f32 ? nQ : nQ2, md.cuU, f32 ? md.cuQ : md.cuQ2, f32 ? md.tileQ : md.tileQ2,
-                (float)(1.4426950408889634 / std::sqrt((double)dk))};
+                (float)(1.4426950408889634 / std::sqrt((double)dk)), f32 ? 0 : nQ, md.cuQ, md.tileQ};
   DwParams dp;
   dp.in = hid; dp.out = hid2; dp.d = d; dp.n_tiles = nQ; dp.cuU = md.cuU; dp.cuQ = md.cuQ;
   dp.tileQ = md.tileQ; dp.tileG = md.tileG; dp.eps = c.bn_eps;
@@ -1037,7 +1037,8 @@ extern "C" int gigaam_debug_attention(int32_t dtype, int32_t d_model, int32_t n_
   HIP_TRY(launch_meta(meta, md, U_tot, U_tot, U_tot, s));
   const bool f32 = dtype == GIGAAM_F32;
   AttnParams ap{qkv_dev, out_dev, d_model, n_heads, f32 ? nQ : nQ2, md.cuU, f32 ? md.cuQ : md.cuQ2,
-                f32 ? md.tileQ : md.tileQ2, (float)(1.4426950408889634 / std::sqrt((double)dk))};
+                f32 ? md.tileQ : md.tileQ2, (float)(1.4426950408889634 / std::sqrt((double)dk)),
+                f32 ? 0 : nQ, md.cuQ, md.tileQ};
   HIP_TRY(launch_attention((DType)dtype, dk, ap, s));
   return GIGAAM_OK;
 }

@@ -1,12 +1,18 @@
 """GPU: the attention kernel alone (gigaam_debug_attention) against a float64
 softmax(q k^T / sqrt(d_k)) v per clip and head, over ragged clip lengths that cover
-partial 64-frame tiles, single-frame clips and the longest workload clip."""
+partial 64-frame tiles, single-frame clips, the longest workload clip, and batches on
+either side of the few-items limit of the 16-bit kernel."""
 import numpy as np
 import pytest
 
 pytestmark = pytest.mark.gpu
 
-FRAMES = [[1], [17], [64], [65], [500], [750], [51, 497, 3, 128, 129, 250]]
+# Batches with fewer (128-query tile x head) items than CUs take the key-split kernel (64-query
+# tiles, keys shared by two wave pairs); the last two cases sit just under that limit and far
+# over it (the 128-query kernel).
+FRAMES = [[1], [17], [64], [65], [500], [750], [51, 497, 3, 128, 129, 250],
+          [500, 500, 500, 128, 127, 64],
+          [250] * 8 + [129] * 4 + [1, 64, 700, 333]]
 
 
 def _ref(q, k, v, frames, H):
@@ -27,7 +33,7 @@ def _ref(q, k, v, frames, H):
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("d", [768, 1024])
-@pytest.mark.parametrize("frames", FRAMES, ids=lambda f: "-".join(map(str, f)))
+@pytest.mark.parametrize("frames", FRAMES, ids=lambda f: "-".join(map(str, f)) if len(f) < 8 else f"{len(f)}clips-{sum(f)}")
 def test_attention_matches_float64(dtype, d, frames):
     import torch
     import conformer_speech_recognition_amd as gg
