@@ -96,7 +96,7 @@ template <> struct AttnMma32<bf16> {
   }
 };
 
-// KS2 = 2 (batches with fewer items than CUs): a block takes a 64-frame query tile; waves 0
+// KS2 = 2 (a clip or two: no more 64-query items than CUs): a block takes a 64-frame query tile; waves 0
 // and 1 own its two 32-query groups over the even 64-key tiles, waves 2 and 3 the same
 // queries over the odd ones, and the pairs' partial results (reference max, unnormalised
 // output with its probability-sum row) are merged at the end; twice the blocks, each
@@ -441,15 +441,16 @@ __global__ void __launch_bounds__(256) k_attn_f32(AttnParams p) {
   }
 }
 
-constexpr long kAttnSplitBelow = 256;
+constexpr long kAttnSplitMax = 256;           // 64-query items: at most one per CU
 
 hipError_t launch_attention(DType dt, int dk, const AttnParams& p, hipStream_t s) {
   if (p.n_tiles <= 0) return hipSuccess;
   dim3 grid(p.n_tiles * p.n_heads), blk(256);
-  // fewer 128-query items than CUs (a clip or two): 64-query items with the keys split
-  // between two wave pairs (one 20 s clip: 64 -> 128 workgroups)
+  // a clip or two: 64-query items with the keys split between two wave pairs (one 20 s clip:
+  // 64 -> 128 workgroups), as long as every such workgroup gets a CU of its own (beyond that,
+  // two of them sharing a CU take as long as one 128-query item, and the merge is extra)
   const bool split = dt != DT_F32 && p.n_tiles64 > 0 && p.cuQ64 && p.tileQ64 &&
-                     (long)p.n_tiles * p.n_heads < kAttnSplitBelow;
+                     (long)p.n_tiles64 * p.n_heads <= kAttnSplitMax;
   dim3 grid2(split ? p.n_tiles64 * p.n_heads : 1);
 #define GG_A(T, D) hipLaunchKernelGGL((k_attn<T, D>), grid, blk, 0, s, p)
 #define GG_A2(T, D) hipLaunchKernelGGL((k_attn<T, D, 2>), grid2, blk, 0, s, p)

@@ -1,17 +1,17 @@
 """GPU: the attention kernel alone (gigaam_debug_attention) against a float64
 softmax(q k^T / sqrt(d_k)) v per clip and head, over ragged clip lengths that cover
-partial 64-frame tiles, single-frame clips, the longest workload clip, and batches on
-either side of the few-items limit of the 16-bit kernel."""
+partial 64-frame tiles, single-frame clips, the longest workload clip, and batches at and
+over the few-items limit of the 16-bit kernel."""
 import numpy as np
 import pytest
 
 pytestmark = pytest.mark.gpu
 
-# Batches with fewer (128-query tile x head) items than CUs take the key-split kernel (64-query
-# tiles, keys shared by two wave pairs); the last two cases sit just under that limit and far
-# over it (the 128-query kernel).
+# The 16-bit kernel splits the keys of 64-query tiles between two wave pairs while the batch
+# has at most 256 (64-frame tile x head) items, 16 tiles at 16 heads; the last three cases sit
+# at that limit, just over it and far over it (the 128-query kernel).
 FRAMES = [[1], [17], [64], [65], [500], [750], [51, 497, 3, 128, 129, 250],
-          [500, 500, 500, 128, 127, 64],
+          [500, 436, 1], [500, 500, 1],
           [250] * 8 + [129] * 4 + [1, 64, 700, 333]]
 
 
