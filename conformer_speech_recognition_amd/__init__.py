@@ -483,7 +483,7 @@ def debug_attention(dtype: str, qkv, frames, n_heads: int = 16, stream=None):
     fr = np.ascontiguousarray(np.asarray(frames, dtype=np.int32))
     d = qkv.shape[1] // 3
     out = torch.empty(qkv.shape[0], d, dtype=qkv.dtype, device=qkv.device)
-    nb = 20 * (len(fr) + 1) + 20 * int(fr.sum()) + 4096
+    nb = 20 * (len(fr) + 1) + 36 * int(fr.sum()) + 4096
     ws = torch.empty(nb, dtype=torch.uint8, device=qkv.device)
     s = (stream or torch.cuda.current_stream(qkv.device)).cuda_stream
     _check(lib().gigaam_debug_attention(DTYPES[dtype], d, n_heads, len(fr), fr.ctypes.data_as(_IP),

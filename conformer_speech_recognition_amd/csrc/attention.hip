@@ -121,12 +121,21 @@ __global__ void __launch_bounds__(256, KS2 == 1 ? 4 : 2) k_attn(AttnParams p) {
   const int hf = lane >> 5, c32 = lane & 31;
   const int qg = KS2 == 1 ? wave : (wave & 1);             // the wave's 32-query group
   const int kg = KS2 == 1 ? 0 : (wave >> 1);                // its share of the key tiles
-  const int* cuQ = KS2 == 1 ? p.cuQ : p.cuQ64;
   int tile, h;
   attn_item(blockIdx.x, KS2 == 1 ? p.n_tiles : p.n_tiles64, p.n_heads, tile, h);
-  const int b = (KS2 == 1 ? p.tileQ : p.tileQ64)[tile];
-  const int base = p.cuU[b], U = p.cuU[b + 1] - base;
-  const int q0 = (tile - cuQ[b]) * QT + qg * 32;           // the wave's first query
+  int base, U, q0;                                         // clip's first row, length; wave's first query
+  if constexpr (KS2 == 1) {
+    const int b = p.tileQ[tile];
+    base = p.cuU[b];
+    U = p.cuU[b + 1] - base;
+    q0 = (tile - p.cuQ[b]) * QT + qg * 32;
+  } else {
+    // one load for the tile's clip geometry: first row, length, first frame
+    const int4 geo = *(const int4*)(p.tileG64 + 4 * tile);
+    base = geo.x;
+    U = geo.y;
+    q0 = geo.z + qg * 32;
+  }
   const bool active = q0 < U;                              // wave-uniform
   const int qi = q0 + c32;
   const int ld = 3 * p.d;
@@ -449,7 +458,7 @@ hipError_t launch_attention(DType dt, int dk, const AttnParams& p, hipStream_t s
   // a clip or two: 64-query items with the keys split between two wave pairs (one 20 s clip:
   // 64 -> 128 workgroups), as long as every such workgroup gets a CU of its own (beyond that,
   // two of them sharing a CU take as long as one 128-query item, and the merge is extra)
-  const bool split = dt != DT_F32 && p.n_tiles64 > 0 && p.cuQ64 && p.tileQ64 &&
+  const bool split = dt != DT_F32 && p.n_tiles64 > 0 && p.tileG64 &&
                      (long)p.n_tiles64 * p.n_heads <= kAttnSplitMax;
   dim3 grid2(split ? p.n_tiles64 * p.n_heads : 1);
 #define GG_A(T, D) hipLaunchKernelGGL((k_attn<T, D>), grid, blk, 0, s, p)

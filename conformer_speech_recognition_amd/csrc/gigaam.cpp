@@ -765,7 +765,7 @@ int run(gigaam_model* m, const float* pcm, const int32_t* lengths, int32_t B, in
   };
   const bool f32 = dt == DT_F32;              // the fp32 kernel works on 64-frame tiles
   AttnParams ap{qkv, ao, d, H, f32 ? nQ : nQ2, md.cuU, f32 ? md.cuQ : md.cuQ2, f32 ? md.tileQ : md.tileQ2,
-                (float)(1.4426950408889634 / std::sqrt((double)dk)), f32 ? 0 : nQ, md.cuQ, md.tileQ};
+                (float)(1.4426950408889634 / std::sqrt((double)dk)), f32 ? 0 : nQ, md.tileG};
   DwParams dp;
   dp.in = hid; dp.out = hid2; dp.d = d; dp.n_tiles = nQ; dp.cuU = md.cuU; dp.cuQ = md.cuQ;
   dp.tileQ = md.tileQ; dp.tileG = md.tileG; dp.eps = c.bn_eps;
@@ -1026,19 +1026,20 @@ extern "C" int gigaam_debug_attention(int32_t dtype, int32_t d_model, int32_t n_
   const int U_tot = meta.cuU[batch];
   std::memcpy(meta.cuT, meta.cuU, sizeof meta.cuU);
   std::memcpy(meta.cuS, meta.cuU, sizeof meta.cuU);
-  const size_t need = 20 * (size_t)(batch + 1) + 20 * (size_t)U_tot + 4096;
+  const size_t need = 20 * (size_t)(batch + 1) + 36 * (size_t)U_tot + 4096;
   if (workspace_bytes < need) return fail(GIGAAM_E_WORKSPACE, "workspace %zu < %zu", workspace_bytes, need);
   int* w = (int*)workspace;
-  const int c1 = batch + 1;                    // five clip tables, then five row/tile tables
-  int* rows = w + 5 * c1;
+  const int c1 = batch + 1;                    // five clip tables, five row/tile tables, then
+  int* rows = w + 5 * c1;                      // the 16-byte tile geometry records
+  int* geo = (int*)(((uintptr_t)(rows + 5 * U_tot) + 15) & ~(uintptr_t)15);
   MetaDev md{w, w + c1, w + 2 * c1, w + 3 * c1, rows, rows + U_tot, rows + 2 * U_tot,
-             rows + 3 * U_tot, w + 4 * c1, rows + 4 * U_tot, nullptr};
+             rows + 3 * U_tot, w + 4 * c1, rows + 4 * U_tot, geo, nullptr};
   hipStream_t s = (hipStream_t)hip_stream;
   HIP_TRY(launch_meta(meta, md, U_tot, U_tot, U_tot, s));
   const bool f32 = dtype == GIGAAM_F32;
   AttnParams ap{qkv_dev, out_dev, d_model, n_heads, f32 ? nQ : nQ2, md.cuU, f32 ? md.cuQ : md.cuQ2,
                 f32 ? md.tileQ : md.tileQ2, (float)(1.4426950408889634 / std::sqrt((double)dk)),
-                f32 ? 0 : nQ, md.cuQ, md.tileQ};
+                f32 ? 0 : nQ, md.tileG};
   HIP_TRY(launch_attention((DType)dtype, dk, ap, s));
   return GIGAAM_OK;
 }

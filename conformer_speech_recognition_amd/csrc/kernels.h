@@ -123,9 +123,9 @@ struct AttnParams {
   int d, n_heads, n_tiles;
   const int* cuU; const int* cuQ; const int* tileQ;
   float scale_log2;                // log2(e) / sqrt(d_k)
-  // 16-bit kernel, batches with fewer items than CUs: the 64-frame tiles (MetaDev cuQ / tileQ),
-  // each taken by two wave pairs that split the keys; n_tiles64 = 0: not used
-  int n_tiles64; const int* cuQ64; const int* tileQ64;
+  // 16-bit kernel, a clip or two: the 64-frame tiles, each taken by two wave pairs that split
+  // the keys, and their geometry records (MetaDev tileG); n_tiles64 = 0: not used
+  int n_tiles64; const int* tileG64;
 };
 hipError_t launch_attention(DType dt, int dk, const AttnParams& p, hipStream_t s);
 

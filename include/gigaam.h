@@ -317,7 +317,7 @@ int gigaam_debug_mlp(int32_t dtype, int32_t M, int32_t d, int32_t f, const void*
  * the quantised dtypes = fp16); out_dev [sum U_b][d_model] the same type. qkv_dev and
  * out_dev must be 16-byte aligned (the kernel moves 16 bytes per access). d_model / n_heads must
  * be 48 or 64. workspace: device memory of at least
- *   20 * (batch + 1) + 20 * sum U_b + 4096 bytes (256-B aligned).
+ *   20 * (batch + 1) + 36 * sum U_b + 4096 bytes (256-B aligned).
  * Errors: GIGAAM_E_INVAL, GIGAAM_E_WORKSPACE, GIGAAM_E_UNSUPPORTED, GIGAAM_E_HIP.        */
 int gigaam_debug_attention(int32_t dtype, int32_t d_model, int32_t n_heads, int32_t batch,
                            const int32_t* frames_host, const void* qkv_dev, void* out_dev,
